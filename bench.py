@@ -1,0 +1,365 @@
+"""Benchmark of the proportional-sampling hot path on one MI355X.
+
+A step is one pass of the PER-mid workload: B = 262144 float priorities
+(Exp(1) + 1e-6, alpha 0.6, beta 0.4) and 32 minibatch updates, each one
+rebuilding the CDF (p^alpha + inclusive scan), drawing 8192 stratified
+indices, computing their IS weights and rewriting those 8192 priorities with
+new values.  All inputs are resident in HBM before timing starts.  `value` is
+sampled indices per second over the timed steps.
+
+The JSON line also carries:
+  roofline      the dominant kernel of the step: algorithmic bytes per launch
+                / its average launch duration (HIP events on the launch
+                stream, from an instrumented repeat of the timed steps);
+  cpu_baseline  the CPU oracle (single-threaded, as it stands) running the
+                same 32-update chain on a bounded number of steps;
+  extra         the CDF-scan bandwidth sweep (2^22..2^26, the Infinity Cache
+                flushed before every timed call), the sum-tree workload
+                (1024 updates + 1024 draws on 2^19 leaves), particle
+                resampling (1024 x 4096) and PER large (2^24 / 2^20).
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "CDF-scan HBM GB/s (% of peak) + sampled indices/sec at B=262144, 8192 draws"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--only", default="", help="profiling helper: scan:<n> | copy:<MiB>")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------- GPU side
+class PerMid:
+    """The PER-mid chain with every input resident on the GPU."""
+
+    def __init__(self, ps, torch):
+        import synthetic_inputs as si
+        d = si.per_mid()
+        self.ps, self.torch = ps, torch
+        self.n, self.k, self.rounds = d["p0"].size, d["U"].shape[1], d["U"].shape[0]
+        self.alpha, self.beta = d["alpha"], d["beta"]
+        dev = lambda a: torch.from_numpy(a).cuda()
+        self.p = dev(d["p0"].copy())
+        self.U = dev(d["U"])
+        self.v = dev(d["v"])
+        self.cdf = torch.empty(self.n, dtype=torch.float64, device="cuda")
+        self.tot = torch.empty(1, dtype=torch.float64, device="cuda")
+        self.idx = torch.empty(self.k, dtype=torch.int32, device="cuda")
+        self.w = torch.empty(self.k, dtype=torch.float32, device="cuda")
+        self.ws = ps.Workspace(ps.build_cdf_workspace_size(self.n))
+        self.sws = ps.Workspace(ps.scatter_workspace_size(self.n, self.k))
+
+    def step(self, events=None):
+        ps = self.ps
+        for r in range(self.rounds):
+            calls = (
+                ("build_cdf", lambda: ps.build_cdf(self.p, self.alpha, cdf=self.cdf,
+                                                    total=self.tot, ws=self.ws)),
+                ("sample", lambda: ps.sample(self.cdf, self.tot, self.U[r], stratified=True,
+                                             out=self.idx)),
+                ("is_weights", lambda: ps.is_weights(self.p, self.idx, self.alpha, self.beta,
+                                                     out=self.w)),
+                ("scatter_lww", lambda: ps.scatter_lww(self.p, self.idx, self.v[r], self.sws)),
+            )
+            for name, fn in calls:
+                if events is None:
+                    fn()
+                else:
+                    e0 = self.torch.cuda.Event(enable_timing=True)
+                    e1 = self.torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    fn()
+                    e1.record()
+                    events.setdefault(name, []).append((e0, e1))
+
+    def algo_bytes(self, name):
+        n, k = self.n, self.k
+        return {
+            "build_cdf": 12 * n,                                   # f32 in, f64 out
+            "sample": 8 * k + min(8 * n, 64 * k),                  # U in, idx out, CDF lines
+            "is_weights": 8 * k + min(4 * n, 64 * k),              # idx in, w out, p lines
+            "scatter_lww": 8 * k + 4 * k + 4 * k * 2,              # idx, vals, prio, owner r/w
+        }[name]
+
+
+KERNEL_NAMES = {
+    "build_cdf": "k_build_cdf<4, float, double>",
+    "sample": "k_sample_fp<double>",
+    "is_weights": "k_isw_single<float>",
+    "scatter_lww": "k_scatter_claim + k_scatter_apply",
+}
+
+
+def timed_steps(torch, fn, steps):
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / 1000.0, wall
+
+
+def flush_cache(torch, buf):
+    buf.add_(1)      # a 512 MiB read-modify-write evicts the 256 MB Infinity Cache
+
+
+def scan_sweep(ps, torch, sizes, reps=8):
+    """Median launch time of psamp_build_cdf per size, cache flushed."""
+    out = []
+    flush = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    for n in sizes:
+        g = torch.Generator(device="cuda").manual_seed(n)
+        p = torch.exp(2.0 * torch.randn(n, device="cuda", generator=g)).float()
+        q = torch.randint(1, (1 << 20) + 1, (n,), device="cuda", generator=g,
+                          dtype=torch.int64).to(torch.int32).view(torch.uint32)
+        for mode, prio, cdt, alpha in (("fp64", p, torch.float64, 0.7),
+                                       ("int", q, torch.uint64, 1.0)):
+            cdf = torch.empty(n, dtype=cdt, device="cuda")
+            tot = torch.empty(1, dtype=cdt, device="cuda")
+            ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+            ps.build_cdf(prio, alpha, cdf=cdf, total=tot, ws=ws)
+            ts = []
+            for _ in range(reps):
+                flush_cache(torch, flush)
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record()
+                ps.build_cdf(prio, alpha, cdf=cdf, total=tot, ws=ws)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            us = statistics.median(ts)
+            gbs = 12.0 * n / (us * 1e-6) / 1e9
+            out.append({"n": n, "mode": mode, "us": round(us, 2), "GB/s": round(gbs, 1),
+                        "frac_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            log(f"scan {mode} n=2^{n.bit_length() - 1}: {us:.1f} us {gbs:.0f} GB/s")
+            del cdf, ws
+        del p, q
+    del flush
+    torch.cuda.empty_cache()
+    return out
+
+
+def event_mean_us(torch, pairs):
+    torch.cuda.synchronize()
+    return 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+
+
+def sumtree_bench(ps, torch, rounds=200):
+    import synthetic_inputs as si
+    d = si.sumtree(rounds=rounds)
+    cap, nv = 1 << 19, 500000
+    tree = torch.zeros(2 * cap, dtype=torch.float32, device="cuda")
+    ps.segtree_build(tree, torch.from_numpy(d["p0"]).cuda(), d["alpha"])
+    idx = torch.from_numpy(d["idx"]).cuda()
+    v = torch.from_numpy(d["v"]).cuda()
+    U = torch.from_numpy(d["U"]).cuda()
+    out = torch.empty(d["U"].shape[1], dtype=torch.int32, device="cuda")
+    ev = {}
+    for r in range(rounds):
+        for name, fn in (("update", lambda: ps.segtree_update(tree, idx[r], v[r], d["alpha"])),
+                         ("sample", lambda: ps.segtree_sample(tree, nv, U[r], out=out))):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev.setdefault(name, []).append((e0, e1))
+    res = {k: round(event_mean_us(torch, v_[10:]), 2) for k, v_ in ev.items()}
+    res["samples_per_s"] = round(1024 / (res["sample"] * 1e-6))
+    log(f"sum tree: update {res['update']} us, sample {res['sample']} us")
+    return res
+
+
+def resample_bench(ps, torch, reps=20):
+    import synthetic_inputs as si
+    d = si.resample()
+    lw = torch.from_numpy(d["lw"]).cuda()
+    u = torch.from_numpy(d["u_row"]).cuda()
+    out = torch.empty_like(lw, dtype=torch.int32)
+    ps.resample_rows(lw, u, out=out)
+    ev = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        ps.resample_rows(lw, u, out=out)
+        e1.record()
+        ev.append((e0, e1))
+    us = event_mean_us(torch, ev)
+    gbs = (8 * lw.numel() + 4 * u.numel()) / (us * 1e-6) / 1e9
+    log(f"resample 1024x4096: {us:.1f} us {gbs:.0f} GB/s")
+    return {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def per_large_bench(ps, torch, reps=10):
+    import synthetic_inputs as si
+    d = si.per_large()
+    p = torch.from_numpy(d["p"]).cuda()
+    U = torch.from_numpy(d["U"]).cuda()
+    cdf, tot = ps.build_cdf(p, d["alpha"])
+    idx = ps.sample(cdf, tot, U)
+    w = ps.is_weights(p, idx, d["alpha"], d["beta"])
+    tree = torch.zeros(2 * p.numel(), dtype=torch.float32, device="cuda")
+    ps.segtree_build(tree, p, d["alpha"])
+    ev = {}
+    ws = ps.Workspace(ps.build_cdf_workspace_size(p.numel()))
+    iws = ps.Workspace(ps.is_weights_workspace_size(U.numel()))
+    for _ in range(reps):
+        for name, fn in (
+                ("build_cdf", lambda: ps.build_cdf(p, d["alpha"], cdf=cdf, total=tot, ws=ws)),
+                ("sample", lambda: ps.sample(cdf, tot, U, out=idx)),
+                ("is_weights", lambda: ps.is_weights(p, idx, d["alpha"], d["beta"], out=w,
+                                                     ws=iws)),
+                ("tree_build", lambda: ps.segtree_build(tree, p, d["alpha"])),
+                ("tree_sample", lambda: ps.segtree_sample(tree, p.numel(), U, stratified=True,
+                                                          out=idx))):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            ev.setdefault(name, []).append((e0, e1))
+    res = {k: round(event_mean_us(torch, v), 2) for k, v in ev.items()}
+    res["draws_per_s"] = round(U.numel() / ((res["sample"] + res["is_weights"]) * 1e-6))
+    log(f"per large: {res}")
+    return res
+
+
+# ----------------------------------------------------------------- CPU side
+def cpu_baseline(seconds):
+    import oracle
+    import synthetic_inputs as si
+    d = si.per_mid()
+    p = d["p0"].copy()
+    steps = 0
+    t0 = time.perf_counter()
+    while True:
+        for r in range(d["U"].shape[0]):
+            C, T, t, idx = oracle.sample(p, d["alpha"], d["U"][r], True)
+            oracle.is_weights(p, d["alpha"], T, idx, d["beta"])
+            p = oracle.scatter_lww(p, idx, d["v"][r])
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    k, rounds = d["U"].shape[1], d["U"].shape[0]
+    val = steps * rounds * k / el
+    log(f"cpu oracle: {steps} steps in {el:.1f} s -> {val:.0f} indices/s")
+    return {"value": round(val, 1), "unit": "sampled indices/s", "cores": 1, "kind": "oracle",
+            "sample": f"{steps} full steps (32 updates of B=262144 / 8192 draws each) of the "
+                      f"same seeded workload, {el:.1f} s, single thread"}
+
+
+# ----------------------------------------------------------------- main
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
+              "(this build runs on a single MI355X; see the sharding notes in DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import proportional_sampling_amd as ps
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    ps.lib()
+
+    if args.only.startswith("scan:"):
+        n = int(args.only.split(":")[1])
+        scan_sweep(ps, torch, [n], reps=20)
+        return
+    if args.only.startswith("copy:"):
+        mib = int(args.only.split(":")[1])
+        a = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {mib} MiB x5")
+        return
+
+    work = PerMid(ps, torch)
+    log(f"PER mid: warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        work.step()
+    gpu_s, wall_s = timed_steps(torch, work.step, args.steps)
+    ms_per_step = 1e3 * gpu_s / args.steps
+    draws = work.rounds * work.k * args.steps
+    value = draws / gpu_s
+    log(f"PER mid: {ms_per_step:.3f} ms/step, {value:.4g} indices/s (wall {wall_s:.3f} s)")
+
+    # instrumented repeat: per-call launch durations on the launch stream
+    events = {}
+    for _ in range(args.steps):
+        work.step(events)
+    per_call = {k: event_mean_us(torch, v) for k, v in events.items()}
+    share = {k: per_call[k] for k in per_call}
+    dom = max(share, key=share.get)
+    ab = work.algo_bytes(dom)
+    achieved = ab / (per_call[dom] * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "call": dom,
+                "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                "algo_bytes_per_launch": ab, "avg_launch_us": round(per_call[dom], 3)}
+    log(f"per-call us: { {k: round(v, 2) for k, v in per_call.items()} }; dominant {dom}")
+
+    extra = {"per_call_us": {k: round(v, 3) for k, v in per_call.items()}}
+    if not args.no_extra:
+        extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])
+        extra["sumtree"] = sumtree_bench(ps, torch)
+        extra["resample_rows"] = resample_bench(ps, torch)
+        extra["per_large"] = per_large_bench(ps, torch)
+
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args.cpu_seconds)
+        extra["gpu_over_cpu"] = round(value / cpu["value"], 1)
+        extra["host_cpus"] = os.cpu_count()
+
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "sampled indices/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "PER mid: B=262144 fp32 priorities ~ Exp(1)+1e-6, alpha=0.6, "
+                               "beta=0.4; 32 minibatch updates per step, each rebuilding the "
+                               "CDF, drawing 8192 stratified samples (+ IS weights) and "
+                               "rewriting those 8192 priorities",
+                   "B": work.n, "draws": work.k, "updates_per_step": work.rounds,
+                   "parallelism": "single GPU"},
+        "roofline": roofline, "cpu_baseline": cpu, "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

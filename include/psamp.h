@@ -1,0 +1,223 @@
+/*
+ * psamp.h -- C ABI of libpsamp: proportional (prioritized-replay) sampling
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * Every array argument is a DEVICE pointer owned by the caller.  Every call
+ * validates its arguments on the host, enqueues its kernels on `stream` (a
+ * hipStream_t passed as void*; NULL means the null stream) and returns
+ * without synchronising.  On a validation error nothing is enqueued and no
+ * output is touched.  No call allocates, frees or memsets device memory, or
+ * changes the current device: scratch space ("workspace") comes from the
+ * caller, sized by the matching *_workspace_size() query, and must be
+ * zero-filled once after it is allocated; after that the library keeps it
+ * consistent by itself (no per-call reset).  A workspace must not be used by
+ * two calls that can run at the same time.
+ *
+ * Preconditions that cannot be checked without a device sync (priorities
+ * finite and >= 0 with at least one > 0, indices in range, threshold
+ * fractions in [0, 1)) are the caller's; breaking them yields unspecified
+ * values but never an out-of-bounds access or a hang: every index is clamped
+ * and every cross-workgroup wait is bounded (a timed-out wait sets a bit that
+ * psamp_workspace_errors() reports).
+ *
+ * Sources (page title, then section):
+ *   [PR615] "trainer: parallel build_cdf scan + tiled (bitwise-identical)
+ *           mingru backward" -- "1. Parallel build_cdf".
+ *   [SEGT]  "GPU Segment Tree for PER Sampling" -- "Tree Layout",
+ *           "Operations", "CUDA Kernels", "Memory", "Integration with
+ *           GpuReplayBuffer", "Non-Goals".
+ *   [PF]    POPCORNBENCH particle-filter trace (Kimi-K2.6, l2_p48) -- the
+ *           reference model's resampling step.
+ *   [PER]   prioritized experience replay as named in [SEGT] "Non-Goals":
+ *           P(i) = p_i^alpha / sum_j p_j^alpha, IS_i = (N P(i))^-beta / max.
+ */
+#ifndef PSAMP_H
+#define PSAMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PSAMP_OK = 0,
+    PSAMP_E_NULL = 1,        /* a required pointer is NULL                  */
+    PSAMP_E_SIZE = 2,        /* a size is out of range                      */
+    PSAMP_E_DTYPE = 3,       /* unsupported dtype or dtype pair             */
+    PSAMP_E_PARAM = 4,       /* alpha / beta / flags out of range           */
+    PSAMP_E_WORKSPACE = 5,   /* workspace missing or too small              */
+    PSAMP_E_ALIGN = 6,       /* pointer not aligned to its element size     */
+    PSAMP_E_LAUNCH = 7,      /* the HIP runtime rejected a kernel launch    */
+    PSAMP_E_UNSUPPORTED = 8  /* valid request this build does not support   */
+} psamp_status;
+
+typedef enum {
+    PSAMP_F32 = 0,
+    PSAMP_F64 = 1,
+    PSAMP_U32 = 2,
+    PSAMP_U64 = 3,
+    PSAMP_I32 = 4
+} psamp_dtype;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* psamp_status_string(psamp_status s);
+/* Version of this ABI; bumped on any incompatible change. */
+int psamp_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * (1) p^alpha and the inclusive CDF.  [PR615] "1. Parallel build_cdf": the
+ * CDF of the B priorities, C_i = sum_{j<=i} w_j, one pass per update; [PER]
+ * w_i = p_i^alpha.  Single pass over the input (no size limit beyond n).
+ *
+ *   prio   : n priorities, PSAMP_F32 (fp mode) or PSAMP_U32 (integer mode).
+ *   alpha  : exponent (fp mode, finite, > 0); ignored in integer mode, where
+ *            w_i = q_i so that every sum is exact.
+ *   cdf    : n outputs.  fp mode: PSAMP_F64 (weights and sums in double) or
+ *            PSAMP_F32 (same double arithmetic, stored as float).  Integer
+ *            mode: PSAMP_U64, exact.
+ *   total  : 1 element of cdf_t, receives C_{n-1} (bit-equal to it).  Stays
+ *            on the device; psamp_sample reads it there.
+ *   n      : 1 <= n <= 2^31 - 1 (integer mode: n <= 2^31 - 1 keeps T < 2^63).
+ *   ws     : workspace of psamp_build_cdf_workspace_size(n_max) bytes, where
+ *            n_max is the largest n ever used with it.
+ * fp mode is deterministic run to run (fixed association); integer mode is
+ * exact.  Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_ALIGN
+ * (prio 4-byte, cdf/total element-aligned), E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+size_t psamp_build_cdf_workspace_size(int64_t n);
+psamp_status psamp_build_cdf(const void* prio, psamp_dtype prio_t, int64_t n,
+                             double alpha, void* cdf, psamp_dtype cdf_t,
+                             void* total, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (2a) Thresholds and search.  Sample i gets the threshold
+ *   stratified: t_i = ((i + U_i) / k) * T        (fp64: one rounding each
+ *                                                  for / and *)
+ *   iid:        t_i = U_i * T
+ * and the index idx_i = min(first j with C_j >= t_i, n - 1) -- [PF]
+ * searchsorted with right=False, then clamp to n-1.
+ *   cdf, total : from psamp_build_cdf (PSAMP_F64, PSAMP_F32 or PSAMP_U64).
+ *   u          : k fractions.  fp CDF: PSAMP_F32 values in [0,1).  Integer
+ *                CDF: PSAMP_U32 values r_i (U_i = r_i / 2^32), and
+ *                  stratified: t_i = floor(((i 2^32 + r_i) T) / (k 2^32)) + 1
+ *                  iid:        t_i = floor((r_i T) / 2^32) + 1
+ *                computed exactly, so integer mode is bit-exact.
+ *   out_idx    : k int32 indices (non-decreasing in i when stratified).
+ *   k          : 0 <= k <= 2^31 - 1 (0 is a no-op).
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (stratified not 0/1), E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+psamp_status psamp_sample(const void* cdf, psamp_dtype cdf_t, int64_t n,
+                          const void* total, const void* u, psamp_dtype u_t,
+                          int64_t k, int stratified, int32_t* out_idx, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (2b) Importance-sampling weights.  [PER]: P_i = w_{idx_i} / T,
+ * v_i = (N P_i)^-beta, IS_i = v_i / max_j v_j over the k sampled entries.
+ * N and T cancel, so the kernel evaluates the equal closed form
+ * IS_i = (w_min / w_i)^beta = (p_min / p_i)^(alpha beta) (fp mode) or
+ * (q_min / q_i)^beta (integer mode), with w_min the smallest sampled weight.
+ *   prio   : the n priorities the CDF was built from (F32 or U32).
+ *   idx    : k indices from psamp_sample (clamped into [0, n) on use).
+ *   out_w  : k float weights in (0, 1]; the largest is exactly 1.
+ *   ws     : psamp_is_weights_workspace_size(k) bytes (may be 0 bytes and
+ *            NULL when that size is 0).
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (beta < 0 or not finite,
+ * alpha <= 0), E_WORKSPACE, E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+size_t psamp_is_weights_workspace_size(int64_t k);
+psamp_status psamp_is_weights(const void* prio, psamp_dtype prio_t, int64_t n,
+                              double alpha, const int32_t* idx, int64_t k,
+                              double beta, float* out_w, void* ws, size_t ws_bytes,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
+ * (3) Sum tree, in the flat layout of [SEGT] "Tree Layout": an array of
+ * 2*cap_pow2 nodes, index 0 unused, root at 1, children of j at 2j and
+ * 2j+1, leaf i at cap_pow2 + i; every internal node is the sum of its two
+ * children, recomputed as fl(left + right) ([SEGT] "Operations -- Update").
+ * tree_t is PSAMP_F32 (leaves p^alpha rounded to float, sums in float, as
+ * on the page) or PSAMP_U64 (leaves q from U32 priorities, exact sums).
+ * Leaves n_valid .. cap_pow2-1 are 0.  Memory: 2 * cap_pow2 * sizeof(node).
+ * ---------------------------------------------------------------------- */
+/* Capacity rounded up to a power of two ([SEGT] "Tree Layout"); 0 if
+ * capacity < 1 or the result would exceed 2^30. */
+int64_t psamp_segtree_cap_pow2(int64_t capacity);
+
+/* Build every node from n_valid priorities (0 < n_valid <= cap_pow2 <= 2^30).
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_LAUNCH. */
+psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
+                                 const void* prio, psamp_dtype prio_t, int64_t n_valid,
+                                 double alpha, void* stream);
+
+/* Batched update ([SEGT] "Operations -- Update"): leaf idx_j <- prio_j^alpha
+ * for j = 0..m-1; when an index repeats, the entry with the largest j wins
+ * (as if the updates were applied one by one in batch order); every
+ * ancestor of a changed leaf is recomputed exactly once, after both of its
+ * children are final, so the tree stays bit-equal to a fresh build of its
+ * leaves.  idx_j must lie in [0, cap_pow2) (entries outside are ignored).
+ * 1 <= m <= 1024 per call (larger batches: split them; order is kept).
+ * ws: psamp_segtree_update_workspace_size(cap_pow2, m) bytes (0 today).
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_LAUNCH. */
+size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m);
+psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
+                                  const int32_t* idx, const void* prio,
+                                  psamp_dtype prio_t, int64_t m, double alpha,
+                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Root-to-leaf descent ([SEGT] "Operations -- Sample"): at each node go left
+ * if t <= left sum (or if the right sum is 0), else t -= left sum and go
+ * right; the result is clamped to n_valid - 1.  Thresholds: F32 tree --
+ * iid t = U_i * root (float), stratified t = (float)(((i + U_i) / k) * root)
+ * (double); U64 tree -- the integer formulas of psamp_sample with U32 r_i.
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_LAUNCH. */
+psamp_status psamp_segtree_sample(const void* tree, psamp_dtype tree_t, int64_t cap_pow2,
+                                  int64_t n_valid, const void* u, psamp_dtype u_t,
+                                  int64_t k, int stratified, int32_t* out_idx, void* stream);
+
+/* ------------------------------------------------------------------------
+ * (4) Row-batched systematic resampling ([PF], the reference model's
+ * resampling step).  Per row b of P float log-weights:
+ *   lse  = m + log(sum_j exp(lw_j - m)),  m = max_j lw_j
+ *   W_j  = exp(lw_j - lse),  C = inclusive cumsum of W   (double)
+ *   u_k  = (k + u_row[b]) / P                           (float arithmetic)
+ *   anc_k = min(first j with C_j >= u_k, P - 1)
+ *   logw   : rows x P floats, row stride ld_in elements (>= P).
+ *   u_row  : rows floats in [0, 1).
+ *   out_anc: rows x P int32, row stride ld_out elements (>= P).
+ *   1 <= P <= 8192, 1 <= rows <= 2^31 - 1.
+ * Errors: E_NULL, E_SIZE, E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+psamp_status psamp_resample_rows(const float* logw, int64_t rows, int64_t P,
+                                 int64_t ld_in, const float* u_row, int32_t* out_anc,
+                                 int64_t ld_out, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Priority rewrite (the scatter of [SEGT] "Integration" --
+ * update_priorities_gpu): prio[idx_j] = vals_j for j = 0..m-1, the largest
+ * j winning on repeated indices; indices outside [0, n) are ignored.
+ * prio_t / vals: PSAMP_F32 or PSAMP_U32 (same dtype for both).
+ * ws: psamp_scatter_workspace_size(n, m) bytes (one uint32 per item).
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_WORKSPACE, E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+size_t psamp_scatter_workspace_size(int64_t n, int64_t m);
+psamp_status psamp_scatter_lww(void* prio, psamp_dtype prio_t, int64_t n,
+                               const int32_t* idx, const void* vals, int64_t m,
+                               void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Diagnostics.  Copies the error bits a psamp_build_cdf workspace has
+ * accumulated (bit 0: a bounded cross-workgroup wait timed out; bit 1: a
+ * workgroup drew a ticket outside the call's grid) into *bits_host, with a
+ * synchronous device-to-host copy on `stream`.  The only call that syncs.
+ * Errors: E_NULL, E_WORKSPACE, E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+psamp_status psamp_workspace_errors(const void* ws, size_t ws_bytes,
+                                    uint64_t* bits_host, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PSAMP_H */

@@ -1,0 +1,278 @@
+"""proportional_sampling_amd -- Python binding of libpsamp (MI355X / gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of
+``libpsamp.so`` (built in-tree by ``proportional_sampling_amd.build``).
+PyTorch supplies device memory (``tensor.data_ptr()``) and the stream
+(``torch.cuda.current_stream().cuda_stream``).  There is no CPU fallback:
+importing works anywhere, but every call needs the built library and a GPU,
+and fails loudly otherwise.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpsamp.so")
+
+F32, F64, U32, U64, I32 = 0, 1, 2, 3, 4
+_DT = {torch.float32: F32, torch.float64: F64, torch.uint32: U32, torch.uint64: U64,
+       torch.int32: I32}
+
+_STATUS = {0: "ok", 1: "null pointer", 2: "size out of range", 3: "unsupported dtype",
+           4: "parameter out of range", 5: "workspace missing or too small",
+           6: "misaligned pointer", 7: "kernel launch failed", 8: "unsupported"}
+
+
+class PsampError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn}: {_STATUS.get(code, 'unknown')} (status {code})")
+        self.code = code
+
+
+# Exported symbols and their C signatures (mirrors include/psamp.h).
+_i64, _dbl, _int, _sz, _p = C.c_int64, C.c_double, C.c_int, C.c_size_t, C.c_void_p
+SIGNATURES = {
+    "psamp_status_string": (C.c_char_p, [_int]),
+    "psamp_abi_version": (_int, []),
+    "psamp_build_cdf_workspace_size": (_sz, [_i64]),
+    "psamp_build_cdf": (_int, [_p, _int, _i64, _dbl, _p, _int, _p, _p, _sz, _p]),
+    "psamp_sample": (_int, [_p, _int, _i64, _p, _p, _int, _i64, _int, _p, _p]),
+    "psamp_is_weights_workspace_size": (_sz, [_i64]),
+    "psamp_is_weights": (_int, [_p, _int, _i64, _dbl, _p, _i64, _dbl, _p, _p, _sz, _p]),
+    "psamp_segtree_cap_pow2": (_i64, [_i64]),
+    "psamp_segtree_build": (_int, [_p, _int, _i64, _p, _int, _i64, _dbl, _p]),
+    "psamp_segtree_update_workspace_size": (_sz, [_i64, _i64]),
+    "psamp_segtree_update": (_int, [_p, _int, _i64, _p, _p, _int, _i64, _dbl, _p, _sz, _p]),
+    "psamp_segtree_sample": (_int, [_p, _int, _i64, _i64, _p, _int, _i64, _int, _p, _p]),
+    "psamp_resample_rows": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p]),
+    "psamp_scatter_workspace_size": (_sz, [_i64, _i64]),
+    "psamp_scatter_lww": (_int, [_p, _int, _i64, _p, _p, _i64, _p, _sz, _p]),
+    "psamp_workspace_errors": (_int, [_p, _sz, C.POINTER(C.c_uint64), _p]),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """The loaded libpsamp.so; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m proportional_sampling_amd.build` (hipcc, gfx950)")
+        L = C.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn: str, code: int):
+    if code != 0:
+        raise PsampError(fn, code)
+
+
+def _stream(stream=None) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtypes=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtypes is not None and t.dtype not in dtypes:
+        raise TypeError(f"{name}: dtype {t.dtype} not in {dtypes}")
+    return t.data_ptr()
+
+
+class Workspace:
+    """Caller-owned scratch for calls that need one: zero-filled once, on
+    allocation; the library keeps it consistent afterwards.  One workspace
+    must not serve two calls that may run concurrently."""
+
+    def __init__(self, nbytes: int, device=None):
+        n = max(int(nbytes), 8)
+        self.buf = torch.zeros((n + 7) // 8, dtype=torch.int64,
+                               device=device if device is not None else "cuda")
+        self.nbytes = self.buf.numel() * 8
+
+    @property
+    def ptr(self) -> int:
+        return self.buf.data_ptr()
+
+    def errors(self, stream=None) -> int:
+        out = C.c_uint64(0)
+        _check("psamp_workspace_errors",
+               lib().psamp_workspace_errors(self.ptr, self.nbytes, C.byref(out), _stream(stream)))
+        return int(out.value)
+
+
+def abi_version() -> int:
+    return lib().psamp_abi_version()
+
+
+# ------------------------------------------------------------ (1) CDF
+def build_cdf_workspace_size(n: int) -> int:
+    return int(lib().psamp_build_cdf_workspace_size(int(n)))
+
+
+def build_cdf(prio: torch.Tensor, alpha: float = 1.0, *, cdf: torch.Tensor | None = None,
+              total: torch.Tensor | None = None, cdf_dtype=None, ws: Workspace | None = None,
+              stream=None):
+    """Inclusive CDF of prio^alpha (float32 prio) or of prio (uint32 prio).
+    Returns (cdf, total) -- both stay on the device."""
+    n = prio.numel()
+    p = _dev(prio, "prio", (torch.float32, torch.uint32))
+    if cdf_dtype is None:
+        cdf_dtype = torch.float64 if prio.dtype == torch.float32 else torch.uint64
+    if cdf is None:
+        cdf = torch.empty(n, dtype=cdf_dtype, device=prio.device)
+    if total is None:
+        total = torch.empty(1, dtype=cdf.dtype, device=prio.device)
+    if ws is None:
+        ws = Workspace(build_cdf_workspace_size(n), prio.device)
+    c = _dev(cdf, "cdf")
+    t = _dev(total, "total")
+    _check("psamp_build_cdf", lib().psamp_build_cdf(
+        p, _DT[prio.dtype], n, float(alpha), c, _DT[cdf.dtype], t, ws.ptr, ws.nbytes,
+        _stream(stream)))
+    return cdf, total
+
+
+def sample(cdf: torch.Tensor, total: torch.Tensor, u: torch.Tensor, *, stratified: bool = True,
+           out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """int32 indices: first j with cdf[j] >= t_i, clamped to n-1."""
+    k = u.numel()
+    if out is None:
+        out = torch.empty(k, dtype=torch.int32, device=cdf.device)
+    c = _dev(cdf, "cdf")
+    t = _dev(total, "total")
+    uu = _dev(u, "u", (torch.float32, torch.uint32))
+    o = _dev(out, "out", (torch.int32,))
+    _check("psamp_sample", lib().psamp_sample(
+        c, _DT[cdf.dtype], cdf.numel(), t, uu, _DT[u.dtype], k, int(bool(stratified)), o,
+        _stream(stream)))
+    return out
+
+
+def is_weights_workspace_size(k: int) -> int:
+    return int(lib().psamp_is_weights_workspace_size(int(k)))
+
+
+def is_weights(prio: torch.Tensor, idx: torch.Tensor, alpha: float, beta: float, *,
+               out: torch.Tensor | None = None, ws: Workspace | None = None,
+               stream=None) -> torch.Tensor:
+    """Float IS weights (w_min / w_i)^beta of the sampled entries."""
+    k = idx.numel()
+    if out is None:
+        out = torch.empty(k, dtype=torch.float32, device=prio.device)
+    need = is_weights_workspace_size(k)
+    if ws is None and need > 0:
+        ws = Workspace(need, prio.device)
+    p = _dev(prio, "prio", (torch.float32, torch.uint32))
+    i = _dev(idx, "idx", (torch.int32,))
+    o = _dev(out, "out", (torch.float32,))
+    _check("psamp_is_weights", lib().psamp_is_weights(
+        p, _DT[prio.dtype], prio.numel(), float(alpha), i, k, float(beta), o,
+        ws.ptr if ws is not None else None, ws.nbytes if ws is not None else 0,
+        _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------ (3) sum tree
+def segtree_cap_pow2(capacity: int) -> int:
+    return int(lib().psamp_segtree_cap_pow2(int(capacity)))
+
+
+def segtree_empty(capacity: int, kind=torch.float32, device="cuda") -> torch.Tensor:
+    cap = segtree_cap_pow2(capacity)
+    if cap == 0:
+        raise ValueError("capacity out of range")
+    return torch.zeros(2 * cap, dtype=kind, device=device)
+
+
+def segtree_build(tree: torch.Tensor, prio: torch.Tensor, alpha: float = 1.0,
+                  n_valid: int | None = None, stream=None) -> torch.Tensor:
+    cap = tree.numel() // 2
+    nv = prio.numel() if n_valid is None else int(n_valid)
+    t = _dev(tree, "tree", (torch.float32, torch.uint64))
+    p = _dev(prio, "prio", (torch.float32, torch.uint32))
+    _check("psamp_segtree_build", lib().psamp_segtree_build(
+        t, _DT[tree.dtype], cap, p, _DT[prio.dtype], nv, float(alpha), _stream(stream)))
+    return tree
+
+
+def segtree_update(tree: torch.Tensor, idx: torch.Tensor, prio: torch.Tensor,
+                   alpha: float = 1.0, stream=None) -> torch.Tensor:
+    cap = tree.numel() // 2
+    m = idx.numel()
+    if prio.numel() != m:
+        raise ValueError("idx and prio must have the same length")
+    t = _dev(tree, "tree", (torch.float32, torch.uint64))
+    i = _dev(idx, "idx", (torch.int32,))
+    p = _dev(prio, "prio", (torch.float32, torch.uint32))
+    _check("psamp_segtree_update", lib().psamp_segtree_update(
+        t, _DT[tree.dtype], cap, i, p, _DT[prio.dtype], m, float(alpha), None, 0,
+        _stream(stream)))
+    return tree
+
+
+def segtree_sample(tree: torch.Tensor, n_valid: int, u: torch.Tensor, *,
+                   stratified: bool = False, out: torch.Tensor | None = None,
+                   stream=None) -> torch.Tensor:
+    cap = tree.numel() // 2
+    k = u.numel()
+    if out is None:
+        out = torch.empty(k, dtype=torch.int32, device=tree.device)
+    t = _dev(tree, "tree", (torch.float32, torch.uint64))
+    uu = _dev(u, "u", (torch.float32, torch.uint32))
+    o = _dev(out, "out", (torch.int32,))
+    _check("psamp_segtree_sample", lib().psamp_segtree_sample(
+        t, _DT[tree.dtype], cap, int(n_valid), uu, _DT[u.dtype], k, int(bool(stratified)), o,
+        _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------ (4) rows
+def resample_rows(logw: torch.Tensor, u_row: torch.Tensor, *, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+    if logw.dim() != 2:
+        raise ValueError("logw must be rows x P")
+    rows, P = logw.shape
+    if out is None:
+        out = torch.empty(rows, P, dtype=torch.int32, device=logw.device)
+    lw = _dev(logw, "logw", (torch.float32,))
+    ur = _dev(u_row, "u_row", (torch.float32,))
+    o = _dev(out, "out", (torch.int32,))
+    _check("psamp_resample_rows", lib().psamp_resample_rows(
+        lw, rows, P, P, ur, o, P, _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------ rewrite
+def scatter_workspace_size(n: int, m: int) -> int:
+    return int(lib().psamp_scatter_workspace_size(int(n), int(m)))
+
+
+def scatter_lww(prio: torch.Tensor, idx: torch.Tensor, vals: torch.Tensor, ws: Workspace,
+                stream=None) -> torch.Tensor:
+    m = idx.numel()
+    if vals.numel() != m or vals.dtype != prio.dtype:
+        raise ValueError("vals must match idx in length and prio in dtype")
+    p = _dev(prio, "prio", (torch.float32, torch.uint32))
+    i = _dev(idx, "idx", (torch.int32,))
+    v = _dev(vals, "vals", (torch.float32, torch.uint32))
+    _check("psamp_scatter_lww", lib().psamp_scatter_lww(
+        p, _DT[prio.dtype], prio.numel(), i, v, m, ws.ptr, ws.nbytes, _stream(stream)))
+    return prio

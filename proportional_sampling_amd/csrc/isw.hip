@@ -1,0 +1,186 @@
+// isw.hip -- importance-sampling weights of a sampled batch.
+//
+// [PER] (named in "GPU Segment Tree for PER Sampling", "Non-Goals"):
+// P_i = w_{idx_i} / T, v_i = (N P_i)^-beta, IS_i = v_i / max_j v_j.
+// Since N and T cancel, IS_i = (w_min / w_i)^beta with w_min the smallest
+// sampled weight; with w = p^alpha that is (p_min / p_i)^(alpha beta) (fp
+// mode) and (q_min / q_i)^beta in integer mode (alpha not applied).  The
+// minimum is taken exactly on the raw priorities (uint32 order of the
+// non-negative float bits), the power in double via log2 / exp2, and the
+// largest weight comes out as exactly 1.
+//
+// Small batches (k <= 8192) run in one 1024-thread workgroup.  Larger ones
+// use two kernels: per-block minima with a last-block reduction, then the
+// weights.
+#include "psamp_device.h"
+#include "psamp_host.h"
+
+namespace psamp {
+
+constexpr int kIswThreads = 1024;
+constexpr int kIswPerThread = 4;
+constexpr int kIswBlock = kIswThreads * kIswPerThread;   // samples per block
+constexpr int64_t kIswSingleMax = 8192;
+constexpr int kIswHdrWords = 64;                        // 256-byte header (uint32)
+
+template <class P>
+__device__ __forceinline__ uint32_t prio_key(P x);
+template <>
+__device__ __forceinline__ uint32_t prio_key<float>(float x) { return __float_as_uint(x); }
+template <>
+__device__ __forceinline__ uint32_t prio_key<uint32_t>(uint32_t x) { return x; }
+
+template <class P>
+__device__ __forceinline__ double prio_val(uint32_t key);
+template <>
+__device__ __forceinline__ double prio_val<float>(uint32_t key) { return (double)__uint_as_float(key); }
+template <>
+__device__ __forceinline__ double prio_val<uint32_t>(uint32_t key) { return (double)key; }
+
+__device__ __forceinline__ int64_t clamp_idx(int32_t i, int64_t n) {
+    return i < 0 ? 0 : (i >= n ? n - 1 : (int64_t)i);
+}
+
+// IS = (pmin / p)^e.  p == 0 forces pmin == 0: 0/0 -> NaN; pmin == 0 < p -> 0.
+__device__ __forceinline__ float is_weight(double pmin, double lpmin, double p, double e,
+                                           const MathLds* M) {
+    if (!(p > 0.0)) return __int_as_float(0x7FC00000);
+    if (!(pmin > 0.0)) return 0.0f;
+    return (float)exp2_tab(e * (lpmin - log2_sig32(p, M)), M);
+}
+
+template <class P>
+__global__ __launch_bounds__(kIswThreads) void k_isw_single(const P* __restrict__ prio, int64_t n,
+                                                            const int32_t* __restrict__ idx,
+                                                            int64_t k, double e,
+                                                            float* __restrict__ out) {
+    __shared__ MathLds M;
+    __shared__ uint32_t s_min;
+    const int tid = threadIdx.x;
+    math_lds_fill(&M, tid, kIswThreads);
+    if (tid == 0) s_min = 0xFFFFFFFFu;
+    __syncthreads();
+    uint32_t mn = 0xFFFFFFFFu;
+    for (int64_t i = tid; i < k; i += kIswThreads) mn = min_(mn, prio_key<P>(prio[clamp_idx(idx[i], n)]));
+    atomicMin(&s_min, mn);
+    __syncthreads();
+    const double pmin = prio_val<P>(s_min);
+    const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
+    for (int64_t i = tid; i < k; i += kIswThreads) {
+        const double p = prio_val<P>(prio_key<P>(prio[clamp_idx(idx[i], n)]));
+        out[i] = is_weight(pmin, lpmin, p, e, &M);
+    }
+}
+
+// Pass 1: per-block minimum; the last block to finish reduces them into
+// hdr[1] and rearms the block counter hdr[0] for the next call.
+template <class P>
+__global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ prio, int64_t n,
+                                                         const int32_t* __restrict__ idx, int64_t k,
+                                                         uint32_t* __restrict__ ws, int nblocks) {
+    __shared__ uint32_t s_min;
+    __shared__ int s_last;
+    const int tid = threadIdx.x;
+    if (tid == 0) s_min = 0xFFFFFFFFu;
+    __syncthreads();
+    uint32_t mn = 0xFFFFFFFFu;
+    const int64_t b0 = (int64_t)blockIdx.x * kIswBlock;
+#pragma unroll
+    for (int j = 0; j < kIswPerThread; ++j) {
+        const int64_t i = b0 + j * kIswThreads + tid;
+        if (i < k) mn = min_(mn, prio_key<P>(prio[clamp_idx(idx[i], n)]));
+    }
+    atomicMin(&s_min, mn);
+    __syncthreads();
+    uint32_t* hdr = ws;
+    uint32_t* part = ws + kIswHdrWords;
+    if (tid == 0) {
+        part[blockIdx.x] = s_min;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t t = __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        s_last = (t == (uint32_t)(nblocks - 1));
+        if (s_last) s_min = 0xFFFFFFFFu;
+    }
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    uint32_t m2 = 0xFFFFFFFFu;
+    for (int b = tid; b < nblocks; b += kIswThreads)
+        m2 = min_(m2, __hip_atomic_load(&part[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    atomicMin(&s_min, m2);
+    __syncthreads();
+    if (tid == 0) {
+        hdr[1] = s_min;
+        __hip_atomic_store(&hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
+template <class P>
+__global__ __launch_bounds__(kIswThreads) void k_isw_apply(const P* __restrict__ prio, int64_t n,
+                                                           const int32_t* __restrict__ idx, int64_t k,
+                                                           double e, const uint32_t* __restrict__ ws,
+                                                           float* __restrict__ out) {
+    __shared__ MathLds M;
+    const int tid = threadIdx.x;
+    math_lds_fill(&M, tid, kIswThreads);
+    __syncthreads();
+    const double pmin = prio_val<P>(ws[1]);
+    const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
+    const int64_t b0 = (int64_t)blockIdx.x * kIswBlock;
+#pragma unroll
+    for (int j = 0; j < kIswPerThread; ++j) {
+        const int64_t i = b0 + j * kIswThreads + tid;
+        if (i < k) {
+            const double p = prio_val<P>(prio_key<P>(prio[clamp_idx(idx[i], n)]));
+            out[i] = is_weight(pmin, lpmin, p, e, &M);
+        }
+    }
+}
+
+template <class P>
+static psamp_status launch_isw(const void* prio, int64_t n, const int32_t* idx, int64_t k,
+                               double e, float* out, void* ws, hipStream_t st) {
+    if (k <= kIswSingleMax) {
+        if (trace_enabled()) trace_launch("k_isw_single", 1, kIswThreads, k);
+        hipLaunchKernelGGL(k_isw_single<P>, dim3(1), dim3(kIswThreads), 0, st, (const P*)prio, n,
+                           idx, k, e, out);
+        return launch_status();
+    }
+    const int nb = (int)ceil_div(k, kIswBlock);
+    if (trace_enabled()) trace_launch("k_isw_min+apply", nb, kIswThreads, k);
+    hipLaunchKernelGGL(k_isw_min<P>, dim3(nb), dim3(kIswThreads), 0, st, (const P*)prio, n, idx, k,
+                       (uint32_t*)ws, nb);
+    psamp_status s = launch_status();
+    if (s != PSAMP_OK) return s;
+    hipLaunchKernelGGL(k_isw_apply<P>, dim3(nb), dim3(kIswThreads), 0, st, (const P*)prio, n, idx,
+                       k, e, (const uint32_t*)ws, out);
+    return launch_status();
+}
+
+}  // namespace psamp
+
+using namespace psamp;
+
+extern "C" size_t psamp_is_weights_workspace_size(int64_t k) {
+    if (k < 0 || k > kMaxN) return 0;
+    if (k <= kIswSingleMax) return 0;
+    return (size_t)kIswHdrWords * 4 + (size_t)ceil_div(k, kIswBlock) * 4;
+}
+
+extern "C" psamp_status psamp_is_weights(const void* prio, psamp_dtype prio_t, int64_t n,
+                                         double alpha, const int32_t* idx, int64_t k, double beta,
+                                         float* out_w, void* ws, size_t ws_bytes, void* stream) {
+    if (n < 1 || n > kMaxN || k < 0 || k > kMaxN) return PSAMP_E_SIZE;
+    if (prio_t != PSAMP_F32 && prio_t != PSAMP_U32) return PSAMP_E_DTYPE;
+    if (!(finite_d(beta) && beta >= 0.0)) return PSAMP_E_PARAM;
+    if (prio_t == PSAMP_F32 && !(finite_d(alpha) && alpha > 0.0)) return PSAMP_E_PARAM;
+    if (k == 0) return PSAMP_OK;
+    if (!prio || !idx || !out_w) return PSAMP_E_NULL;
+    const size_t need = psamp_is_weights_workspace_size(k);
+    if (need > 0 && (!ws || ws_bytes < need)) return PSAMP_E_WORKSPACE;
+    if (!aligned(prio, 4) || !aligned(idx, 4) || !aligned(out_w, 4) || (need && !aligned(ws, 8)))
+        return PSAMP_E_ALIGN;
+    hipStream_t st = as_stream(stream);
+    if (prio_t == PSAMP_F32) return launch_isw<float>(prio, n, idx, k, alpha * beta, out_w, ws, st);
+    return launch_isw<uint32_t>(prio, n, idx, k, beta, out_w, ws, st);
+}

@@ -1,0 +1,298 @@
+// psamp_device.h -- device building blocks shared by the libpsamp kernels
+// (gfx950 / CDNA4, wave64).
+//
+//  * wave64 inclusive scans built from DPP row shifts and row broadcasts;
+//  * 64-bit status words for the single-pass scan (value and "ready" flag in
+//    one word, so relaxed agent-scope atomics are enough to pass them
+//    between workgroups on different XCDs);
+//  * a table-driven fp64 log2 / exp2 (range reduction after Tang's method,
+//    Taylor kernels on the reduced argument) used for p^alpha, exp and the
+//    importance-sampling weights.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pow_tables.h"
+
+namespace psamp {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ DPP
+// DPP control words (GFX9 encoding).
+enum : int {
+    kRowShr1 = 0x111,
+    kRowShr2 = 0x112,
+    kRowShr4 = 0x114,
+    kRowShr8 = 0x118,
+    kWaveShr1 = 0x138,
+    kRowBcast15 = 0x142,
+    kRowBcast31 = 0x143,
+};
+
+// Lanes that have no source (or whose row is masked off) receive 0.
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint32_t dpp32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, BOUND_ZERO);
+}
+
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ double dpp(double x) {
+    uint32_t lo = dpp32<CTRL, ROW_MASK, BOUND_ZERO>((uint32_t)__double2loint(x));
+    uint32_t hi = dpp32<CTRL, ROW_MASK, BOUND_ZERO>((uint32_t)__double2hiint(x));
+    return __hiloint2double((int)hi, (int)lo);
+}
+
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ uint64_t dpp(uint64_t x) {
+    uint32_t lo = dpp32<CTRL, ROW_MASK, BOUND_ZERO>((uint32_t)x);
+    uint32_t hi = dpp32<CTRL, ROW_MASK, BOUND_ZERO>((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+template <int CTRL, int ROW_MASK, bool BOUND_ZERO>
+__device__ __forceinline__ float dpp(float x) {
+    return __uint_as_float(dpp32<CTRL, ROW_MASK, BOUND_ZERO>(__float_as_uint(x)));
+}
+
+// Inclusive sum over the 64 lanes: Kogge-Stone inside each 16-lane row,
+// then row 0 -> row 1, row 2 -> row 3 (bcast15) and rows 0..1 -> rows 2..3
+// (bcast31).  The association is fixed, so the result is deterministic.
+template <class T>
+__device__ __forceinline__ T wave_incl_scan(T x) {
+    x = x + dpp<kRowShr1, 0xF, true>(x);
+    x = x + dpp<kRowShr2, 0xF, true>(x);
+    x = x + dpp<kRowShr4, 0xF, true>(x);
+    x = x + dpp<kRowShr8, 0xF, true>(x);
+    x = x + dpp<kRowBcast15, 0xA, false>(x);
+    x = x + dpp<kRowBcast31, 0xC, false>(x);
+    return x;
+}
+
+// Value of lane-1 (lane 0 gets 0): turns an inclusive scan into an exclusive one.
+template <class T>
+__device__ __forceinline__ T wave_shr1(T x) {
+    return dpp<kWaveShr1, 0xF, true>(x);
+}
+
+__device__ __forceinline__ double readlane(double x, int lane) {
+    int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+    int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+    return __hiloint2double(hi, lo);
+}
+__device__ __forceinline__ uint64_t readlane(uint64_t x, int lane) {
+    uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)x, lane);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(x >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ float readlane(float x, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), lane));
+}
+
+// Sum of all 64 lanes, same association as wave_incl_scan (lane 63's value).
+template <class T>
+__device__ __forceinline__ T wave_sum(T x) {
+    return readlane(wave_incl_scan(x), kWave - 1);
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// ------------------------------------------------------- atomics / status
+__device__ __forceinline__ uint64_t load_agent(const uint64_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_agent(uint64_t* p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fetch_add_agent(uint64_t* p, uint64_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t fetch_max_agent(uint64_t* p, uint64_t v) {
+    return __hip_atomic_fetch_max(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// A status word is 0 while not ready; a published value v is stored as
+// enc(v) != 0.  Doubles: bit pattern + 1 (NaN first made canonical, so the
+// all-ones pattern never appears).  uint64: v + 1 (sums stay below 2^63).
+__device__ __forceinline__ uint64_t status_enc(double v) {
+    uint64_t b = (uint64_t)__double_as_longlong(v);
+    if (v != v) b = 0x7FF8000000000000ull;
+    return b + 1;
+}
+__device__ __forceinline__ uint64_t status_enc(uint64_t v) { return v + 1; }
+__device__ __forceinline__ void status_dec(uint64_t w, double& v) {
+    v = __longlong_as_double((long long)(w - 1));
+}
+__device__ __forceinline__ void status_dec(uint64_t w, uint64_t& v) { v = w - 1; }
+
+// Wait until the status word of every lane with `need` is non-zero, then
+// return it (0 for lanes without `need`).  The wait is bounded: after
+// `limit` polls the wave records an error bit and gives up, so a broken
+// invariant turns into a reported error instead of a hang.
+__device__ __forceinline__ uint64_t wait_status(const uint64_t* addr, bool need,
+                                                uint64_t* err_word, uint64_t err_bit,
+                                                int limit) {
+    uint64_t v = need ? load_agent(addr) : 0;
+    int polls = 0;
+    while (__any(need && v == 0)) {
+        if (++polls > limit) {
+            if (lane_id() == 0) __hip_atomic_fetch_or(err_word, err_bit, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+        if (need && v == 0) v = load_agent(addr);
+    }
+    return v;
+}
+
+// ------------------------------------------------------------ fp64 math
+// log2 and exp2 in double, accurate to a few 1e-16 relative (exp2) and a
+// few 1e-16 absolute (log2) -- far below what the sampling contract needs
+// (about 1e-9 on the weights).  Tables live in LDS (one copy per
+// workgroup): entry k of the log table holds {c_k, -log2(c_k)}.
+struct MathLds {
+    double2 log_tab[128];
+    double exp_tab[64];
+};
+
+__device__ __forceinline__ void math_lds_fill(MathLds* m, int tid, int nthreads) {
+    for (int i = tid; i < 128; i += nthreads)
+        m->log_tab[i] = make_double2(__longlong_as_double((long long)kLog2Tab[i][0]),
+                                     __longlong_as_double((long long)kLog2Tab[i][1]));
+    for (int i = tid; i < 64; i += nthreads)
+        m->exp_tab[i] = __longlong_as_double((long long)kExp2Tab[i][0]);
+}
+
+constexpr double kLog2e = 1.4426950408889634074;   // 1/ln 2
+constexpr double kLn2 = 0.69314718055994530942;
+
+// log2(x) for a positive, finite, normal double whose significand has at
+// most 32 significant bits (every float and every uint32 converts to one).
+// x = 2^e * m, m in [1,2); k = top 7 fraction bits of m; c_k ~ 1/m (21
+// bits) so r = m*c_k - 1 is exact and |r| < 2^-8; ln(1+r) by Taylor to r^6
+// (truncation < 3e-18).
+__device__ __forceinline__ double log2_sig32(double x, const MathLds* M) {
+    uint64_t b = (uint64_t)__double_as_longlong(x);
+    int e = (int)(b >> 52) - 1023;
+    int k = (int)(b >> 45) & 127;
+    double m = __longlong_as_double((long long)((b & 0x000FFFFFFFFFFFFFull) | 0x3FF0000000000000ull));
+    double2 ct = M->log_tab[k];
+    double r = fma(m, ct.x, -1.0);
+    double q = fma(r, -1.0 / 6.0, 0.2);
+    q = fma(r, q, -0.25);
+    q = fma(r, q, 1.0 / 3.0);
+    q = fma(r, q, -0.5);
+    double ln1p = fma(r * r, q, r);
+    return ((double)e + ct.y) + ln1p * kLog2e;
+}
+
+// 2^y.  y = N/64 + f with N = rint(64 y), |f| <= 1/128 (f exact);
+// 2^f = e^g, g = f ln2, |g| < 0.0055, Taylor to g^5 (truncation < 4e-17);
+// 2^(j/64) from the table; the power of two by ldexp.
+__device__ __forceinline__ double exp2_tab(double y, const MathLds* M) {
+    if (!(y < 1025.0)) return (y != y) ? y : __longlong_as_double(0x7FF0000000000000ll);
+    if (y < -1100.0) return 0.0;
+    double N = rint(y * 64.0);
+    double f = fma(N, -1.0 / 64.0, y);
+    int Ni = (int)N;
+    int j = Ni & 63;
+    int n = Ni >> 6;
+    double g = f * kLn2;
+    double q = fma(g, 1.0 / 120.0, 1.0 / 24.0);
+    q = fma(g, q, 1.0 / 6.0);
+    q = fma(g, q, 0.5);
+    q = fma(g, q, 1.0);
+    double em1 = g * q;                  // e^g - 1
+    double s = M->exp_tab[j];
+    return ldexp(fma(s, em1, s), n);
+}
+
+// p^alpha for a float priority p >= 0 and alpha > 0 (double).
+__device__ __forceinline__ double pow_prio(float p, double alpha, const MathLds* M) {
+    if (!(p > 0.0f)) return (p == 0.0f) ? 0.0 : __longlong_as_double(0x7FF8000000000000ll);
+    if (p == __int_as_float(0x7F800000)) return (double)p;
+    return exp2_tab(alpha * log2_sig32((double)p, M), M);
+}
+
+// e^x for a finite double x (the particle weights).
+__device__ __forceinline__ double exp_d(double x, const MathLds* M) {
+    return exp2_tab(x * kLog2e, M);
+}
+
+// ------------------------------------------------ integer thresholds
+// floor(((i 2^32 + r) T) / (k 2^32)) + 1  (stratified) or
+// floor((r T) / 2^32) + 1 (iid), exactly, with T < 2^63 and k < 2^31.
+__device__ __forceinline__ uint64_t int_threshold(uint64_t i, uint32_t r, uint64_t k, uint64_t T,
+                                                  int stratified, int k_log2) {
+    if (!stratified) {
+        const uint64_t lo = (uint64_t)r * T;
+        const uint64_t hi = __umul64hi((uint64_t)r, T);
+        return ((hi << 32) | (lo >> 32)) + 1;
+    }
+    const uint64_t a = (i << 32) | (uint64_t)r;      // < 2^63
+    const uint64_t lo = a * T;
+    const uint64_t hi = __umul64hi(a, T);            // product < 2^126
+    const uint64_t h2 = hi >> 32;                    // x = floor(prod / 2^32) = h2:l2
+    const uint64_t l2 = (hi << 32) | (lo >> 32);
+    uint64_t q;
+    if (k_log2 >= 0) {
+        q = (k_log2 == 0) ? l2 : ((l2 >> k_log2) | (h2 << (64 - k_log2)));
+    } else {
+        // floor(x / k) < 2^63 implies h2 < k: long division in 32-bit digits.
+        uint64_t cur = (h2 << 32) | (l2 >> 32);
+        const uint64_t q1 = cur / k;
+        const uint64_t rem = cur - q1 * k;
+        cur = (rem << 32) | (l2 & 0xFFFFFFFFull);
+        const uint64_t q0 = cur / k;
+        q = (q1 << 32) | q0;
+    }
+    return q + 1;
+}
+
+// ------------------------------------------------- 256-thread tile scan
+// A tile of 256 threads x R rows x 4 elements: thread t holds elements
+// r*1024 + 4t + c (c = 0..3) of row r.  On entry q[r][c] is the thread-local
+// inclusive prefix of its 4 elements.  On exit X[r] is the sum of everything
+// before the thread's 4 elements of row r (so element (r, c) has inclusive
+// prefix X[r] + q[r][c]) and A is the tile total.  Association is fixed:
+// DPP inside each wave, then the 4 wave totals in order, rows in order.
+// s_wtot: LDS scratch of 4 x R values; the call contains one barrier.
+template <int R, class Acc>
+__device__ __forceinline__ void tile_scan_256(const Acc (&q)[R][4], Acc (&X)[R], Acc& A,
+                                              Acc (*s_wtot)[R]) {
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    Acc iex[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const Acc I = wave_incl_scan(q[r][3]);
+        iex[r] = wave_shr1(I);
+        const Acc wt = readlane(I, kWave - 1);
+        if (lane == 0) s_wtot[wave][r] = wt;
+    }
+    __syncthreads();
+    A = Acc(0);
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        Acc pw = Acc(0), rt = Acc(0);
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+            const Acc t = s_wtot[w2][r];
+            if (w2 < wave) pw = pw + t;
+            rt = rt + t;
+        }
+        X[r] = A + (pw + iex[r]);
+        A = A + rt;
+    }
+}
+
+// ------------------------------------------------------------- helpers
+template <class T>
+__host__ __device__ __forceinline__ T min_(T a, T b) { return a < b ? a : b; }
+template <class T>
+__host__ __device__ __forceinline__ T max_(T a, T b) { return a > b ? a : b; }
+
+}  // namespace psamp

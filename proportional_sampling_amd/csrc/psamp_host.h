@@ -1,0 +1,41 @@
+// psamp_host.h -- host-side helpers shared by the libpsamp entry points.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/psamp.h"
+
+namespace psamp {
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline bool aligned(const void* p, size_t a) {
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+inline bool finite_d(double x) { return x == x && x - x == 0.0; }
+
+// Report a launch failure (never aborts).
+inline psamp_status launch_status() {
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? PSAMP_OK : PSAMP_E_LAUNCH;
+}
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline int ilog2_exact(int64_t x) {   // x must be a power of two
+    int r = 0;
+    while ((int64_t(1) << r) < x) ++r;
+    return r;
+}
+
+inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+constexpr int64_t kMaxN = 0x7FFFFFFFll;   // int32 indices
+
+// Optional launch trace: PSAMP_TRACE=1 prints one line per launch.
+bool trace_enabled();
+void trace_launch(const char* kernel, int64_t grid, int block, int64_t n);
+
+}  // namespace psamp

@@ -1,0 +1,403 @@
+// tree.hip -- sum tree ("GPU Segment Tree for PER Sampling").
+//
+// Layout ([SEGT] "Tree Layout"): flat array of 2*cap nodes, index 0 unused,
+// root at 1, children of j at 2j and 2j+1, leaf i at cap+i.  F32 trees hold
+// p^alpha rounded to float and float sums (the page's precision); U64 trees
+// hold uint32 priorities and exact sums.
+//
+// Build: passes of up to 11 levels each; a workgroup reduces 2048 nodes of a
+// level through LDS and writes every node it forms.
+//
+// Update ([SEGT] "Operations -- Update": write the leaf, recompute each
+// ancestor as left + right).  The page's one-thread-per-update kernel races
+// when two updates share an ancestor (a thread can read a stale sibling and
+// overwrite a correct parent) and on repeated indices.  Here one 1024-thread
+// workgroup handles a batch of up to 1024 updates deterministically:
+//   1. sort the (leaf, batch position) keys in LDS (bitonic);
+//   2. keep the last entry of each run of equal leaves (largest batch
+//      position: last write wins);
+//   3. each winning leaf's thread prefetches the old values of all siblings
+//      on its root path at once (one round of loads, no per-level latency);
+//   4. level by level, the first winner under each dirty node (its "owner")
+//      forms fl(left + right) from its own value, a clean sibling from its
+//      registers, or the dirty sibling's value from LDS; each owner also
+//      carries the index of the next owner, so it finds that sibling in O(1).
+// Every dirty node is written exactly once, after both children are final,
+// as fl(left + right): the tree stays bit-equal to a fresh build.
+//
+// Sample ([SEGT] "Operations -- Sample"): descend from the root, left if
+// t <= left sum (or the right sum is 0), else subtract and go right.  The
+// top 13 (F32) or 12 (U64) levels are copied into LDS per workgroup; the
+// remaining levels load the two children as one vector.
+#include "psamp_device.h"
+#include "psamp_host.h"
+
+namespace psamp {
+
+constexpr int kBuildThreads = 256;
+constexpr int kBuildLevels = 11;                 // levels per build pass
+constexpr int kUpdThreads = 1024;
+constexpr int kMaxDepth = 30;                    // cap <= 2^30
+constexpr int kSampleTreeThreads = 256;
+
+template <class V> struct TreeTop;
+template <> struct TreeTop<float> { static constexpr int levels = 13; };
+template <> struct TreeTop<uint64_t> { static constexpr int levels = 12; };
+
+__device__ __forceinline__ float leaf_value(float p, double alpha, const MathLds* M) {
+    return (float)pow_prio(p, alpha, M);
+}
+__device__ __forceinline__ uint64_t leaf_value(uint32_t q, double, const MathLds*) {
+    return (uint64_t)q;
+}
+
+// One build pass.  Input level: `cnt` nodes at tree indices [cnt, 2 cnt)
+// (the leaves when FROM_PRIO, whose values are formed from prio).  Each
+// workgroup takes 2^s consecutive nodes and writes the s levels above them.
+template <class V, class P, bool FROM_PRIO>
+__global__ __launch_bounds__(kBuildThreads) void k_tree_build_pass(
+    V* __restrict__ tree, int64_t cnt, const P* __restrict__ prio, int64_t n_valid,
+    double alpha, int s) {
+    __shared__ V buf[2][1 << kBuildLevels];
+    __shared__ MathLds M;
+    const int tid = threadIdx.x;
+    if (FROM_PRIO && sizeof(P) == 4 && sizeof(V) == 4) math_lds_fill(&M, tid, kBuildThreads);
+    __syncthreads();
+    const int sub = 1 << s;
+    const int64_t first = (int64_t)blockIdx.x << s;      // first input node (relative)
+    for (int i = tid; i < sub; i += kBuildThreads) {
+        const int64_t node = first + i;
+        V v;
+        if (FROM_PRIO) {
+            v = node < n_valid ? leaf_value(prio[node], alpha, &M) : V(0);
+            tree[cnt + node] = v;
+        } else {
+            v = tree[cnt + node];
+        }
+        buf[0][i] = v;
+    }
+    __syncthreads();
+    int64_t lvl = cnt;                                   // tree index of the level's first node
+    for (int d = 1; d <= s; ++d) {
+        const int m = sub >> d;
+        const V* src = buf[(d - 1) & 1];
+        V* dst = buf[d & 1];
+        lvl >>= 1;
+        for (int q = tid; q < m; q += kBuildThreads) {
+            const V x = src[2 * q] + src[2 * q + 1];
+            dst[q] = x;
+            tree[lvl + (first >> d) + q] = x;
+        }
+        __syncthreads();
+    }
+}
+
+template <class V, class P>
+__global__ __launch_bounds__(kUpdThreads) void k_tree_update(
+    V* __restrict__ tree, int64_t cap, int D, const int32_t* __restrict__ idx,
+    const P* __restrict__ prio, int m, double alpha) {
+    __shared__ uint64_t keys[kUpdThreads];
+    __shared__ uint32_t wcount[kUpdThreads / kWave];
+    __shared__ int32_t wl[kUpdThreads];                  // winner leaves, ascending
+    __shared__ int32_t wj[kUpdThreads];                  // their batch positions
+    __shared__ V vbuf[2][kUpdThreads];
+    __shared__ int32_t ebuf[2][kUpdThreads];
+    __shared__ uint32_t s_u;
+    __shared__ MathLds M;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    if (sizeof(P) == 4 && sizeof(V) == 4) math_lds_fill(&M, tid, kUpdThreads);
+
+    // 1. keys = (leaf << 32) | batch position; out-of-range entries sort last.
+    uint64_t key = ~0ull;
+    if (tid < m) {
+        const int32_t l = idx[tid];
+        if (l >= 0 && (int64_t)l < cap) key = ((uint64_t)(uint32_t)l << 32) | (uint32_t)tid;
+    }
+    keys[tid] = key;
+    __syncthreads();
+    for (int size = 2; size <= kUpdThreads; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const int j = tid ^ stride;
+            if (j > tid) {
+                const uint64_t a = keys[tid];
+                const uint64_t b = keys[j];
+                const bool up = (tid & size) == 0;
+                if ((a > b) == up) {
+                    keys[tid] = b;
+                    keys[j] = a;
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    // 2. winners: the last key of each run of equal leaves.
+    const uint64_t my = keys[tid];
+    const uint64_t nx = tid + 1 < kUpdThreads ? keys[tid + 1] : ~0ull;
+    const bool win = my != ~0ull && (nx >> 32) != (my >> 32);
+    const uint64_t bal = __ballot(win);
+    if (lane == 0) wcount[wave] = (uint32_t)__popcll(bal);
+    __syncthreads();
+    uint32_t pos = (uint32_t)__popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+    uint32_t tot = 0;
+    for (int w2 = 0; w2 < kUpdThreads / kWave; ++w2) {
+        const uint32_t c = wcount[w2];
+        if (w2 < wave) pos += c;
+        tot += c;
+    }
+    if (win) {
+        wl[pos] = (int32_t)(my >> 32);
+        wj[pos] = (int32_t)(uint32_t)my;
+    }
+    if (tid == 0) s_u = tot;
+    __syncthreads();
+    const int u = (int)s_u;
+
+    // 3. per-winner state and the prefetch of all path siblings.
+    const bool act = tid < u;
+    int64_t L = 0, Lp = -1;
+    V val = V(0);
+    int32_t end = tid + 1;
+    V sib[kMaxDepth];
+    if (act) {
+        L = wl[tid];
+        Lp = tid > 0 ? (int64_t)wl[tid - 1] : -1;
+        val = leaf_value(prio[wj[tid]], alpha, &M);
+#pragma unroll
+        for (int d = 0; d < kMaxDepth; ++d)
+            if (d < D) sib[d] = tree[((cap + L) >> d) ^ 1];
+        tree[cap + L] = val;
+        vbuf[0][tid] = val;
+        ebuf[0][tid] = end;
+    }
+    __syncthreads();
+
+    // 4. levels 1..D (unrolled so that sib[] stays in registers).
+#pragma unroll
+    for (int d = 1; d <= kMaxDepth; ++d) {
+        if (d <= D) {
+            const int bi = (d - 1) & 1;
+            const int bo = d & 1;
+            const bool own = act && (tid == 0 || ((cap + Lp) >> d) != ((cap + L) >> d));
+            if (own) {
+                const int64_t c = (cap + L) >> (d - 1);
+                const int64_t N = c >> 1;
+                V left, right;
+                int32_t ne = end;
+                if ((c & 1) == 0) {
+                    left = val;
+                    const int32_t j = end;
+                    if (j < u && ((cap + (int64_t)wl[j]) >> d) == N) {
+                        right = vbuf[bi][j];
+                        ne = ebuf[bi][j];
+                    } else {
+                        right = sib[d - 1];
+                    }
+                } else {
+                    left = sib[d - 1];
+                    right = val;
+                }
+                val = left + right;
+                end = ne;
+                tree[N] = val;
+                vbuf[bo][tid] = val;
+                ebuf[bo][tid] = end;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+template <class V>
+__global__ __launch_bounds__(kSampleTreeThreads) void k_tree_sample(
+    const V* __restrict__ tree, int64_t cap, int D, int64_t n_valid, const void* __restrict__ u,
+    int64_t k, int stratified, int k_log2, int lt, int32_t* __restrict__ out) {
+    __shared__ V top[1 << TreeTop<V>::levels];
+    const int tid = threadIdx.x;
+    const int ntop = 1 << lt;
+    for (int i = tid; i < ntop; i += kSampleTreeThreads) top[i] = i > 0 ? tree[i] : V(0);
+    __syncthreads();
+    const int64_t i = (int64_t)blockIdx.x * kSampleTreeThreads + tid;
+    if (i >= k) return;
+    V t;
+    if constexpr (sizeof(V) == 4) {
+        const float root = top[1];
+        const float U = ((const float*)u)[i];
+        if (stratified) {
+            const double a = (double)i + (double)U;
+            const double b = a / (double)k;
+            t = (float)(b * (double)root);
+        } else {
+            t = U * root;
+        }
+    } else {
+        const uint64_t root = top[1];
+        t = int_threshold((uint64_t)i, ((const uint32_t*)u)[i], (uint64_t)k, root, stratified, k_log2);
+    }
+    int64_t node = 1;
+    for (int d = 0; d < D; ++d) {
+        const int64_t c = 2 * node;
+        V Lv, Rv;
+        if (c + 1 < ntop) {
+            Lv = top[c];
+            Rv = top[c + 1];
+        } else if constexpr (sizeof(V) == 4) {
+            const float2 pr = *reinterpret_cast<const float2*>(tree + c);
+            Lv = pr.x;
+            Rv = pr.y;
+        } else {
+            const ulonglong2 pr = *reinterpret_cast<const ulonglong2*>(tree + c);
+            Lv = pr.x;
+            Rv = pr.y;
+        }
+        if (t <= Lv || Rv == V(0)) {
+            node = c;
+        } else {
+            t = t - Lv;
+            node = c + 1;
+        }
+    }
+    const int64_t leaf = node - cap;
+    out[i] = (int32_t)(leaf < n_valid ? leaf : n_valid - 1);
+}
+
+template <class V, class P>
+static psamp_status launch_build(void* tree, int64_t cap, const void* prio, int64_t n_valid,
+                                 double alpha, hipStream_t st) {
+    const int D = ilog2_exact(cap);
+    int64_t cnt = cap;
+    bool from_prio = true;
+    if (D == 0) {   // a single leaf is the root
+        hipLaunchKernelGGL((k_tree_build_pass<V, P, true>), dim3(1), dim3(kBuildThreads), 0, st,
+                           (V*)tree, (int64_t)1, (const P*)prio, n_valid, alpha, 0);
+        return launch_status();
+    }
+    int done = 0;
+    while (done < D) {
+        const int s = min_(kBuildLevels, D - done);
+        const int64_t grid = cnt >> s;
+        if (trace_enabled()) trace_launch("k_tree_build_pass", grid, kBuildThreads, cnt);
+        if (from_prio)
+            hipLaunchKernelGGL((k_tree_build_pass<V, P, true>), dim3((unsigned)grid),
+                               dim3(kBuildThreads), 0, st, (V*)tree, cnt, (const P*)prio, n_valid,
+                               alpha, s);
+        else
+            hipLaunchKernelGGL((k_tree_build_pass<V, P, false>), dim3((unsigned)grid),
+                               dim3(kBuildThreads), 0, st, (V*)tree, cnt, (const P*)prio, n_valid,
+                               alpha, s);
+        psamp_status e = launch_status();
+        if (e != PSAMP_OK) return e;
+        from_prio = false;
+        cnt >>= s;
+        done += s;
+    }
+    return PSAMP_OK;
+}
+
+}  // namespace psamp
+
+using namespace psamp;
+
+extern "C" int64_t psamp_segtree_cap_pow2(int64_t capacity) {
+    if (capacity < 1 || capacity > (int64_t(1) << kMaxDepth)) return 0;
+    int64_t c = 1;
+    while (c < capacity) c <<= 1;
+    return c;
+}
+
+static psamp_status tree_types(psamp_dtype tree_t, psamp_dtype prio_t) {
+    if (tree_t == PSAMP_F32 && prio_t == PSAMP_F32) return PSAMP_OK;
+    if (tree_t == PSAMP_U64 && prio_t == PSAMP_U32) return PSAMP_OK;
+    return PSAMP_E_DTYPE;
+}
+
+extern "C" psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
+                                            const void* prio, psamp_dtype prio_t, int64_t n_valid,
+                                            double alpha, void* stream) {
+    if (!tree || !prio) return PSAMP_E_NULL;
+    if (!is_pow2(cap_pow2) || cap_pow2 > (int64_t(1) << kMaxDepth) || n_valid < 1 ||
+        n_valid > cap_pow2)
+        return PSAMP_E_SIZE;
+    if (tree_types(tree_t, prio_t) != PSAMP_OK) return PSAMP_E_DTYPE;
+    if (tree_t == PSAMP_F32 && !(finite_d(alpha) && alpha > 0.0)) return PSAMP_E_PARAM;
+    if (!aligned(tree, 16) || !aligned(prio, 4)) return PSAMP_E_ALIGN;
+    hipStream_t st = as_stream(stream);
+    if (tree_t == PSAMP_F32) return launch_build<float, float>(tree, cap_pow2, prio, n_valid, alpha, st);
+    return launch_build<uint64_t, uint32_t>(tree, cap_pow2, prio, n_valid, 0.0, st);
+}
+
+extern "C" size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m) {
+    (void)cap_pow2;
+    (void)m;
+    return 0;
+}
+
+extern "C" psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
+                                             const int32_t* idx, const void* prio,
+                                             psamp_dtype prio_t, int64_t m, double alpha, void* ws,
+                                             size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    if (!is_pow2(cap_pow2) || cap_pow2 > (int64_t(1) << kMaxDepth) || m < 0 || m > kMaxN)
+        return PSAMP_E_SIZE;
+    if (tree_types(tree_t, prio_t) != PSAMP_OK) return PSAMP_E_DTYPE;
+    if (tree_t == PSAMP_F32 && !(finite_d(alpha) && alpha > 0.0)) return PSAMP_E_PARAM;
+    if (m == 0) return PSAMP_OK;
+    if (!tree || !idx || !prio) return PSAMP_E_NULL;
+    if (!aligned(tree, 16) || !aligned(prio, 4) || !aligned(idx, 4)) return PSAMP_E_ALIGN;
+    hipStream_t st = as_stream(stream);
+    const int D = ilog2_exact(cap_pow2);
+    // Batches larger than one workgroup go in order, chunk by chunk: later
+    // chunks overwrite earlier ones, which keeps last-write-wins.
+    for (int64_t off = 0; off < m; off += kUpdThreads) {
+        const int mm = (int)min_<int64_t>(kUpdThreads, m - off);
+        if (trace_enabled()) trace_launch("k_tree_update", 1, kUpdThreads, mm);
+        if (tree_t == PSAMP_F32)
+            hipLaunchKernelGGL((k_tree_update<float, float>), dim3(1), dim3(kUpdThreads), 0, st,
+                               (float*)tree, cap_pow2, D, idx + off, (const float*)prio + off, mm,
+                               alpha);
+        else
+            hipLaunchKernelGGL((k_tree_update<uint64_t, uint32_t>), dim3(1), dim3(kUpdThreads), 0,
+                               st, (uint64_t*)tree, cap_pow2, D, idx + off,
+                               (const uint32_t*)prio + off, mm, 0.0);
+        psamp_status e = launch_status();
+        if (e != PSAMP_OK) return e;
+    }
+    return PSAMP_OK;
+}
+
+extern "C" psamp_status psamp_segtree_sample(const void* tree, psamp_dtype tree_t,
+                                             int64_t cap_pow2, int64_t n_valid, const void* u,
+                                             psamp_dtype u_t, int64_t k, int stratified,
+                                             int32_t* out_idx, void* stream) {
+    if (!is_pow2(cap_pow2) || cap_pow2 > (int64_t(1) << kMaxDepth) || n_valid < 1 ||
+        n_valid > cap_pow2 || k < 0 || k > kMaxN)
+        return PSAMP_E_SIZE;
+    if (stratified != 0 && stratified != 1) return PSAMP_E_PARAM;
+    const bool f = tree_t == PSAMP_F32 && u_t == PSAMP_F32;
+    const bool in = tree_t == PSAMP_U64 && u_t == PSAMP_U32;
+    if (!f && !in) return PSAMP_E_DTYPE;
+    if (k == 0) return PSAMP_OK;
+    if (!tree || !u || !out_idx) return PSAMP_E_NULL;
+    if (!aligned(tree, 16) || !aligned(u, 4) || !aligned(out_idx, 4)) return PSAMP_E_ALIGN;
+    hipStream_t st = as_stream(stream);
+    const int D = ilog2_exact(cap_pow2);
+    const int64_t grid = ceil_div(k, kSampleTreeThreads);
+    const int k_log2 = is_pow2(k) ? ilog2_exact(k) : -1;
+    if (trace_enabled()) trace_launch("k_tree_sample", grid, kSampleTreeThreads, k);
+    if (f) {
+        const int lt = min_(TreeTop<float>::levels, D + 1);
+        hipLaunchKernelGGL(k_tree_sample<float>, dim3((unsigned)grid), dim3(kSampleTreeThreads), 0,
+                           st, (const float*)tree, cap_pow2, D, n_valid, u, k, stratified, k_log2,
+                           lt, out_idx);
+    } else {
+        const int lt = min_(TreeTop<uint64_t>::levels, D + 1);
+        hipLaunchKernelGGL(k_tree_sample<uint64_t>, dim3((unsigned)grid),
+                           dim3(kSampleTreeThreads), 0, st, (const uint64_t*)tree, cap_pow2, D,
+                           n_valid, u, k, stratified, k_log2, lt, out_idx);
+    }
+    return launch_status();
+}

@@ -1,0 +1,140 @@
+"""The C-ABI library loads, exports every symbol include/psamp.h declares,
+and rejects bad arguments on the host before anything is enqueued.
+
+No call here reaches the GPU: every case fails validation first (the
+pointers passed are fake and never dereferenced)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "psamp.h")
+
+FAKE = 0x10000   # a 64 KiB-aligned non-null address that is never touched
+
+
+@pytest.fixture(scope="module")
+def L():
+    import proportional_sampling_amd as ps
+    if not os.path.exists(ps.LIB_PATH):
+        from proportional_sampling_amd import build
+        build.build(verbose=False)
+    return ps.lib()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(psamp_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    import proportional_sampling_amd as ps
+    names = header_functions()
+    assert len(names) >= 16
+    for n in names:
+        assert hasattr(L, n), n
+    # the binding declares exactly the header's functions
+    assert sorted(ps.SIGNATURES) == names
+
+
+def test_status_strings_and_version(L):
+    assert L.psamp_abi_version() == 1
+    assert L.psamp_status_string(0) == b"ok"
+    assert L.psamp_status_string(5) == b"workspace missing or too small"
+    assert L.psamp_status_string(99) == b"unknown status"
+
+
+def test_workspace_sizes(L):
+    assert L.psamp_build_cdf_workspace_size(0) == 0
+    assert L.psamp_build_cdf_workspace_size(1) == 256 + 32
+    assert L.psamp_build_cdf_workspace_size(1 << 24) == 256 + 32 * (1 << 14)
+    assert L.psamp_is_weights_workspace_size(8192) == 0
+    assert L.psamp_is_weights_workspace_size(1 << 20) == 256 + 4 * 256
+    assert L.psamp_scatter_workspace_size(262144, 8192) == 262144 * 4
+    assert L.psamp_segtree_cap_pow2(500000) == 524288
+    assert L.psamp_segtree_cap_pow2(100000) == 131072
+    assert L.psamp_segtree_cap_pow2(1) == 1
+    assert L.psamp_segtree_cap_pow2(0) == 0
+    assert L.psamp_segtree_cap_pow2((1 << 30) + 1) == 0
+
+
+F32, F64, U32, U64, I32 = 0, 1, 2, 3, 4
+OK, E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WS, E_ALIGN = 0, 1, 2, 3, 4, 5, 6
+
+
+def test_build_cdf_validation(L):
+    ws = L.psamp_build_cdf_workspace_size(1000)
+    f = L.psamp_build_cdf
+    assert f(None, F32, 1000, 0.6, FAKE, F64, FAKE, FAKE, ws, None) == E_NULL
+    assert f(FAKE, F32, 0, 0.6, FAKE, F64, FAKE, FAKE, ws, None) == E_SIZE
+    assert f(FAKE, F32, 1 << 31, 0.6, FAKE, F64, FAKE, FAKE, ws, None) == E_SIZE
+    assert f(FAKE, F32, 1000, 0.6, FAKE, U64, FAKE, FAKE, ws, None) == E_DTYPE
+    assert f(FAKE, U32, 1000, 0.6, FAKE, F64, FAKE, FAKE, ws, None) == E_DTYPE
+    assert f(FAKE, F32, 1000, 0.0, FAKE, F64, FAKE, FAKE, ws, None) == E_PARAM
+    assert f(FAKE, F32, 1000, float("nan"), FAKE, F64, FAKE, FAKE, ws, None) == E_PARAM
+    assert f(FAKE, F32, 1000, float("inf"), FAKE, F64, FAKE, FAKE, ws, None) == E_PARAM
+    assert f(FAKE, F32, 1000, 0.6, FAKE, F64, FAKE, None, ws, None) == E_WS
+    assert f(FAKE, F32, 1000, 0.6, FAKE, F64, FAKE, FAKE, ws - 1, None) == E_WS
+    assert f(FAKE + 2, F32, 1000, 0.6, FAKE, F64, FAKE, FAKE, ws, None) == E_ALIGN
+    assert f(FAKE, F32, 1000, 0.6, FAKE + 4, F64, FAKE, FAKE, ws, None) == E_ALIGN
+
+
+def test_sample_validation(L):
+    f = L.psamp_sample
+    assert f(FAKE, F64, 0, FAKE, FAKE, F32, 10, 1, FAKE, None) == E_SIZE
+    assert f(FAKE, F64, 10, FAKE, FAKE, F32, -1, 1, FAKE, None) == E_SIZE
+    assert f(FAKE, F64, 10, FAKE, FAKE, F32, 10, 2, FAKE, None) == E_PARAM
+    assert f(FAKE, F64, 10, FAKE, FAKE, U32, 10, 1, FAKE, None) == E_DTYPE
+    assert f(FAKE, U64, 10, FAKE, FAKE, F32, 10, 1, FAKE, None) == E_DTYPE
+    assert f(FAKE, F64, 10, FAKE, FAKE, F32, 0, 1, None, None) == OK      # k = 0: no-op
+    assert f(FAKE, F64, 10, None, FAKE, F32, 10, 1, FAKE, None) == E_NULL
+
+
+def test_is_weights_validation(L):
+    f = L.psamp_is_weights
+    assert f(FAKE, F64, 10, 0.6, FAKE, 5, 0.4, FAKE, None, 0, None) == E_DTYPE
+    assert f(FAKE, F32, 10, 0.6, FAKE, 5, -0.1, FAKE, None, 0, None) == E_PARAM
+    assert f(FAKE, F32, 10, -1.0, FAKE, 5, 0.4, FAKE, None, 0, None) == E_PARAM
+    assert f(FAKE, F32, 10, 0.6, FAKE, 1 << 20, 0.4, FAKE, None, 0, None) == E_WS
+    assert f(FAKE, F32, 10, 0.6, FAKE, 0, 0.4, None, None, 0, None) == OK
+    assert f(None, F32, 10, 0.6, FAKE, 5, 0.4, FAKE, None, 0, None) == E_NULL
+
+
+def test_segtree_validation(L):
+    b, u, s = L.psamp_segtree_build, L.psamp_segtree_update, L.psamp_segtree_sample
+    assert b(FAKE, F32, 1000, FAKE, F32, 10, 0.6, None) == E_SIZE          # not a power of 2
+    assert b(FAKE, F32, 1024, FAKE, F32, 1025, 0.6, None) == E_SIZE        # n_valid > cap
+    assert b(FAKE, F32, 1024, FAKE, U32, 10, 0.6, None) == E_DTYPE
+    assert b(FAKE, U64, 1024, FAKE, F32, 10, 0.6, None) == E_DTYPE
+    assert b(FAKE, F32, 1024, FAKE, F32, 10, 0.0, None) == E_PARAM
+    assert b(FAKE + 8, F32, 1024, FAKE, F32, 10, 0.6, None) == E_ALIGN
+    assert b(None, F32, 1024, FAKE, F32, 10, 0.6, None) == E_NULL
+    assert u(FAKE, F32, 1024, FAKE, FAKE, F32, 0, 0.6, None, 0, None) == OK
+    assert u(FAKE, F32, 1024, FAKE, FAKE, F32, -1, 0.6, None, 0, None) == E_SIZE
+    assert u(FAKE, F32, 1024, None, FAKE, F32, 4, 0.6, None, 0, None) == E_NULL
+    assert s(FAKE, F32, 1024, 0, FAKE, F32, 4, 0, FAKE, None) == E_SIZE
+    assert s(FAKE, F32, 1024, 10, FAKE, U32, 4, 0, FAKE, None) == E_DTYPE
+    assert s(FAKE, F32, 1024, 10, FAKE, F32, 4, 3, FAKE, None) == E_PARAM
+
+
+def test_resample_and_scatter_validation(L):
+    r = L.psamp_resample_rows
+    assert r(FAKE, 4, 4096, 4095, FAKE, FAKE, 4096, None) == E_SIZE
+    assert r(FAKE, 4, 8193, 8193, FAKE, FAKE, 8193, None) == E_SIZE
+    assert r(FAKE, 0, 4096, 4096, FAKE, FAKE, 4096, None) == E_SIZE
+    assert r(None, 4, 4096, 4096, FAKE, FAKE, 4096, None) == E_NULL
+    sc = L.psamp_scatter_lww
+    assert sc(FAKE, F64, 100, FAKE, FAKE, 10, FAKE, 400, None) == E_DTYPE
+    assert sc(FAKE, F32, 100, FAKE, FAKE, 10, FAKE, 399, None) == E_WS
+    assert sc(FAKE, F32, 100, FAKE, FAKE, 0, None, 0, None) == OK
+    assert L.psamp_workspace_errors(None, 256, None, None) == E_NULL
+
+
+def test_binding_fails_loudly_without_gpu_tensors():
+    import torch
+    import proportional_sampling_amd as ps
+    with pytest.raises(ValueError):
+        ps.build_cdf(torch.ones(10, dtype=torch.float32), 0.6, ws=None)

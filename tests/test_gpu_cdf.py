@@ -1,0 +1,249 @@
+"""GPU parity of the CDF path (scan, search, IS weights, rewrite) against
+the CPU oracle, through the C ABI (proportional_sampling_amd binding)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from parity_util import assert_indices, rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ps():
+    import proportional_sampling_amd as ps
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ps.lib()
+    return ps
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+SIZES = [1, 2, 63, 64, 1023, 1024, 1025, 4095, 4096, 4097, 65536 + 3, 100003,
+         (1 << 20), (1 << 20) + 1, (1 << 22) + 17]
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_scan_int_bit_exact(ps, n):
+    say(f"scan int n={n}")
+    q = si.sweep_u32(n)
+    C_o, T_o = oracle.build_cdf_int(q)
+    cdf, tot = ps.build_cdf(dev(q))
+    C_g = host(cdf)
+    assert C_g.dtype == np.uint64
+    assert np.array_equal(C_g, C_o)
+    assert int(host(tot)[0]) == T_o
+
+
+@pytest.mark.parametrize("n", SIZES)
+def test_scan_fp(ps, n):
+    say(f"scan fp n={n}")
+    p = si.sweep_f32(n)
+    C_o, T_o = oracle.build_cdf(p, 0.7)
+    ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+    cdf, tot = ps.build_cdf(dev(p), 0.7, ws=ws)
+    C_g = host(cdf)
+    e = rel_err(C_g, C_o)
+    say(f"  max rel CDF err {e:.3e}")
+    assert e <= 1e-6
+    assert e <= 1e-12            # what fp64 weights and sums actually give
+    assert host(tot)[0] == C_g[-1]
+    # deterministic: the same bits on a second run with the same workspace
+    cdf2, _ = ps.build_cdf(dev(p), 0.7, ws=ws)
+    assert np.array_equal(host(cdf2), C_g)
+    assert ws.errors() == 0
+
+
+def test_scan_all_ones_exact(ps):
+    n = (1 << 21) + 5
+    cdf, tot = ps.build_cdf(torch.ones(n, dtype=torch.float32, device="cuda"), 0.6)
+    assert np.array_equal(host(cdf), np.arange(1, n + 1, dtype=np.float64))
+    assert host(tot)[0] == float(n)
+
+
+def test_scan_f32_cdf_variant(ps):
+    p = si.sweep_f32(300007)
+    C_o, T_o = oracle.build_cdf(p, 0.7)
+    cdf, tot = ps.build_cdf(dev(p), 0.7, cdf_dtype=torch.float32)
+    C_g = host(cdf)
+    assert C_g.dtype == np.float32
+    assert rel_err(C_g, C_o) <= 1e-6
+    assert host(tot)[0] == C_g[-1]
+
+
+def test_scan_workspace_reuse_across_sizes(ps):
+    # alternate parities and sizes on one workspace; zeros and a tail
+    ws = ps.Workspace(ps.build_cdf_workspace_size(1 << 21))
+    for n in [(1 << 21), 7, 5000, (1 << 21) - 3, 1, 300000, 4096]:
+        q = si.sweep_u32(n)
+        q[::7] = 0
+        C_o, T_o = oracle.build_cdf_int(q)
+        cdf, tot = ps.build_cdf(dev(q), ws=ws)
+        assert np.array_equal(host(cdf), C_o), n
+    assert ws.errors() == 0
+
+
+def test_scan_unaligned_views(ps):
+    q = si.sweep_u32(100001)
+    t = dev(q)
+    sub = t[3:]                      # 12-byte offset: scalar path
+    C_o, _ = oracle.build_cdf_int(q[3:])
+    cdf = torch.empty(sub.numel() + 1, dtype=torch.uint64, device="cuda")[1:]
+    ps.build_cdf(sub, cdf=cdf)
+    assert np.array_equal(host(cdf), C_o)
+
+
+def _per_round(ps, p, U, alpha, beta, ws=None):
+    Pd = dev(p)
+    cdf, tot = ps.build_cdf(Pd, alpha, ws=ws)
+    idx = ps.sample(cdf, tot, dev(U), stratified=True)
+    w = ps.is_weights(Pd, idx, alpha, beta)
+    return host(cdf), host(tot)[0], host(idx), host(w)
+
+
+def test_per_small_cfg(ps):
+    d = si.per_small()
+    say("PER small: B=8192 k=1024")
+    C_o, T_o, t_o, idx_o = oracle.sample(d["p"], d["alpha"], d["U"], True)
+    C_g, T_g, idx_g, w_g = _per_round(ps, d["p"], d["U"], d["alpha"], d["beta"])
+    assert rel_err(C_g, C_o) <= 1e-6
+    assert_indices(idx_g, idx_o, t_o, C_o, T_o, "per_small")
+    assert np.all(np.diff(idx_g) >= 0)
+    w_o = oracle.is_weights(d["p"], d["alpha"], T_o, idx_o, d["beta"])
+    if np.array_equal(idx_g, idx_o):
+        e = rel_err(w_g, w_o)
+        say(f"  IS max rel err {e:.3e}")
+        assert e <= 1e-6
+    assert w_g.max() == 1.0
+
+
+@pytest.mark.parametrize("k,strat", [(1, True), (7, True), (1000, True), (1024, False),
+                                     (5000, True), (8192, True), (8193, True), (100000, False),
+                                     (1 << 18, True)])
+def test_sample_and_weights_shapes(ps, k, strat):
+    say(f"sample k={k} stratified={strat}")
+    p = si.generic_f32(262144, 77 + k, "exp")
+    U = si.uniform_f32(np.random.default_rng(k), k)
+    C_o, T_o, t_o, idx_o = oracle.sample(p, 0.6, U, strat)
+    Pd = dev(p)
+    cdf, tot = ps.build_cdf(Pd, 0.6)
+    idx = host(ps.sample(cdf, tot, dev(U), stratified=strat))
+    assert_indices(idx, idx_o, t_o, C_o, T_o, f"k={k}")
+    w_g = host(ps.is_weights(Pd, dev(idx), 0.6, 0.4))
+    w_o = oracle.is_weights(p, 0.6, T_o, idx_o, 0.4)
+    if np.array_equal(idx, idx_o):
+        assert rel_err(w_g, w_o) <= 1e-6
+    assert w_g.max() == 1.0 and np.all(w_g > 0)
+
+
+def test_sample_edges(ps):
+    # zero-weight items, ties, t = 0 (U = 0 at i = 0), and the clamp
+    p = np.array([0.0, 2.0, 0.0, 0.0, 1.0, 0.0], np.float32)
+    U = np.array([0.0, 0.5, 0.999999, 0.0], np.float32)
+    for strat in (True, False):
+        C_o, T_o, t_o, idx_o = oracle.sample(p, 1.0, U, strat)
+        cdf, tot = ps.build_cdf(dev(p), 1.0)
+        idx = host(ps.sample(cdf, tot, dev(U), stratified=strat))
+        assert_indices(idx, idx_o, t_o, C_o, T_o, f"edges strat={strat}")
+    # a single item
+    cdf, tot = ps.build_cdf(dev(np.array([3.0], np.float32)), 0.5)
+    assert list(host(ps.sample(cdf, tot, dev(np.array([0.0, 0.7], np.float32))))) == [0, 0]
+
+
+@pytest.mark.parametrize("k,strat", [(1, True), (1000, True), (1 << 16, True), (1000, False),
+                                     (4099, False)])
+def test_sample_int_bit_exact(ps, k, strat):
+    say(f"sample int k={k} stratified={strat}")
+    d = si.per_large_int(n=300007, k=k)
+    C_o, T_o, t_o, idx_o = oracle.sample_int(d["q"], d["r"], strat)
+    Q = dev(d["q"])
+    cdf, tot = ps.build_cdf(Q)
+    idx = host(ps.sample(cdf, tot, dev(d["r"]), stratified=strat))
+    assert np.array_equal(idx, idx_o)
+    w_g = host(ps.is_weights(Q, dev(idx), 1.0, d["beta"]))
+    w_o = oracle.is_weights_int(d["q"], T_o, idx_o, d["beta"])
+    assert rel_err(w_g, w_o) <= 1e-6
+
+
+def test_per_mid_cfg_32_rounds(ps):
+    """PER mid: B=262144, 32 updates of (CDF rebuild, 8192 stratified draws,
+    IS weights, rewrite of the drawn priorities).  The oracle runs its own
+    chain; both must agree on every index of every round."""
+    d = si.per_mid()
+    n, k = d["p0"].size, d["U"].shape[1]
+    p_o = d["p0"].copy()
+    Pd = dev(d["p0"])
+    ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+    sws = ps.Workspace(ps.scatter_workspace_size(n, k))
+    exc_total = 0
+    for r in range(d["U"].shape[0]):
+        C_o, T_o, t_o, idx_o = oracle.sample(p_o, d["alpha"], d["U"][r], True)
+        cdf, tot = ps.build_cdf(Pd, d["alpha"], ws=ws)
+        idx = ps.sample(cdf, tot, dev(d["U"][r]), stratified=True)
+        w = ps.is_weights(Pd, idx, d["alpha"], d["beta"])
+        ps.scatter_lww(Pd, idx, dev(d["v"][r]), sws)
+        idx_g = host(idx)
+        exc = assert_indices(idx_g, idx_o, t_o, C_o, T_o, f"per_mid round {r}")
+        exc_total += exc
+        assert exc == 0, "chains would fork; the oracle never takes GPU data"
+        w_o = oracle.is_weights(p_o, d["alpha"], T_o, idx_o, d["beta"])
+        assert rel_err(host(w), w_o) <= 1e-6
+        p_o = oracle.scatter_lww(p_o, idx_o, d["v"][r])
+        assert np.array_equal(host(Pd), p_o)
+    assert exc_total < 1e-4 * k * d["U"].shape[0]
+
+
+def test_scatter_lww(ps):
+    n = 10000
+    rng = np.random.default_rng(5)
+    p = si.generic_f32(n, 6)
+    Pd = dev(p)
+    ws = ps.Workspace(ps.scatter_workspace_size(n, 1))
+    for m in (1, 100, 5000, 30000):
+        idx = rng.integers(-3, n + 3, m).astype(np.int32)     # some out of range
+        v = si.generic_f32(m, m)
+        ok = (idx >= 0) & (idx < n)
+        p = oracle.scatter_lww(p, idx[ok], v[ok])
+        ps.scatter_lww(Pd, dev(idx), dev(v), ws)
+        assert np.array_equal(host(Pd), p), m
+    # the owner words are all zero again after each call
+    assert int(host(ws.buf).astype(np.int64).sum()) == 0
+
+
+def test_per_large_cfg(ps):
+    """PER large: B=2^24 LogNormal(0,2), alpha=0.7, beta=0.5, 2^20 draws."""
+    d = si.per_large()
+    say("PER large: oracle (serial) ...")
+    C_o, T_o, t_o, idx_o = oracle.sample(d["p"], d["alpha"], d["U"], True)
+    say("PER large: GPU ...")
+    C_g, T_g, idx_g, w_g = _per_round(ps, d["p"], d["U"], d["alpha"], d["beta"])
+    e = rel_err(C_g, C_o)
+    say(f"  max rel CDF err {e:.3e}; T gpu {T_g!r} oracle {T_o!r}")
+    assert e <= 1e-6
+    assert_indices(idx_g, idx_o, t_o, C_o, T_o, "per_large")
+    w_o = oracle.is_weights(d["p"], d["alpha"], T_o, idx_o, d["beta"])
+    if np.array_equal(idx_g, idx_o):
+        assert rel_err(w_g, w_o) <= 1e-6
+
+
+def test_per_large_int_cfg(ps):
+    d = si.per_large_int()
+    C_o, T_o, t_o, idx_o = oracle.sample_int(d["q"], d["r"], True)
+    Q = dev(d["q"])
+    cdf, tot = ps.build_cdf(Q)
+    assert np.array_equal(host(cdf), C_o)
+    assert int(host(tot)[0]) == T_o
+    idx = host(ps.sample(cdf, tot, dev(d["r"]), stratified=True))
+    assert np.array_equal(idx, idx_o)
+    w_g = host(ps.is_weights(Q, dev(idx), 1.0, d["beta"]))
+    w_o = oracle.is_weights_int(d["q"], T_o, idx_o, d["beta"])
+    assert rel_err(w_g, w_o) <= 1e-6

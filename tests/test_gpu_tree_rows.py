@@ -1,0 +1,206 @@
+"""GPU parity of the sum tree and of row resampling against the CPU oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synthetic_inputs as si
+from parity_util import assert_indices, say, ulp_diff_f32
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ps():
+    import proportional_sampling_amd as ps
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ps.lib()
+    return ps
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def check_f32_tree(flat_g, otree, cap, what):
+    """Leaves equal bit for bit (they are p^alpha rounded to float on both
+    sides), then every node equal to the oracle's."""
+    flat_o = otree.flat()
+    lg, lo = flat_g[cap:], flat_o[cap:]
+    if not np.array_equal(lg, lo):
+        d = ulp_diff_f32(lg, lo)
+        raise AssertionError(f"{what}: {np.count_nonzero(d)} leaves differ (max {d.max()} ulp)")
+    assert np.array_equal(flat_g[1:], flat_o[1:]), what
+
+
+@pytest.mark.parametrize("cap,n_valid", [(1, 1), (2, 1), (8, 5), (1024, 1000), (4096, 4096),
+                                         (1 << 19, 500000), (1 << 22, (1 << 22) - 9)])
+def test_tree_build(ps, cap, n_valid):
+    say(f"tree build cap={cap} n_valid={n_valid}")
+    p = si.generic_f32(n_valid, cap + 3, "uniform")
+    tree = torch.zeros(2 * cap, dtype=torch.float32, device="cuda")
+    ps.segtree_build(tree, dev(p), 0.6)
+    ot = oracle.Tree("f32", cap).build(p, n_valid, 0.6)
+    check_f32_tree(host(tree), ot, cap, "build f32")
+    q = si.sweep_u32(n_valid)
+    treeq = torch.zeros(2 * cap, dtype=torch.uint64, device="cuda")
+    ps.segtree_build(treeq, dev(q))
+    otq = oracle.Tree("u64", cap).build(q, n_valid)
+    assert np.array_equal(host(treeq)[1:], otq.flat()[1:])
+
+
+def test_sumtree_cfg_rounds(ps):
+    """Sum tree: cap 2^19 (500000 valid), 1000 rounds of a 1024-entry batch
+    update (duplicates kept, last write wins) then 1024 iid descents."""
+    d = si.sumtree()
+    cap, nv, a = 1 << 19, 500000, d["alpha"]
+    tree = torch.zeros(2 * cap, dtype=torch.float32, device="cuda")
+    ps.segtree_build(tree, dev(d["p0"]), a)
+    ot = oracle.Tree("f32", cap).build(d["p0"], nv, a)
+    check_f32_tree(host(tree), ot, cap, "initial build")
+    rounds = d["idx"].shape[0]
+    for r in range(rounds):
+        ps.segtree_update(tree, dev(d["idx"][r]), dev(d["v"][r]), a)
+        idx_g = host(ps.segtree_sample(tree, nv, dev(d["U"][r])))
+        ot.update(d["idx"][r], d["v"][r], a)
+        idx_o = ot.sample(d["U"][r], nv, stratified=False)
+        if r % 100 == 0 or r == rounds - 1:
+            say(f"sumtree round {r}")
+            check_f32_tree(host(tree), ot, cap, f"round {r}")
+        assert np.array_equal(idx_g, idx_o), f"round {r}"
+    check_f32_tree(host(tree), ot, cap, "final")
+
+
+def _stress_batches(cap, rng):
+    m = 1024
+    yield "one leaf", np.full(m, 17, np.int32)
+    yield "sibling pairs", (np.arange(m) % 64).astype(np.int32) ^ (np.arange(m) % 2)
+    yield "one subtree", rng.integers(4096, 4096 + 256, m).astype(np.int32)
+    yield "ascending", np.arange(m, dtype=np.int32) * (cap // m)
+    yield "descending dup", np.repeat(np.arange(m // 4, dtype=np.int32)[::-1] * 3, 4)
+    yield "random", rng.integers(0, cap, m).astype(np.int32)
+    yield "small batch", rng.integers(0, cap, 3).astype(np.int32)
+    yield "with out-of-range", np.where(rng.random(m) < 0.1, -1,
+                                        rng.integers(0, cap, m)).astype(np.int32)
+    yield "two chunks", rng.integers(0, 64, 2500).astype(np.int32)
+
+
+@pytest.mark.parametrize("kind", ["f32", "u64"])
+def test_tree_update_stress(ps, kind):
+    cap = 1 << 16
+    rng = np.random.default_rng(9)
+    if kind == "f32":
+        p0 = si.generic_f32(cap, 1, "uniform")
+        tree = torch.zeros(2 * cap, dtype=torch.float32, device="cuda")
+        ps.segtree_build(tree, dev(p0), 0.6)
+        ot = oracle.Tree("f32", cap).build(p0, cap, 0.6)
+    else:
+        p0 = si.sweep_u32(cap)
+        tree = torch.zeros(2 * cap, dtype=torch.uint64, device="cuda")
+        ps.segtree_build(tree, dev(p0))
+        ot = oracle.Tree("u64", cap).build(p0, cap)
+    for name, idx in _stress_batches(cap, rng):
+        say(f"stress {kind}: {name}")
+        m = idx.size
+        if kind == "f32":
+            v = si.generic_f32(m, m + 11, "uniform")
+            ps.segtree_update(tree, dev(idx), dev(v), 0.6)
+            ok = (idx >= 0) & (idx < cap)
+            ot.update(idx[ok], v[ok], 0.6)
+            check_f32_tree(host(tree), ot, cap, name)
+        else:
+            v = si.sweep_u32(m)
+            ps.segtree_update(tree, dev(idx), dev(v))
+            ok = (idx >= 0) & (idx < cap)
+            ot.update(idx[ok], v[ok])
+            assert np.array_equal(host(tree)[1:], ot.flat()[1:]), name
+        # the tree equals a fresh build of its own leaves
+        flat = host(tree)
+        j = np.arange(1, cap)
+        s = (flat[2 * j] + flat[2 * j + 1]).astype(flat.dtype)
+        assert np.array_equal(flat[1:cap], s), name
+
+
+@pytest.mark.parametrize("k,strat", [(1, False), (1024, False), (1000, True), (1 << 16, True)])
+def test_tree_sample_int_matches_cdf_path(ps, k, strat):
+    d = si.per_large_int(n=300000, k=k)
+    cap = ps.segtree_cap_pow2(300000)
+    tree = torch.zeros(2 * cap, dtype=torch.uint64, device="cuda")
+    Q = dev(d["q"])
+    ps.segtree_build(tree, Q)
+    idx_t = host(ps.segtree_sample(tree, 300000, dev(d["r"]), stratified=strat))
+    _, _, _, idx_o = oracle.sample_int(d["q"], d["r"], strat)
+    assert np.array_equal(idx_t, idx_o)
+
+
+def test_per_large_tree_path(ps):
+    """PER large, the same 2^20 draws through a 2^24-leaf sum tree: F32 tree
+    bit-exact against the oracle's pointer tree; U64 tree identical to the
+    integer CDF path."""
+    d = si.per_large()
+    n = d["p"].size
+    cap = n
+    say("PER large tree: oracle build (2^24 pointer tree) ...")
+    ot = oracle.Tree("f32", cap).build(d["p"], n, d["alpha"])
+    tree = torch.zeros(2 * cap, dtype=torch.float32, device="cuda")
+    ps.segtree_build(tree, dev(d["p"]), d["alpha"])
+    check_f32_tree(host(tree), ot, cap, "per_large f32 tree")
+    idx_g = host(ps.segtree_sample(tree, n, dev(d["U"]), stratified=True))
+    idx_o = ot.sample(d["U"], n, stratified=True)
+    assert np.array_equal(idx_g, idx_o)
+    del ot
+    di = si.per_large_int()
+    treeq = torch.zeros(2 * cap, dtype=torch.uint64, device="cuda")
+    ps.segtree_build(treeq, dev(di["q"]))
+    idx_t = host(ps.segtree_sample(treeq, n, dev(di["r"]), stratified=True))
+    _, _, _, idx_c = oracle.sample_int(di["q"], di["r"], True)
+    assert np.array_equal(idx_t, idx_c)
+
+
+# ------------------------------------------------------------ resampling
+def _row_check(lw, u_row, anc_g, what):
+    anc_o = oracle.resample_rows(lw, u_row)
+    if np.array_equal(anc_g, anc_o):
+        say(f"{what}: identical")
+        return
+    P = lw.shape[1]
+    unexc = exc = 0
+    for b in np.nonzero(np.any(anc_g != anc_o, axis=1))[0]:
+        _, Cc = oracle.row_cdf(lw[b])
+        uk = ((np.arange(P, dtype=np.float32) + u_row[b]) / np.float32(P)).astype(np.float64)
+        from parity_util import excuse_counts
+        a, e = excuse_counts(anc_g[b], anc_o[b], uk, Cc, 1.0)
+        unexc += a
+        exc += e
+    say(f"{what}: unexcused={unexc} excused={exc}")
+    assert unexc == 0 and exc < 1e-4 * anc_g.size
+
+
+def test_resample_cfg(ps):
+    """Particle resampling: 1024 rows x 4096 particles, log-weights N(0, 3^2)."""
+    d = si.resample()
+    anc = host(ps.resample_rows(dev(d["lw"]), dev(d["u_row"])))
+    _row_check(d["lw"], d["u_row"], anc, "resample cfg")
+    assert np.all(np.diff(anc, axis=1) >= 0)
+
+
+@pytest.mark.parametrize("rows,P", [(3, 1), (5, 7), (16, 1000), (16, 1024), (8, 1025),
+                                    (8, 3000), (4, 8192), (2, 8191)])
+def test_resample_shapes(ps, rows, P):
+    d = si.resample(seed=P, rows=rows, P=P, sigma=2.0)
+    anc = host(ps.resample_rows(dev(d["lw"]), dev(d["u_row"])))
+    _row_check(d["lw"], d["u_row"], anc, f"resample {rows}x{P}")
+
+
+def test_resample_uniform_identity(ps):
+    P = 4096
+    lw = np.zeros((8, P), np.float32)
+    lw[3] = -7.5
+    u = np.linspace(0.01, 0.99, 8).astype(np.float32)
+    anc = host(ps.resample_rows(dev(lw), dev(u)))
+    assert np.array_equal(anc, np.tile(np.arange(P, dtype=np.int32), (8, 1)))
