@@ -71,7 +71,6 @@ class PerMid:
         self.idx = torch.empty(self.k, dtype=torch.int32, device="cuda")
         self.w = torch.empty(self.k, dtype=torch.float32, device="cuda")
         self.ws = ps.Workspace(ps.build_cdf_workspace_size(self.n))
-        self.sws = ps.Workspace(ps.scatter_workspace_size(self.n, self.k))
 
     def step(self, events=None):
         ps = self.ps
@@ -83,7 +82,8 @@ class PerMid:
                                              out=self.idx)),
                 ("is_weights", lambda: ps.is_weights(self.p, self.idx, self.alpha, self.beta,
                                                      out=self.w)),
-                ("scatter_lww", lambda: ps.scatter_lww(self.p, self.idx, self.v[r], self.sws)),
+                ("scatter_lww", lambda: ps.scatter_lww(self.p, self.idx, self.v[r],
+                                                       grouped=True)),
             )
             for name, fn in calls:
                 if events is None:
@@ -102,7 +102,7 @@ class PerMid:
             "build_cdf": 12 * n,                                   # f32 in, f64 out
             "sample": 8 * k + min(8 * n, 64 * k),                  # U in, idx out, CDF lines
             "is_weights": 8 * k + min(4 * n, 64 * k),              # idx in, w out, p lines
-            "scatter_lww": 8 * k + 4 * k + 4 * k * 2,              # idx, vals, prio, owner r/w
+            "scatter_lww": 8 * k + 4 * k,                          # idx, vals in; prio out
         }[name]
 
 
@@ -110,7 +110,7 @@ KERNEL_NAMES = {
     "build_cdf": "k_build_cdf<4, float, double>",
     "sample": "k_sample_fp<double>",
     "is_weights": "k_isw_single<float>",
-    "scatter_lww": "k_scatter_claim + k_scatter_apply",
+    "scatter_lww": "k_scatter_grouped",
 }
 
 

@@ -198,12 +198,19 @@ psamp_status psamp_resample_rows(const float* logw, int64_t rows, int64_t P,
  * update_priorities_gpu): prio[idx_j] = vals_j for j = 0..m-1, the largest
  * j winning on repeated indices; indices outside [0, n) are ignored.
  * prio_t / vals: PSAMP_F32 or PSAMP_U32 (same dtype for both).
- * ws: psamp_scatter_workspace_size(n, m) bytes (one uint32 per item).
- * Errors: E_NULL, E_SIZE, E_DTYPE, E_WORKSPACE, E_LAUNCH.
+ * flags: 0, or PSAMP_SCATTER_GROUPED when equal indices are adjacent in idx
+ *   (true of the non-decreasing output of stratified psamp_sample): then one
+ *   atomic-free kernel runs and ws may be NULL.  A false promise gives
+ *   unspecified (but in-bounds) results.
+ * ws: psamp_scatter_workspace_size(n, m) bytes (one uint32 per item, zeroed
+ *   once; every call leaves it zeroed again), unless GROUPED.
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (unknown flag), E_WORKSPACE,
+ * E_LAUNCH.
  * ---------------------------------------------------------------------- */
+#define PSAMP_SCATTER_GROUPED 1
 size_t psamp_scatter_workspace_size(int64_t n, int64_t m);
 psamp_status psamp_scatter_lww(void* prio, psamp_dtype prio_t, int64_t n,
-                               const int32_t* idx, const void* vals, int64_t m,
+                               const int32_t* idx, const void* vals, int64_t m, int flags,
                                void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------

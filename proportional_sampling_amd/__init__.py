@@ -49,7 +49,7 @@ SIGNATURES = {
     "psamp_segtree_sample": (_int, [_p, _int, _i64, _i64, _p, _int, _i64, _int, _p, _p]),
     "psamp_resample_rows": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p]),
     "psamp_scatter_workspace_size": (_sz, [_i64, _i64]),
-    "psamp_scatter_lww": (_int, [_p, _int, _i64, _p, _p, _i64, _p, _sz, _p]),
+    "psamp_scatter_lww": (_int, [_p, _int, _i64, _p, _p, _i64, _int, _p, _sz, _p]),
     "psamp_workspace_errors": (_int, [_p, _sz, C.POINTER(C.c_uint64), _p]),
 }
 
@@ -265,14 +265,24 @@ def scatter_workspace_size(n: int, m: int) -> int:
     return int(lib().psamp_scatter_workspace_size(int(n), int(m)))
 
 
-def scatter_lww(prio: torch.Tensor, idx: torch.Tensor, vals: torch.Tensor, ws: Workspace,
+SCATTER_GROUPED = 1
+
+
+def scatter_lww(prio: torch.Tensor, idx: torch.Tensor, vals: torch.Tensor,
+                ws: Workspace | None = None, *, grouped: bool = False,
                 stream=None) -> torch.Tensor:
+    """prio[idx_j] = vals_j, last j wins.  grouped=True promises that equal
+    indices are adjacent (sorted idx): one kernel, no workspace."""
     m = idx.numel()
     if vals.numel() != m or vals.dtype != prio.dtype:
         raise ValueError("vals must match idx in length and prio in dtype")
     p = _dev(prio, "prio", (torch.float32, torch.uint32))
     i = _dev(idx, "idx", (torch.int32,))
     v = _dev(vals, "vals", (torch.float32, torch.uint32))
+    if ws is None and not grouped:
+        ws = Workspace(scatter_workspace_size(prio.numel(), m), prio.device)
     _check("psamp_scatter_lww", lib().psamp_scatter_lww(
-        p, _DT[prio.dtype], prio.numel(), i, v, m, ws.ptr, ws.nbytes, _stream(stream)))
+        p, _DT[prio.dtype], prio.numel(), i, v, m, SCATTER_GROUPED if grouped else 0,
+        ws.ptr if ws is not None else None, ws.nbytes if ws is not None else 0,
+        _stream(stream)))
     return prio

@@ -3,6 +3,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+
 #include "psamp_host.h"
 
 namespace psamp {
@@ -13,6 +15,38 @@ bool trace_enabled() {
         return (e && e[0] == '1') ? 1 : 0;
     }();
     return on != 0;
+}
+
+// A small lock-protected cache: occupancy depends only on the kernel and the
+// device, so it is computed once per pair.
+int resident_grid(const void* fn, int block) {
+    struct Entry {
+        const void* fn;
+        int dev;
+        int block;
+        int value;
+    };
+    static std::mutex mu;
+    static Entry cache[64];
+    static int used = 0;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (int i = 0; i < used; ++i)
+            if (cache[i].fn == fn && cache[i].dev == dev && cache[i].block == block)
+                return cache[i].value;
+    }
+    int per_cu = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, 0) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    const int value = per_cu * cus;
+    std::lock_guard<std::mutex> lock(mu);
+    if (used < 64) cache[used++] = Entry{fn, dev, block, value};
+    return value;
 }
 
 void trace_launch(const char* kernel, int64_t grid, int block, int64_t n) {

@@ -49,26 +49,50 @@ __device__ __forceinline__ float is_weight(double pmin, double lpmin, double p, 
     return (float)exp2_tab(e * (lpmin - log2_sig32(p, M)), M);
 }
 
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) x = min_(x, (uint32_t)__shfl_xor((int)x, m));
+    return x;
+}
+
+// k <= 8192 in one workgroup: each thread owns up to 8 samples; all index
+// loads, then all priority gathers, are in flight together (two round
+// trips), the values stay in registers for the weights.
 template <class P>
 __global__ __launch_bounds__(kIswThreads) void k_isw_single(const P* __restrict__ prio, int64_t n,
                                                             const int32_t* __restrict__ idx,
                                                             int64_t k, double e,
                                                             float* __restrict__ out) {
+    constexpr int PER = (int)(kIswSingleMax / kIswThreads);
     __shared__ MathLds M;
     __shared__ uint32_t s_min;
     const int tid = threadIdx.x;
     math_lds_fill(&M, tid, kIswThreads);
     if (tid == 0) s_min = 0xFFFFFFFFu;
-    __syncthreads();
+    int32_t ii[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int64_t i = (int64_t)j * kIswThreads + tid;
+        ii[j] = i < k ? idx[i] : 0;
+    }
+    uint32_t key[PER];
     uint32_t mn = 0xFFFFFFFFu;
-    for (int64_t i = tid; i < k; i += kIswThreads) mn = min_(mn, prio_key<P>(prio[clamp_idx(idx[i], n)]));
-    atomicMin(&s_min, mn);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int64_t i = (int64_t)j * kIswThreads + tid;
+        key[j] = i < k ? prio_key<P>(prio[clamp_idx(ii[j], n)]) : 0xFFFFFFFFu;
+        mn = min_(mn, key[j]);
+    }
+    mn = wave_min_u32(mn);
+    __syncthreads();
+    if ((tid & 63) == 0) atomicMin(&s_min, mn);
     __syncthreads();
     const double pmin = prio_val<P>(s_min);
     const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
-    for (int64_t i = tid; i < k; i += kIswThreads) {
-        const double p = prio_val<P>(prio_key<P>(prio[clamp_idx(idx[i], n)]));
-        out[i] = is_weight(pmin, lpmin, p, e, &M);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        const int64_t i = (int64_t)j * kIswThreads + tid;
+        if (i < k) out[i] = is_weight(pmin, lpmin, prio_val<P>(key[j]), e, &M);
     }
 }
 

@@ -34,6 +34,10 @@ inline bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
 
 constexpr int64_t kMaxN = 0x7FFFFFFFll;   // int32 indices
 
+// Workgroups of `block` threads of kernel `fn` that fit on the current
+// device at once (CUs x resident per CU).  Cached per (kernel, device).
+int resident_grid(const void* fn, int block);
+
 // Optional launch trace: PSAMP_TRACE=1 prints one line per launch.
 bool trace_enabled();
 void trace_launch(const char* kernel, int64_t grid, int block, int64_t n);

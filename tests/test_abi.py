@@ -127,9 +127,10 @@ def test_resample_and_scatter_validation(L):
     assert r(FAKE, 0, 4096, 4096, FAKE, FAKE, 4096, None) == E_SIZE
     assert r(None, 4, 4096, 4096, FAKE, FAKE, 4096, None) == E_NULL
     sc = L.psamp_scatter_lww
-    assert sc(FAKE, F64, 100, FAKE, FAKE, 10, FAKE, 400, None) == E_DTYPE
-    assert sc(FAKE, F32, 100, FAKE, FAKE, 10, FAKE, 399, None) == E_WS
-    assert sc(FAKE, F32, 100, FAKE, FAKE, 0, None, 0, None) == OK
+    assert sc(FAKE, F64, 100, FAKE, FAKE, 10, 0, FAKE, 400, None) == E_DTYPE
+    assert sc(FAKE, F32, 100, FAKE, FAKE, 10, 0, FAKE, 399, None) == E_WS
+    assert sc(FAKE, F32, 100, FAKE, FAKE, 10, 2, FAKE, 400, None) == E_PARAM
+    assert sc(FAKE, F32, 100, FAKE, FAKE, 0, 0, None, 0, None) == OK
     assert L.psamp_workspace_errors(None, 256, None, None) == E_NULL
 
 

@@ -183,14 +183,14 @@ def test_per_mid_cfg_32_rounds(ps):
     p_o = d["p0"].copy()
     Pd = dev(d["p0"])
     ws = ps.Workspace(ps.build_cdf_workspace_size(n))
-    sws = ps.Workspace(ps.scatter_workspace_size(n, k))
     exc_total = 0
     for r in range(d["U"].shape[0]):
         C_o, T_o, t_o, idx_o = oracle.sample(p_o, d["alpha"], d["U"][r], True)
         cdf, tot = ps.build_cdf(Pd, d["alpha"], ws=ws)
         idx = ps.sample(cdf, tot, dev(d["U"][r]), stratified=True)
         w = ps.is_weights(Pd, idx, d["alpha"], d["beta"])
-        ps.scatter_lww(Pd, idx, dev(d["v"][r]), sws)
+        # stratified indices are non-decreasing: the grouped rewrite applies
+        ps.scatter_lww(Pd, idx, dev(d["v"][r]), grouped=True)
         idx_g = host(idx)
         exc = assert_indices(idx_g, idx_o, t_o, C_o, T_o, f"per_mid round {r}")
         exc_total += exc
@@ -217,6 +217,14 @@ def test_scatter_lww(ps):
         assert np.array_equal(host(Pd), p), m
     # the owner words are all zero again after each call
     assert int(host(ws.buf).astype(np.int64).sum()) == 0
+    # grouped indices (sorted, with runs): one kernel, no workspace
+    for m in (1, 7, 8192, 20000):
+        idx = np.sort(rng.integers(-2, n + 2, m)).astype(np.int32)
+        v = si.generic_f32(m, m + 1)
+        ok = (idx >= 0) & (idx < n)
+        p = oracle.scatter_lww(p, idx[ok], v[ok])
+        ps.scatter_lww(Pd, dev(idx), dev(v), grouped=True)
+        assert np.array_equal(host(Pd), p), ("grouped", m)
 
 
 def test_per_large_cfg(ps):

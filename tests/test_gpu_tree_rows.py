@@ -79,7 +79,7 @@ def test_sumtree_cfg_rounds(ps):
 def _stress_batches(cap, rng):
     m = 1024
     yield "one leaf", np.full(m, 17, np.int32)
-    yield "sibling pairs", (np.arange(m) % 64).astype(np.int32) ^ (np.arange(m) % 2)
+    yield "sibling pairs", ((np.arange(m) % 64) ^ (np.arange(m) % 2)).astype(np.int32)
     yield "one subtree", rng.integers(4096, 4096 + 256, m).astype(np.int32)
     yield "ascending", np.arange(m, dtype=np.int32) * (cap // m)
     yield "descending dup", np.repeat(np.arange(m // 4, dtype=np.int32)[::-1] * 3, 4)
