@@ -71,6 +71,25 @@ class PerMid:
         self.idx = torch.empty(self.k, dtype=torch.int32, device="cuda")
         self.w = torch.empty(self.k, dtype=torch.float32, device="cuda")
         self.ws = ps.Workspace(ps.build_cdf_workspace_size(self.n))
+        self.rws = ps.Workspace(ps.per_round_workspace_size(self.n, self.k))
+
+    def step_fused(self, events=None):
+        """One step through the fused update entry point (one kernel per
+        minibatch update when it fits on the GPU at once)."""
+        ps = self.ps
+        for r in range(self.rounds):
+            fn = lambda: ps.per_round(self.p, self.U[r], self.alpha, self.beta, self.v[r],
+                                      out_idx=self.idx, out_w=self.w, cdf=self.cdf,
+                                      total=self.tot, ws=self.rws)
+            if events is None:
+                fn()
+            else:
+                e0 = self.torch.cuda.Event(enable_timing=True)
+                e1 = self.torch.cuda.Event(enable_timing=True)
+                e0.record()
+                fn()
+                e1.record()
+                events.setdefault("per_round", []).append((e0, e1))
 
     def step(self, events=None):
         ps = self.ps
@@ -103,6 +122,8 @@ class PerMid:
             "sample": 8 * k + min(8 * n, 64 * k),                  # U in, idx out, CDF lines
             "is_weights": 8 * k + min(4 * n, 64 * k),              # idx in, w out, p lines
             "scatter_lww": 8 * k + 4 * k,                          # idx, vals in; prio out
+            # fused: p in, CDF out, U in, idx + w out, new p in, p rewrites
+            "per_round": 12 * n + 4 * k + 8 * k + 4 * k + 4 * k,
         }[name]
 
 
@@ -111,6 +132,7 @@ KERNEL_NAMES = {
     "sample": "k_sample_fp<double>",
     "is_weights": "k_isw_single<float>",
     "scatter_lww": "k_scatter_grouped",
+    "per_round": "k_per_round<1>",
 }
 
 
@@ -310,20 +332,26 @@ def main():
     work = PerMid(ps, torch)
     log(f"PER mid: warmup {args.warmup} steps")
     for _ in range(args.warmup):
+        work.step_fused()
         work.step()
-    gpu_s, wall_s = timed_steps(torch, work.step, args.steps)
+    gpu_s, wall_s = timed_steps(torch, work.step_fused, args.steps)
     ms_per_step = 1e3 * gpu_s / args.steps
     draws = work.rounds * work.k * args.steps
     value = draws / gpu_s
-    log(f"PER mid: {ms_per_step:.3f} ms/step, {value:.4g} indices/s (wall {wall_s:.3f} s)")
+    log(f"PER mid (fused update): {ms_per_step:.3f} ms/step, {value:.4g} indices/s "
+        f"(wall {wall_s:.3f} s)")
+    sep_s, _ = timed_steps(torch, work.step, args.steps)
+    log(f"PER mid (four separate calls): {1e3 * sep_s / args.steps:.3f} ms/step, "
+        f"{draws / sep_s:.4g} indices/s")
 
     # instrumented repeat: per-call launch durations on the launch stream
     events = {}
     for _ in range(args.steps):
+        work.step_fused(events)
+    for _ in range(args.steps):
         work.step(events)
     per_call = {k: event_mean_us(torch, v) for k, v in events.items()}
-    share = {k: per_call[k] for k in per_call}
-    dom = max(share, key=share.get)
+    dom = "per_round"
     ab = work.algo_bytes(dom)
     achieved = ab / (per_call[dom] * 1e-6) / 1e9
     roofline = {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "call": dom,
@@ -332,7 +360,9 @@ def main():
                 "algo_bytes_per_launch": ab, "avg_launch_us": round(per_call[dom], 3)}
     log(f"per-call us: { {k: round(v, 2) for k, v in per_call.items()} }; dominant {dom}")
 
-    extra = {"per_call_us": {k: round(v, 3) for k, v in per_call.items()}}
+    extra = {"per_call_us": {k: round(v, 3) for k, v in per_call.items()},
+             "separate_calls": {"ms_per_step": round(1e3 * sep_s / args.steps, 4),
+                                "indices_per_s": round(draws / sep_s, 1)}}
     if not args.no_extra:
         extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])
         extra["sumtree"] = sumtree_bench(ps, torch)

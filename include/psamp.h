@@ -214,6 +214,31 @@ psamp_status psamp_scatter_lww(void* prio, psamp_dtype prio_t, int64_t n,
                                void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * One prioritized-replay minibatch update, fused: exactly
+ *   psamp_build_cdf(prio F32 -> cdf F64, total)
+ *   psamp_sample(stratified, u -> out_idx)
+ *   psamp_is_weights(-> out_w)
+ *   psamp_scatter_lww(prio[out_idx] = new_prio, PSAMP_SCATTER_GROUPED)
+ * (the per-update hot loop of the PER trainers on the pages: [PR615] runs
+ * the CDF rebuild 32-128 times per train call; [SEGT] "Problem" samples
+ * from the rebuilt prefix sum every step).  Same results, bit for bit, as
+ * the four calls; in one kernel when one workgroup per 1024 (or 4096)
+ * priorities can be resident at once, else as the four kernels.
+ *   prio     : n float priorities, read, then rewritten at the drawn indices
+ *              with new_prio (skipped when new_prio is NULL).
+ *   u        : k float fractions in [0,1) (stratified thresholds).
+ *   out_idx, out_w : k draws and their IS weights.
+ *   cdf, total : n + 1 doubles of output (the CDF before the rewrite).
+ *   ws       : psamp_per_round_workspace_size(n, k) bytes, 256-byte aligned.
+ * Errors: as the four calls.
+ * ---------------------------------------------------------------------- */
+size_t psamp_per_round_workspace_size(int64_t n, int64_t k);
+psamp_status psamp_per_round(void* prio, int64_t n, double alpha, double beta,
+                             const float* u, int64_t k, const float* new_prio,
+                             int32_t* out_idx, float* out_w, double* cdf, double* total,
+                             void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.  Copies the error bits a psamp_build_cdf workspace has
  * accumulated (bit 0: a bounded cross-workgroup wait timed out; bit 1: a
  * workgroup drew a ticket outside the call's grid) into *bits_host, with a

@@ -50,6 +50,8 @@ SIGNATURES = {
     "psamp_resample_rows": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p]),
     "psamp_scatter_workspace_size": (_sz, [_i64, _i64]),
     "psamp_scatter_lww": (_int, [_p, _int, _i64, _p, _p, _i64, _int, _p, _sz, _p]),
+    "psamp_per_round_workspace_size": (_sz, [_i64, _i64]),
+    "psamp_per_round": (_int, [_p, _i64, _dbl, _dbl, _p, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "psamp_workspace_errors": (_int, [_p, _sz, C.POINTER(C.c_uint64), _p]),
 }
 
@@ -286,3 +288,36 @@ def scatter_lww(prio: torch.Tensor, idx: torch.Tensor, vals: torch.Tensor,
         ws.ptr if ws is not None else None, ws.nbytes if ws is not None else 0,
         _stream(stream)))
     return prio
+
+
+# ------------------------------------------------------------ fused update
+def per_round_workspace_size(n: int, k: int) -> int:
+    return int(lib().psamp_per_round_workspace_size(int(n), int(k)))
+
+
+def per_round(prio: torch.Tensor, u: torch.Tensor, alpha: float, beta: float,
+              new_prio: torch.Tensor | None = None, *, out_idx: torch.Tensor | None = None,
+              out_w: torch.Tensor | None = None, cdf: torch.Tensor | None = None,
+              total: torch.Tensor | None = None, ws: Workspace | None = None, stream=None):
+    """One fused PER minibatch update (CDF, stratified draws, IS weights,
+    rewrite of the drawn priorities).  Returns (idx, w, cdf, total)."""
+    n, k = prio.numel(), u.numel()
+    dev_ = prio.device
+    out_idx = torch.empty(k, dtype=torch.int32, device=dev_) if out_idx is None else out_idx
+    out_w = torch.empty(k, dtype=torch.float32, device=dev_) if out_w is None else out_w
+    cdf = torch.empty(n, dtype=torch.float64, device=dev_) if cdf is None else cdf
+    total = torch.empty(1, dtype=torch.float64, device=dev_) if total is None else total
+    if ws is None:
+        ws = Workspace(per_round_workspace_size(n, k), dev_)
+    p = _dev(prio, "prio", (torch.float32,))
+    uu = _dev(u, "u", (torch.float32,))
+    npp = None
+    if new_prio is not None:
+        if new_prio.numel() != k:
+            raise ValueError("new_prio must have one value per draw")
+        npp = _dev(new_prio, "new_prio", (torch.float32,))
+    _check("psamp_per_round", lib().psamp_per_round(
+        p, n, float(alpha), float(beta), uu, k, npp, _dev(out_idx, "out_idx", (torch.int32,)),
+        _dev(out_w, "out_w", (torch.float32,)), _dev(cdf, "cdf", (torch.float64,)),
+        _dev(total, "total", (torch.float64,)), ws.ptr, ws.nbytes, _stream(stream)))
+    return out_idx, out_w, cdf, total

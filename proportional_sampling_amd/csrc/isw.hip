@@ -41,20 +41,6 @@ __device__ __forceinline__ int64_t clamp_idx(int32_t i, int64_t n) {
     return i < 0 ? 0 : (i >= n ? n - 1 : (int64_t)i);
 }
 
-// IS = (pmin / p)^e.  p == 0 forces pmin == 0: 0/0 -> NaN; pmin == 0 < p -> 0.
-__device__ __forceinline__ float is_weight(double pmin, double lpmin, double p, double e,
-                                           const MathLds* M) {
-    if (!(p > 0.0)) return __int_as_float(0x7FC00000);
-    if (!(pmin > 0.0)) return 0.0f;
-    return (float)exp2_tab(e * (lpmin - log2_sig32(p, M)), M);
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = min_(x, (uint32_t)__shfl_xor((int)x, m));
-    return x;
-}
-
 // k <= 8192 in one workgroup: each thread owns up to 8 samples; all index
 // loads, then all priority gathers, are in flight together (two round
 // trips), the values stay in registers for the weights.

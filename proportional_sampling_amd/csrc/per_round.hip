@@ -1,0 +1,313 @@
+// per_round.hip -- one prioritized-replay minibatch update in one kernel.
+//
+// What it computes is exactly the composition of the separate calls:
+//   psamp_build_cdf (p^alpha, inclusive CDF, T)      [PR615] "1. Parallel
+//   psamp_sample    (k stratified draws)               build_cdf"; [PF]
+//   psamp_is_weights(IS = (p_min / p_i)^(alpha beta))  searchsorted; [PER]
+//   psamp_scatter_lww(prio[idx_i] = new_i, grouped)    [SEGT] "Integration"
+// -- the PER update the PufferLib page runs once per minibatch (32 to 128
+// times per train call), the hot loop of the trainer.
+//
+// Why one kernel: once T is known, everything a stratified draw needs lies
+// in one tile.  The CDF of scan_tile.h is exactly monotone and every tile j
+// owns the thresholds in (excl_j, excl_{j+1}], so after the scan each tile
+// (one workgroup) keeps its CDF values and priorities in LDS and
+//   1. waits for T (published by the last tile after its lookback);
+//   2. finds its samples: the stratified thresholds are non-decreasing in i,
+//      so they form one index range, located from the stratum estimate
+//      i ~ B k / T and checked exactly on a 32-wide window;
+//   3. searches each sample's threshold in LDS and writes the index;
+//   4. publishes the smallest priority it drew and waits for every tile's;
+//   5. writes the IS weights and, for the last draw of each index (draws of
+//      one index are adjacent and all in this tile), the new priority --
+//      only this tile ever reads that part of the priority array, so no
+//      other synchronisation is needed.
+// The grid is one workgroup per tile and must be resident at once (two
+// grid-wide waits); the host checks the occupancy and otherwise runs the
+// separate kernels, which give the same bits.
+#include "psamp_host.h"
+#include "scan_tile.h"
+
+namespace psamp {
+
+// Stratified threshold of sample i (same operations as psamp_sample).
+__device__ __forceinline__ double strat_threshold(int64_t i, float u, int64_t k, double T) {
+    const double a = (double)i + (double)u;
+    const double b = a / (double)k;
+    return b * T;
+}
+
+// First i in [0, k] with t_i > B (t_i non-decreasing in i).  Lanes 0..31
+// answer for B0, lanes 32..63 for B1, in one round trip: each half tests a
+// 32-wide window around the stratum estimate B k / T (the answer lies within
+// 2 of it); a binary search covers the case the window misses (T = 0, or
+// inputs outside the preconditions).
+__device__ __forceinline__ int64_t first_above2(double B0, double B1, double T,
+                                                const float* __restrict__ U, int64_t k) {
+    const int lane = lane_id();
+    const bool hi = lane >= 32;
+    const double B = hi ? B1 : B0;
+    int64_t est = 0;
+    if (T > 0.0) {
+        const double e = floor(B / T * (double)k);
+        est = !(e > 0.0) ? 0 : (e > (double)k ? k : (int64_t)e);
+    }
+    const int64_t c0 = est - 8;
+    const int64_t c = c0 + (lane & 31);
+    const bool above = c < 0 ? false : (c >= k ? true : strat_threshold(c, U[c], k, T) > B);
+    const uint64_t bal = __ballot(above);
+    const uint32_t m = hi ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+    if (m != 0 && ((m & 1u) == 0 || c0 <= 0)) {
+        const int64_t r = c0 + (__ffs((int)m) - 1);
+        return r < 0 ? 0 : r;
+    }
+    int64_t lo = 0, hi_i = k;
+    while (lo < hi_i) {
+        const int64_t mid = lo + ((hi_i - lo) >> 1);
+        if (strat_threshold(mid, U[mid], k, T) > B) hi_i = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
+
+template <int R>
+__global__ __launch_bounds__(kScanThreads) void k_per_round(
+    float* __restrict__ prio, int64_t n, double alpha, double ab, const float* __restrict__ U,
+    int64_t k, const float* __restrict__ newp, int32_t* __restrict__ out_idx,
+    float* __restrict__ out_w, double* __restrict__ cdf, double* __restrict__ total,
+    uint64_t* __restrict__ ws, int n_tiles, uint64_t max_slots, int vec_ok) {
+    constexpr int ROW = kScanThreads * 4;
+    constexpr int TILE = ROW * R;
+
+    __shared__ MathLds M;
+    __shared__ double s_wtot[4][R];
+    __shared__ double s_wmax[4][R];
+    __shared__ double s_excl[2];
+    __shared__ double s_C[TILE];
+    __shared__ float s_p[TILE];
+    __shared__ uint32_t s_calls;
+    __shared__ double s_T;
+    __shared__ int64_t s_range[2];
+    __shared__ uint32_t s_min, s_gmin;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    uint64_t* hdr = ws;
+    uint64_t* slots = ws + kWsHeaderWords;
+    const int tile = (int)blockIdx.x;
+    const bool last_tile = tile == n_tiles - 1;
+    const int64_t base = (int64_t)tile * TILE;
+    const int tlen = (int)min_<int64_t>(TILE, n - base);
+
+    if (tid == 0) {
+        s_calls = (uint32_t)load_agent(&hdr[kHdrCalls]);
+        s_min = 0xFFFFFFFFu;
+    }
+    math_lds_fill(&M, tid, kScanThreads);
+    float v[R][4];
+    load_tile<R, float>(prio, n, base, vec_ok, v);
+    __syncthreads();
+    const uint32_t calls = s_calls;
+    const int par = (int)(calls & 1u);
+    clear_other_parity(hdr, slots, par, n_tiles, max_slots);
+
+    // ---- 1. scan (as psamp_build_cdf)
+    double q[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const double w = pow_prio(v[r][c], alpha, &M);
+            q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
+            s_p[r * ROW + 4 * tid + c] = v[r][c];
+        }
+    double X[R];
+    double A;
+    tile_scan_256<R, double>(q, X, A, s_wtot);
+    if (tid == 0) store_agent(slot_word(slots, (uint64_t)tile, kSlotA, par), status_enc(A));
+    if (wave == 0) lookback<double>(tile, n_tiles, par, A, slots, hdr, calls, s_excl);
+    __syncthreads();
+    const double excl = s_excl[0];
+    const double excl_next = s_excl[1];
+    TileValues<R, double> tv;
+    tv.prepare(q, X, excl, excl_next, last_tile, s_wmax);
+    const bool vec_out = vec_ok && tlen == TILE;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        double c[R][4];
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) c[r][cc] = tv.at(q, X, r, cc);
+        if (vec_out) {
+            double2* o = reinterpret_cast<double2*>(cdf + base + r * ROW + 4 * tid);
+            o[0] = make_double2(c[r][0], c[r][1]);
+            o[1] = make_double2(c[r][2], c[r][3]);
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {
+            const int e = r * ROW + 4 * tid + cc;
+            s_C[e] = c[r][cc];
+            if (!vec_out && e < tlen) cdf[base + e] = c[r][cc];
+            if (last_tile && e == tlen - 1) {
+                total[0] = c[r][cc];
+                store_agent(&hdr[kHdrT + par], status_enc(c[r][cc]));
+            }
+        }
+    }
+
+    // ---- 2. T, then this tile's samples
+    if (wave == 0) {
+        const uint64_t* addr[1] = {&hdr[kHdrT + par]};
+        const bool need[1] = {lane == 0};
+        uint64_t w[1];
+        wait_words<1>(addr, need, w, &hdr[kHdrErr]);
+        if (lane == 0) {
+            double T;
+            status_dec(w[0], T);
+            s_T = T;
+        }
+    }
+    __syncthreads();
+    const double T = s_T;
+    if (wave == 0) {
+        const int64_t r = first_above2(excl, excl_next, T, U, k);
+        if (lane == 0) s_range[0] = (tile == 0) ? 0 : r;
+        if (lane == 32) s_range[1] = last_tile ? k : r;
+    }
+    __syncthreads();
+    const int64_t i_lo = s_range[0];
+    const int64_t i_hi = s_range[1];
+
+    // ---- 3. search in LDS, write the indices, local minimum of p
+    uint32_t mn = 0xFFFFFFFFu;
+    for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
+        const double t = strat_threshold(i, U[i], k, T);
+        int b = 0, len = tlen;
+        while (len > 1) {
+            const int half = len >> 1;
+            b = (s_C[b + half - 1] < t) ? b + half : b;
+            len -= half;
+        }
+        b += (s_C[b] < t) ? 1 : 0;
+        if (b >= tlen) b = tlen - 1;
+        out_idx[i] = (int32_t)(base + b);
+        const uint32_t key = __float_as_uint(s_p[b]);
+        mn = key < mn ? key : mn;
+    }
+    mn = wave_min_u32(mn);
+    if (lane == 0) atomicMin(&s_min, mn);
+    __syncthreads();
+
+    // ---- 4. global minimum of the drawn priorities
+    if (tid == 0) store_agent(slot_word(slots, (uint64_t)tile, kSlotMin, par),
+                              (uint64_t)s_min + 1);
+    if (wave == 0) {
+        uint32_t g = 0xFFFFFFFFu;
+        for (int t0 = 0; t0 < n_tiles; t0 += kGtWords * kWave) {
+            const uint64_t* addr[kGtWords];
+            bool need[kGtWords];
+            uint64_t w[kGtWords];
+#pragma unroll
+            for (int j = 0; j < kGtWords; ++j) {
+                const int tt = t0 + j * kWave + lane;
+                addr[j] = slot_word(slots, (uint64_t)tt, kSlotMin, par);
+                need[j] = tt < n_tiles;
+            }
+            wait_words<kGtWords>(addr, need, w, &hdr[kHdrErr]);
+#pragma unroll
+            for (int j = 0; j < kGtWords; ++j)
+                if (need[j]) {
+                    const uint32_t key = (uint32_t)(w[j] - 1);
+                    g = key < g ? key : g;
+                }
+        }
+        g = wave_min_u32(g);
+        if (lane == 0) s_gmin = g;
+    }
+    __syncthreads();
+
+    // ---- 5. IS weights and the rewrite of the last draw of each index
+    const double pmin = (double)__uint_as_float(s_gmin);
+    const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
+    for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
+        const int b = (int)(out_idx[i] - base);
+        out_w[i] = is_weight(pmin, lpmin, (double)s_p[b], ab, &M);
+        if (newp != nullptr) {
+            bool winner = i + 1 >= i_hi;
+            if (!winner) winner = out_idx[i + 1] != out_idx[i];
+            if (winner) prio[base + b] = newp[i];
+        }
+    }
+}
+
+template <int R>
+static int per_round_capacity() {
+    return resident_grid(reinterpret_cast<const void*>(&k_per_round<R>), kScanThreads);
+}
+
+template <int R>
+static psamp_status launch_per_round(void* prio, int64_t n, double alpha, double ab,
+                                     const float* u, int64_t k, const float* newp,
+                                     int32_t* out_idx, float* out_w, double* cdf, double* total,
+                                     void* ws, uint64_t max_slots, int vec_ok, hipStream_t st) {
+    const int tiles = (int)ceil_div(n, kScanThreads * 4 * R);
+    if (trace_enabled()) trace_launch("k_per_round", tiles, kScanThreads, n);
+    hipLaunchKernelGGL(k_per_round<R>, dim3(tiles), dim3(kScanThreads), 0, st, (float*)prio, n,
+                       alpha, ab, u, k, newp, out_idx, out_w, cdf, total, (uint64_t*)ws, tiles,
+                       max_slots, vec_ok);
+    return launch_status();
+}
+
+}  // namespace psamp
+
+using namespace psamp;
+
+extern "C" size_t psamp_per_round_workspace_size(int64_t n, int64_t k) {
+    const size_t a = psamp_build_cdf_workspace_size(n);
+    const size_t b = psamp_is_weights_workspace_size(k);
+    if (a == 0) return 0;
+    return a + ((b + 255) / 256) * 256;
+}
+
+extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, double beta,
+                                        const float* u, int64_t k, const float* new_prio,
+                                        int32_t* out_idx, float* out_w, double* cdf,
+                                        double* total, void* ws, size_t ws_bytes, void* stream) {
+    if (!prio || !cdf || !total) return PSAMP_E_NULL;
+    if (n < 1 || n > kMaxN || k < 0 || k > kMaxN) return PSAMP_E_SIZE;
+    if (!(finite_d(alpha) && alpha > 0.0) || !(finite_d(beta) && beta >= 0.0)) return PSAMP_E_PARAM;
+    if (!ws || ws_bytes < psamp_per_round_workspace_size(n, k)) return PSAMP_E_WORKSPACE;
+    if (!aligned(prio, 4) || !aligned(cdf, 8) || !aligned(total, 8) || !aligned(ws, 256))
+        return PSAMP_E_ALIGN;
+    if (k > 0 && (!u || !out_idx || !out_w)) return PSAMP_E_NULL;
+    if (k > 0 && (!aligned(u, 4) || !aligned(out_idx, 4) || !aligned(out_w, 4) ||
+                  (new_prio && !aligned(new_prio, 4))))
+        return PSAMP_E_ALIGN;
+    hipStream_t st = as_stream(stream);
+    const size_t scan_ws = psamp_build_cdf_workspace_size(n);
+    const uint64_t max_slots = (scan_ws - (size_t)kWsHeaderWords * 8) / (kSlotWords * 8);
+    const int vec_ok = aligned(prio, 16) && aligned(cdf, 16);
+    if (k > 0) {
+        const int64_t t1 = ceil_div(n, kScanThreads * 4);
+        const int64_t t4 = ceil_div(n, kScanThreads * 16);
+        if (t1 <= per_round_capacity<1>())
+            return launch_per_round<1>(prio, n, alpha, alpha * beta, u, k, new_prio, out_idx,
+                                       out_w, cdf, total, ws, max_slots, vec_ok, st);
+        if (t4 <= per_round_capacity<4>())
+            return launch_per_round<4>(prio, n, alpha, alpha * beta, u, k, new_prio, out_idx,
+                                       out_w, cdf, total, ws, max_slots, vec_ok, st);
+    }
+    // Too large to be resident at once (or nothing to draw): the separate
+    // kernels, same results.
+    psamp_status s = psamp_build_cdf(prio, PSAMP_F32, n, alpha, cdf, PSAMP_F64, total, ws, scan_ws,
+                                     stream);
+    if (s != PSAMP_OK || k == 0) return s;
+    s = psamp_sample(cdf, PSAMP_F64, n, total, u, PSAMP_F32, k, 1, out_idx, stream);
+    if (s != PSAMP_OK) return s;
+    const size_t off = ((scan_ws + 255) / 256) * 256;
+    s = psamp_is_weights(prio, PSAMP_F32, n, alpha, out_idx, k, beta, out_w,
+                         (char*)ws + off, ws_bytes - off, stream);
+    if (s != PSAMP_OK || !new_prio) return s;
+    return psamp_scatter_lww(prio, PSAMP_F32, n, out_idx, new_prio, k, PSAMP_SCATTER_GROUPED,
+                             nullptr, 0, stream);
+}

@@ -289,6 +289,24 @@ __device__ __forceinline__ void tile_scan_256(const Acc (&q)[R][4], Acc (&X)[R],
     }
 }
 
+// ------------------------------------------------- IS weights
+// IS = (pmin / p)^e.  p == 0 forces pmin == 0: 0/0 -> NaN; pmin == 0 < p -> 0.
+__device__ __forceinline__ float is_weight(double pmin, double lpmin, double p, double e,
+                                           const MathLds* M) {
+    if (!(p > 0.0)) return __int_as_float(0x7FC00000);
+    if (!(pmin > 0.0)) return 0.0f;
+    return (float)exp2_tab(e * (lpmin - log2_sig32(p, M)), M);
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) {
+        const uint32_t y = (uint32_t)__shfl_xor((int)x, m);
+        x = y < x ? y : x;
+    }
+    return x;
+}
+
 // ------------------------------------------------------------- helpers
 template <class T>
 __host__ __device__ __forceinline__ T min_(T a, T b) { return a < b ? a : b; }

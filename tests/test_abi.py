@@ -49,8 +49,10 @@ def test_status_strings_and_version(L):
 
 def test_workspace_sizes(L):
     assert L.psamp_build_cdf_workspace_size(0) == 0
-    assert L.psamp_build_cdf_workspace_size(1) == 256 + 32
-    assert L.psamp_build_cdf_workspace_size(1 << 24) == 256 + 32 * (1 << 14)
+    assert L.psamp_build_cdf_workspace_size(1) == 256 + 64
+    assert L.psamp_build_cdf_workspace_size(1 << 24) == 256 + 64 * (1 << 14)
+    assert L.psamp_per_round_workspace_size(262144, 8192) == 256 + 64 * 256
+    assert L.psamp_per_round_workspace_size(1 << 20, 1 << 20) == 256 + 64 * 1024 + 256 + 4 * 256
     assert L.psamp_is_weights_workspace_size(8192) == 0
     assert L.psamp_is_weights_workspace_size(1 << 20) == 256 + 4 * 256
     assert L.psamp_scatter_workspace_size(262144, 8192) == 262144 * 4
@@ -132,6 +134,14 @@ def test_resample_and_scatter_validation(L):
     assert sc(FAKE, F32, 100, FAKE, FAKE, 10, 2, FAKE, 400, None) == E_PARAM
     assert sc(FAKE, F32, 100, FAKE, FAKE, 0, 0, None, 0, None) == OK
     assert L.psamp_workspace_errors(None, 256, None, None) == E_NULL
+    pr = L.psamp_per_round
+    wsz = L.psamp_per_round_workspace_size(1000, 10)
+    assert pr(None, 1000, 0.6, 0.4, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, wsz, None) == E_NULL
+    assert pr(FAKE, 0, 0.6, 0.4, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, wsz, None) == E_SIZE
+    assert pr(FAKE, 1000, 0.0, 0.4, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, wsz, None) == E_PARAM
+    assert pr(FAKE, 1000, 0.6, -1.0, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, wsz, None) == E_PARAM
+    assert pr(FAKE, 1000, 0.6, 0.4, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE, wsz - 1, None) == E_WS
+    assert pr(FAKE, 1000, 0.6, 0.4, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE + 8, wsz, None) == E_ALIGN
 
 
 def test_binding_fails_loudly_without_gpu_tensors():

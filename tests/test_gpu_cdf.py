@@ -255,3 +255,59 @@ def test_per_large_int_cfg(ps):
     w_g = host(ps.is_weights(Q, dev(idx), 1.0, d["beta"]))
     w_o = oracle.is_weights_int(d["q"], T_o, idx_o, d["beta"])
     assert rel_err(w_g, w_o) <= 1e-6
+
+
+# ------------------------------------------------------------ fused update
+def _separate_round(ps, p, U, newp, alpha, beta):
+    """The four separate calls, for comparison with the fused update."""
+    Pd = dev(p)
+    cdf, tot = ps.build_cdf(Pd, alpha)
+    idx = ps.sample(cdf, tot, dev(U), stratified=True)
+    w = ps.is_weights(Pd, idx, alpha, beta)
+    if newp is not None:
+        ps.scatter_lww(Pd, idx, dev(newp), grouped=True)
+    return host(cdf), host(tot), host(idx), host(w), host(Pd)
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (1000, 7), (1024, 1024), (5000, 300), (8192, 1024),
+                                 (262144, 8192), (262147, 8191), (100000, 100000),
+                                 (1 << 20, 4096), ((1 << 22) + 5, 1 << 16)])
+def test_per_round_equals_separate_calls(ps, n, k):
+    say(f"per_round n={n} k={k}")
+    p = si.generic_f32(n, n + 13, "exp")
+    p[::17] = 0.0                          # zero-weight items too
+    p[0] = max(p[0], np.float32(1e-3))
+    U = si.uniform_f32(np.random.default_rng(k + 1), k)
+    newp = si.generic_f32(k, k + 2, "exp")
+    C_s, T_s, idx_s, w_s, p_s = _separate_round(ps, p, U, newp, 0.6, 0.4)
+    Pd = dev(p)
+    idx, w, cdf, tot = ps.per_round(Pd, dev(U), 0.6, 0.4, dev(newp))
+    assert np.array_equal(host(cdf), C_s)
+    assert np.array_equal(host(tot), T_s)
+    assert np.array_equal(host(idx), idx_s)
+    assert np.array_equal(host(w), w_s)
+    assert np.array_equal(host(Pd), p_s)
+    # the CDF is exactly monotone and ends at T
+    assert np.all(np.diff(C_s) >= 0) and C_s[-1] == T_s[0]
+
+
+def test_per_round_chain_vs_oracle(ps):
+    """PER mid through the fused update: 32 chained updates against the
+    oracle's own chain."""
+    d = si.per_mid()
+    n, k = d["p0"].size, d["U"].shape[1]
+    p_o = d["p0"].copy()
+    Pd = dev(d["p0"])
+    ws = ps.Workspace(ps.per_round_workspace_size(n, k))
+    for r in range(d["U"].shape[0]):
+        C_o, T_o, t_o, idx_o = oracle.sample(p_o, d["alpha"], d["U"][r], True)
+        idx, w, cdf, tot = ps.per_round(Pd, dev(d["U"][r]), d["alpha"], d["beta"],
+                                        dev(d["v"][r]), ws=ws)
+        exc = assert_indices(host(idx), idx_o, t_o, C_o, T_o, f"per_round chain {r}")
+        assert exc == 0
+        assert rel_err(host(cdf), C_o) <= 1e-12
+        w_o = oracle.is_weights(p_o, d["alpha"], T_o, idx_o, d["beta"])
+        assert rel_err(host(w), w_o) <= 1e-6
+        p_o = oracle.scatter_lww(p_o, idx_o, d["v"][r])
+        assert np.array_equal(host(Pd), p_o)
+    assert ws.errors() == 0
