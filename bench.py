@@ -8,9 +8,12 @@ new values.  All inputs are resident in HBM before timing starts.  `value` is
 sampled indices per second over the timed steps.
 
 The JSON line also carries:
-  roofline      the dominant kernel of the step: algorithmic bytes per launch
-                / its average launch duration (HIP events on the launch
-                stream, from an instrumented repeat of the timed steps);
+  roofline      the kernel of the step (the fused update, the only kernel in
+                the timed region): algorithmic bytes per launch / its average
+                launch duration (HIP events around the timed region, on the
+                launch stream, over the number of launches); `traffic` comes
+                from the committed rocprofv3 counter summary in profiles/ when
+                the kernel's sources still hash to the profiled ones;
   cpu_baseline  the CPU oracle (single-threaded, as it stands) running the
                 same 32-update chain on a bounded number of steps;
   extra         the CDF-scan bandwidth sweep (2^22..2^26, the Infinity Cache
@@ -73,47 +76,22 @@ class PerMid:
         self.ws = ps.Workspace(ps.build_cdf_workspace_size(self.n))
         self.rws = ps.Workspace(ps.per_round_workspace_size(self.n, self.k))
 
-    def step_fused(self, events=None):
+    def step_fused(self):
         """One step through the fused update entry point (one kernel per
-        minibatch update when it fits on the GPU at once)."""
+        minibatch update when the grid fits on the GPU at once)."""
         ps = self.ps
         for r in range(self.rounds):
-            fn = lambda: ps.per_round(self.p, self.U[r], self.alpha, self.beta, self.v[r],
-                                      out_idx=self.idx, out_w=self.w, cdf=self.cdf,
-                                      total=self.tot, ws=self.rws)
-            if events is None:
-                fn()
-            else:
-                e0 = self.torch.cuda.Event(enable_timing=True)
-                e1 = self.torch.cuda.Event(enable_timing=True)
-                e0.record()
-                fn()
-                e1.record()
-                events.setdefault("per_round", []).append((e0, e1))
+            ps.per_round(self.p, self.U[r], self.alpha, self.beta, self.v[r], out_idx=self.idx,
+                         out_w=self.w, cdf=self.cdf, total=self.tot, ws=self.rws)
 
-    def step(self, events=None):
+    def step(self):
+        """The same step as four separate calls per update."""
         ps = self.ps
         for r in range(self.rounds):
-            calls = (
-                ("build_cdf", lambda: ps.build_cdf(self.p, self.alpha, cdf=self.cdf,
-                                                    total=self.tot, ws=self.ws)),
-                ("sample", lambda: ps.sample(self.cdf, self.tot, self.U[r], stratified=True,
-                                             out=self.idx)),
-                ("is_weights", lambda: ps.is_weights(self.p, self.idx, self.alpha, self.beta,
-                                                     out=self.w)),
-                ("scatter_lww", lambda: ps.scatter_lww(self.p, self.idx, self.v[r],
-                                                       grouped=True)),
-            )
-            for name, fn in calls:
-                if events is None:
-                    fn()
-                else:
-                    e0 = self.torch.cuda.Event(enable_timing=True)
-                    e1 = self.torch.cuda.Event(enable_timing=True)
-                    e0.record()
-                    fn()
-                    e1.record()
-                    events.setdefault(name, []).append((e0, e1))
+            ps.build_cdf(self.p, self.alpha, cdf=self.cdf, total=self.tot, ws=self.ws)
+            ps.sample(self.cdf, self.tot, self.U[r], stratified=True, out=self.idx)
+            ps.is_weights(self.p, self.idx, self.alpha, self.beta, out=self.w)
+            ps.scatter_lww(self.p, self.idx, self.v[r], grouped=True)
 
     def algo_bytes(self, name):
         n, k = self.n, self.k
@@ -134,6 +112,29 @@ KERNEL_NAMES = {
     "scatter_lww": "k_scatter_grouped",
     "per_round": "k_per_round<1>",
 }
+
+
+def profiled_traffic(name):
+    """HBM bytes per launch from a committed rocprofv3 summary, or None when
+    the kernel's sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith((" ", "|", "#")):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    try:
+        h = hashlib.sha256()
+        for f in kv["source_files"].split():
+            h.update(open(os.path.join(ROOT, "proportional_sampling_amd", "csrc", f), "rb").read())
+        if h.hexdigest() != kv["source_sha256"]:
+            return None
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, OSError, ValueError):
+        return None
 
 
 def timed_steps(torch, fn, steps):
@@ -191,12 +192,24 @@ def scan_sweep(ps, torch, sizes, reps=8):
     return out
 
 
-def event_mean_us(torch, pairs):
+def loop_us(torch, fn, reps):
+    """Average time of `reps` back-to-back calls (one event pair around the
+    loop, on the launch stream)."""
+    fn()
     torch.cuda.synchronize()
-    return 1e3 * sum(a.elapsed_time(b) for a, b in pairs) / len(pairs)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1e3 * e0.elapsed_time(e1) / reps
 
 
 def sumtree_bench(ps, torch, rounds=200):
+    """Sum tree: 2^19 leaves (500000 valid), rounds of a 1024-entry update
+    then 1024 iid draws."""
     import synthetic_inputs as si
     d = si.sumtree(rounds=rounds)
     cap, nv = 1 << 19, 500000
@@ -206,44 +219,38 @@ def sumtree_bench(ps, torch, rounds=200):
     v = torch.from_numpy(d["v"]).cuda()
     U = torch.from_numpy(d["U"]).cuda()
     out = torch.empty(d["U"].shape[1], dtype=torch.int32, device="cuda")
-    ev = {}
-    for r in range(rounds):
-        for name, fn in (("update", lambda: ps.segtree_update(tree, idx[r], v[r], d["alpha"])),
-                         ("sample", lambda: ps.segtree_sample(tree, nv, U[r], out=out))):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            ev.setdefault(name, []).append((e0, e1))
-    res = {k: round(event_mean_us(torch, v_[10:]), 2) for k, v_ in ev.items()}
-    res["samples_per_s"] = round(1024 / (res["sample"] * 1e-6))
-    log(f"sum tree: update {res['update']} us, sample {res['sample']} us")
+    it = {"r": 0}
+
+    def one_round():
+        r = it["r"] % rounds
+        it["r"] += 1
+        ps.segtree_update(tree, idx[r], v[r], d["alpha"])
+        ps.segtree_sample(tree, nv, U[r], out=out)
+
+    res = {"round_us": round(loop_us(torch, one_round, rounds), 2),
+           "update_us": round(loop_us(torch, lambda: ps.segtree_update(tree, idx[0], v[0],
+                                                                        d["alpha"]), rounds), 2),
+           "sample_us": round(loop_us(torch, lambda: ps.segtree_sample(tree, nv, U[0], out=out),
+                                      rounds), 2)}
+    res["samples_per_s"] = round(1024 / (res["sample_us"] * 1e-6))
+    log(f"sum tree: {res}")
     return res
 
 
-def resample_bench(ps, torch, reps=20):
+def resample_bench(ps, torch, reps=50):
     import synthetic_inputs as si
     d = si.resample()
     lw = torch.from_numpy(d["lw"]).cuda()
     u = torch.from_numpy(d["u_row"]).cuda()
     out = torch.empty_like(lw, dtype=torch.int32)
-    ps.resample_rows(lw, u, out=out)
-    ev = []
-    for _ in range(reps):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        ps.resample_rows(lw, u, out=out)
-        e1.record()
-        ev.append((e0, e1))
-    us = event_mean_us(torch, ev)
+    us = loop_us(torch, lambda: ps.resample_rows(lw, u, out=out), reps)
     gbs = (8 * lw.numel() + 4 * u.numel()) / (us * 1e-6) / 1e9
     log(f"resample 1024x4096: {us:.1f} us {gbs:.0f} GB/s")
     return {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def per_large_bench(ps, torch, reps=10):
+    """PER large: B = 2^24, 2^20 stratified draws, CDF path and tree path."""
     import synthetic_inputs as si
     d = si.per_large()
     p = torch.from_numpy(d["p"]).cuda()
@@ -252,26 +259,16 @@ def per_large_bench(ps, torch, reps=10):
     idx = ps.sample(cdf, tot, U)
     w = ps.is_weights(p, idx, d["alpha"], d["beta"])
     tree = torch.zeros(2 * p.numel(), dtype=torch.float32, device="cuda")
-    ps.segtree_build(tree, p, d["alpha"])
-    ev = {}
     ws = ps.Workspace(ps.build_cdf_workspace_size(p.numel()))
     iws = ps.Workspace(ps.is_weights_workspace_size(U.numel()))
-    for _ in range(reps):
-        for name, fn in (
-                ("build_cdf", lambda: ps.build_cdf(p, d["alpha"], cdf=cdf, total=tot, ws=ws)),
-                ("sample", lambda: ps.sample(cdf, tot, U, out=idx)),
-                ("is_weights", lambda: ps.is_weights(p, idx, d["alpha"], d["beta"], out=w,
-                                                     ws=iws)),
-                ("tree_build", lambda: ps.segtree_build(tree, p, d["alpha"])),
-                ("tree_sample", lambda: ps.segtree_sample(tree, p.numel(), U, stratified=True,
-                                                          out=idx))):
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record()
-            fn()
-            e1.record()
-            ev.setdefault(name, []).append((e0, e1))
-    res = {k: round(event_mean_us(torch, v), 2) for k, v in ev.items()}
+    calls = {
+        "build_cdf": lambda: ps.build_cdf(p, d["alpha"], cdf=cdf, total=tot, ws=ws),
+        "sample": lambda: ps.sample(cdf, tot, U, out=idx),
+        "is_weights": lambda: ps.is_weights(p, idx, d["alpha"], d["beta"], out=w, ws=iws),
+        "tree_build": lambda: ps.segtree_build(tree, p, d["alpha"]),
+        "tree_sample": lambda: ps.segtree_sample(tree, p.numel(), U, stratified=True, out=idx),
+    }
+    res = {k: round(loop_us(torch, fn, reps), 2) for k, fn in calls.items()}
     res["draws_per_s"] = round(U.numel() / ((res["sample"] + res["is_weights"]) * 1e-6))
     log(f"per large: {res}")
     return res
@@ -344,24 +341,22 @@ def main():
     log(f"PER mid (four separate calls): {1e3 * sep_s / args.steps:.3f} ms/step, "
         f"{draws / sep_s:.4g} indices/s")
 
-    # instrumented repeat: per-call launch durations on the launch stream
-    events = {}
-    for _ in range(args.steps):
-        work.step_fused(events)
-    for _ in range(args.steps):
-        work.step(events)
-    per_call = {k: event_mean_us(torch, v) for k, v in events.items()}
+    # The timed region holds only launches of the fused update kernel (one
+    # per minibatch update, all on this stream), so its average launch
+    # duration is the timed region over the number of launches.
+    launches = work.rounds * args.steps
+    avg_us = 1e6 * gpu_s / launches
     dom = "per_round"
     ab = work.algo_bytes(dom)
-    achieved = ab / (per_call[dom] * 1e-6) / 1e9
-    roofline = {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "call": dom,
-                "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
-                "algo_bytes_per_launch": ab, "avg_launch_us": round(per_call[dom], 3)}
-    log(f"per-call us: { {k: round(v, 2) for k, v in per_call.items()} }; dominant {dom}")
+    achieved = ab / (avg_us * 1e-6) / 1e9
+    traffic = profiled_traffic("per_round_per_mid.md")
+    roofline = {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                "traffic": traffic, "algo_bytes_per_launch": ab,
+                "avg_launch_us": round(avg_us, 3), "launches_timed": launches}
+    log(f"k_per_round: {avg_us:.2f} us/launch, {achieved:.0f} GB/s algorithmic, traffic {traffic}")
 
-    extra = {"per_call_us": {k: round(v, 3) for k, v in per_call.items()},
-             "separate_calls": {"ms_per_step": round(1e3 * sep_s / args.steps, 4),
+    extra = {"separate_calls": {"ms_per_step": round(1e3 * sep_s / args.steps, 4),
                                 "indices_per_s": round(draws / sep_s, 1)}}
     if not args.no_extra:
         extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])
