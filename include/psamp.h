@@ -81,7 +81,8 @@ int psamp_abi_version(void);
  *            on the device; psamp_sample reads it there.
  *   n      : 1 <= n <= 2^31 - 1 (integer mode: n <= 2^31 - 1 keeps T < 2^63).
  *   ws     : workspace of psamp_build_cdf_workspace_size(n_max) bytes, where
- *            n_max is the largest n ever used with it.
+ *            n_max is the largest n ever used with it; pass the same ws_bytes
+ *            on every call that shares it (256 B + 4 KiB per 65536 elements).
  * fp mode is deterministic run to run (fixed association); integer mode is
  * exact.  Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_ALIGN
  * (prio 4-byte, cdf/total element-aligned), E_LAUNCH.

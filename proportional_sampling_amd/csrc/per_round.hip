@@ -70,7 +70,11 @@ __device__ __forceinline__ int64_t first_above2(double B0, double B1, double T,
     return lo;
 }
 
-template <int R>
+constexpr int kULds = 8192;   // k up to this: the thresholds' fractions are staged in LDS
+
+// UL: U (k <= kULds values) is copied to LDS at the start, so locating and
+// searching the draws touches no global memory.  VEC: see load_tile.
+template <int R, bool UL, bool VEC>
 __global__ __launch_bounds__(kScanThreads) void k_per_round(
     float* __restrict__ prio, int64_t n, double alpha, double ab, const float* __restrict__ U,
     int64_t k, const float* __restrict__ newp, int32_t* __restrict__ out_idx,
@@ -82,106 +86,136 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     __shared__ MathLds M;
     __shared__ double s_wtot[4][R];
     __shared__ double s_wmax[4][R];
-    __shared__ double s_excl[2];
+    __shared__ double s_lb[3];
     __shared__ double s_C[TILE];
     __shared__ float s_p[TILE];
-    __shared__ uint32_t s_calls;
-    __shared__ double s_T;
+    __shared__ float s_U[UL ? kULds : 1];
     __shared__ int64_t s_range[2];
     __shared__ uint32_t s_min, s_gmin;
+    __shared__ int s_b[kScanThreads + 1];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
-    uint64_t* hdr = ws;
-    uint64_t* slots = ws + kWsHeaderWords;
     const int tile = (int)blockIdx.x;
     const bool last_tile = tile == n_tiles - 1;
     const int64_t base = (int64_t)tile * TILE;
     const int tlen = (int)min_<int64_t>(TILE, n - base);
 
-    if (tid == 0) {
-        s_calls = (uint32_t)load_agent(&hdr[kHdrCalls]);
-        s_min = 0xFFFFFFFFu;
-    }
-    math_lds_fill(&M, tid, kScanThreads);
+    // All first loads (counter, high-water mark, pow tables, priorities) are
+    // issued together, so their latencies overlap.
+    // (The priorities go first: the counter words are made uniform, which
+    // makes the compiler wait for them where they are loaded.)
     float v[R][4];
-    load_tile<R, float>(prio, n, base, vec_ok, v);
+    load_tile<R, VEC, float>(prio + base, tlen, v);
+    asm volatile("" ::: "memory");
+    const MathRegs mr = math_load(tid);
+    const uint64_t calls_w = load_agent(&ws[kHdrCalls]);
+    const uint64_t hw_w = load_agent(&ws[kHdrHw]);
+    math_store(&M, tid, mr);
+    if (tid == 0) s_min = 0xFFFFFFFFu;
+    const float* Us = UL ? s_U : U;
     __syncthreads();
-    const uint32_t calls = s_calls;
+    const uint32_t calls = (uint32_t)calls_w;
     const int par = (int)(calls & 1u);
-    clear_other_parity(hdr, slots, par, n_tiles, max_slots);
 
-    // ---- 1. scan (as psamp_build_cdf)
+    // ---- 1. scan (as psamp_build_cdf); every tile learns T in its lookback
     double q[R][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const double w = pow_prio(v[r][c], alpha, &M);
             q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
             s_p[r * ROW + 4 * tid + c] = v[r][c];
         }
+        // (pinned where formed: see the scan)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(q[r][c]));
+    }
+    // U is loaded now, behind the priorities, and written to LDS during the
+    // lookback: its latency hides under the scan.  (The empty asm keeps the
+    // compiler from hoisting these loads above the pow.)
+    constexpr int kUR = UL ? kULds / kScanThreads : 1;
+    float ureg[kUR];
+    if constexpr (UL) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int m = 0; m < kUR; ++m) {
+            const int i = m * kScanThreads + tid;
+            const bool ok = i < (int)k;
+            const float x = U[ok ? i : 0];      // issued unconditionally (k >= 1)
+            ureg[m] = ok ? x : 0.0f;
+        }
+    }
     double X[R];
     double A;
     tile_scan_256<R, double>(q, X, A, s_wtot);
-    if (tid == 0) store_agent(slot_word(slots, (uint64_t)tile, kSlotA, par), status_enc(A));
-    if (wave == 0) lookback<double>(tile, n_tiles, par, A, slots, hdr, calls, s_excl);
+    if (tid == 0) store_agent(&ws[a_off((uint32_t)tile, par)], status_enc(A));
+    tile_local_values<R, double>(q, X, s_wmax);
+    if (wave != 0) {
+        if constexpr (UL) {
+#pragma unroll
+            for (int m = 0; m < kUR; ++m) s_U[m * kScanThreads + tid] = ureg[m];
+        }
+        clear_other_parity(ws, par, n_tiles, max_slots, hw_w, tid - kWave, kScanThreads - kWave);
+    }
+    if (wave == 0) {
+        lookback_all<double>(tile, n_tiles, par, A, ws, calls, s_lb);
+        if constexpr (UL) {
+#pragma unroll
+            for (int m = 0; m < kUR; ++m) s_U[m * kScanThreads + tid] = ureg[m];
+        }
+    }
     __syncthreads();
-    const double excl = s_excl[0];
-    const double excl_next = s_excl[1];
-    TileValues<R, double> tv;
-    tv.prepare(q, X, excl, excl_next, last_tile, s_wmax);
+    const double excl = s_lb[0];
+    const double excl_next = s_lb[1];
+    const double T = s_lb[2];
+
+    // ---- 2. this tile's samples: the thresholds in (excl, excl_next]
+    if (wave == 0) {
+        const int64_t r = first_above2(excl, excl_next, T, Us, k);
+        if (lane == 0) s_range[0] = (tile == 0) ? 0 : r;
+        if (lane == 32) s_range[1] = last_tile ? k : r;
+    }
     const bool vec_out = vec_ok && tlen == TILE;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        double c[R][4];
+        double c[4];
 #pragma unroll
-        for (int cc = 0; cc < 4; ++cc) c[r][cc] = tv.at(q, X, r, cc);
+        for (int cc = 0; cc < 4; ++cc)
+            c[cc] = tile_value<double>(q[r][cc], excl, excl_next, r * ROW + 4 * tid + cc == tlen - 1);
         if (vec_out) {
             double2* o = reinterpret_cast<double2*>(cdf + base + r * ROW + 4 * tid);
-            o[0] = make_double2(c[r][0], c[r][1]);
-            o[1] = make_double2(c[r][2], c[r][3]);
+            o[0] = make_double2(c[0], c[1]);
+            o[1] = make_double2(c[2], c[3]);
         }
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             const int e = r * ROW + 4 * tid + cc;
-            s_C[e] = c[r][cc];
-            if (!vec_out && e < tlen) cdf[base + e] = c[r][cc];
-            if (last_tile && e == tlen - 1) {
-                total[0] = c[r][cc];
-                store_agent(&hdr[kHdrT + par], status_enc(c[r][cc]));
-            }
+            s_C[e] = c[cc];
+            if (!vec_out && e < tlen) cdf[base + e] = c[cc];
+            if (last_tile && e == tlen - 1) total[0] = c[cc];
         }
-    }
-
-    // ---- 2. T, then this tile's samples
-    if (wave == 0) {
-        const uint64_t* addr[1] = {&hdr[kHdrT + par]};
-        const bool need[1] = {lane == 0};
-        uint64_t w[1];
-        wait_words<1>(addr, need, w, &hdr[kHdrErr]);
-        if (lane == 0) {
-            double T;
-            status_dec(w[0], T);
-            s_T = T;
-        }
-    }
-    __syncthreads();
-    const double T = s_T;
-    if (wave == 0) {
-        const int64_t r = first_above2(excl, excl_next, T, U, k);
-        if (lane == 0) s_range[0] = (tile == 0) ? 0 : r;
-        if (lane == 32) s_range[1] = last_tile ? k : r;
     }
     __syncthreads();
     const int64_t i_lo = s_range[0];
     const int64_t i_hi = s_range[1];
 
-    // ---- 3. search in LDS, write the indices, local minimum of p
+    // ---- 3. search in LDS, write the indices, local minimum of p.  With at
+    // most one draw per thread (the usual case) each thread keeps its draw's
+    // index, the log2 of its priority and its new priority (fetched while it
+    // searches) in registers, and publishes the index in LDS for its
+    // neighbour.
+    const bool one_pass = i_hi - i_lo <= kScanThreads;
+    const int64_t i1 = i_lo + tid;
+    float my_new = 0.0f;
+    if (one_pass && newp != nullptr && i1 < i_hi) my_new = newp[i1];
+    int my_b = -1;
+    double my_lp = 0.0;
     uint32_t mn = 0xFFFFFFFFu;
-    for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
-        const double t = strat_threshold(i, U[i], k, T);
+    for (int64_t i = i1; i < i_hi; i += kScanThreads) {
+        const double t = strat_threshold(i, Us[i], k, T);
         int b = 0, len = tlen;
         while (len > 1) {
             const int half = len >> 1;
@@ -191,31 +225,51 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
         b += (s_C[b] < t) ? 1 : 0;
         if (b >= tlen) b = tlen - 1;
         out_idx[i] = (int32_t)(base + b);
-        const uint32_t key = __float_as_uint(s_p[b]);
+        my_b = b;
+        const float pb = s_p[b];
+        const uint32_t key = __float_as_uint(pb);
         mn = key < mn ? key : mn;
+        if (one_pass && pb > 0.0f) my_lp = log2_sig32((double)pb, &M);
     }
+    if (one_pass) s_b[tid] = my_b;
     mn = wave_min_u32(mn);
     if (lane == 0) atomicMin(&s_min, mn);
     __syncthreads();
 
-    // ---- 4. global minimum of the drawn priorities
-    if (tid == 0) store_agent(slot_word(slots, (uint64_t)tile, kSlotMin, par),
-                              (uint64_t)s_min + 1);
+    // ---- 4. publish the local minimum; rewrite the last draw of each index
+    // (draws of one index are adjacent and all in this tile, and only this
+    // tile reads that part of the priority array) while the others arrive
+    if (tid == 0) store_agent(&ws[min_off((uint32_t)tile, par)], (uint64_t)s_min + 1);
+    if (newp != nullptr) {
+        if (one_pass) {
+            if (i1 < i_hi) {
+                const bool winner = i1 + 1 >= i_hi || s_b[tid + 1] != my_b;
+                if (winner) prio[base + my_b] = my_new;
+            }
+        } else {
+            for (int64_t i = i1; i < i_hi; i += kScanThreads) {
+                const int32_t b = out_idx[i];
+                const bool winner = i + 1 >= i_hi || out_idx[i + 1] != b;
+                if (winner) prio[b] = newp[i];
+            }
+        }
+    }
     if (wave == 0) {
         uint32_t g = 0xFFFFFFFFu;
-        for (int t0 = 0; t0 < n_tiles; t0 += kGtWords * kWave) {
-            const uint64_t* addr[kGtWords];
-            bool need[kGtWords];
-            uint64_t w[kGtWords];
+#pragma nounroll
+        for (int t0 = 0; t0 < n_tiles; t0 += kAllWords * kWave) {
+            uint32_t off[kAllWords];
+            bool need[kAllWords];
+            uint64_t w[kAllWords];
 #pragma unroll
-            for (int j = 0; j < kGtWords; ++j) {
+            for (int j = 0; j < kAllWords; ++j) {
                 const int tt = t0 + j * kWave + lane;
-                addr[j] = slot_word(slots, (uint64_t)tt, kSlotMin, par);
                 need[j] = tt < n_tiles;
+                off[j] = min_off((uint32_t)(need[j] ? tt : 0), par);
             }
-            wait_words<kGtWords>(addr, need, w, &hdr[kHdrErr]);
+            wait_words<kAllWords>(ws, off, need, w);
 #pragma unroll
-            for (int j = 0; j < kGtWords; ++j)
+            for (int j = 0; j < kAllWords; ++j)
                 if (need[j]) {
                     const uint32_t key = (uint32_t)(w[j] - 1);
                     g = key < g ? key : g;
@@ -226,35 +280,40 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     }
     __syncthreads();
 
-    // ---- 5. IS weights and the rewrite of the last draw of each index
+    // ---- 5. IS weights
     const double pmin = (double)__uint_as_float(s_gmin);
     const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
-    for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
-        const int b = (int)(out_idx[i] - base);
-        out_w[i] = is_weight(pmin, lpmin, (double)s_p[b], ab, &M);
-        if (newp != nullptr) {
-            bool winner = i + 1 >= i_hi;
-            if (!winner) winner = out_idx[i + 1] != out_idx[i];
-            if (winner) prio[base + b] = newp[i];
+    if (one_pass) {
+        if (i1 < i_hi) out_w[i1] = is_weight_lp(pmin, lpmin, (double)s_p[my_b], my_lp, ab, &M);
+    } else {
+        for (int64_t i = i1; i < i_hi; i += kScanThreads) {
+            const int b = (int)(out_idx[i] - base);
+            out_w[i] = is_weight(pmin, lpmin, (double)s_p[b], ab, &M);
         }
     }
 }
 
-template <int R>
+template <int R, bool UL>
 static int per_round_capacity() {
-    return resident_grid(reinterpret_cast<const void*>(&k_per_round<R>), kScanThreads);
+    // VEC does not change the resources.
+    return resident_grid(reinterpret_cast<const void*>(&k_per_round<R, UL, true>), kScanThreads);
 }
 
-template <int R>
+template <int R, bool UL>
 static psamp_status launch_per_round(void* prio, int64_t n, double alpha, double ab,
                                      const float* u, int64_t k, const float* newp,
                                      int32_t* out_idx, float* out_w, double* cdf, double* total,
                                      void* ws, uint64_t max_slots, int vec_ok, hipStream_t st) {
     const int tiles = (int)ceil_div(n, kScanThreads * 4 * R);
     if (trace_enabled()) trace_launch("k_per_round", tiles, kScanThreads, n);
-    hipLaunchKernelGGL(k_per_round<R>, dim3(tiles), dim3(kScanThreads), 0, st, (float*)prio, n,
-                       alpha, ab, u, k, newp, out_idx, out_w, cdf, total, (uint64_t*)ws, tiles,
-                       max_slots, vec_ok);
+    if (aligned(prio, 16) && n % 4 == 0)
+        hipLaunchKernelGGL((k_per_round<R, UL, true>), dim3(tiles), dim3(kScanThreads), 0, st,
+                           (float*)prio, n, alpha, ab, u, k, newp, out_idx, out_w, cdf, total,
+                           (uint64_t*)ws, tiles, max_slots, vec_ok);
+    else
+        hipLaunchKernelGGL((k_per_round<R, UL, false>), dim3(tiles), dim3(kScanThreads), 0, st,
+                           (float*)prio, n, alpha, ab, u, k, newp, out_idx, out_w, cdf, total,
+                           (uint64_t*)ws, tiles, max_slots, vec_ok);
     return launch_status();
 }
 
@@ -285,17 +344,22 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
     const size_t scan_ws = psamp_build_cdf_workspace_size(n);
-    const uint64_t max_slots = (scan_ws - (size_t)kWsHeaderWords * 8) / (kSlotWords * 8);
-    const int vec_ok = aligned(prio, 16) && aligned(cdf, 16);
+    const uint64_t max_slots = ws_tile_capacity(scan_ws);
+    const int vec_ok = aligned(cdf, 16);   // 16-byte stores of whole tiles
     if (k > 0) {
-        const int64_t t1 = ceil_div(n, kScanThreads * 4);
-        const int64_t t4 = ceil_div(n, kScanThreads * 16);
-        if (t1 <= per_round_capacity<1>())
-            return launch_per_round<1>(prio, n, alpha, alpha * beta, u, k, new_prio, out_idx,
-                                       out_w, cdf, total, ws, max_slots, vec_ok, st);
-        if (t4 <= per_round_capacity<4>())
-            return launch_per_round<4>(prio, n, alpha, alpha * beta, u, k, new_prio, out_idx,
-                                       out_w, cdf, total, ws, max_slots, vec_ok, st);
+        // The scan's own tiling (so the CDF is the same bits as psamp_build_cdf's);
+        // U in LDS when it fits and the grid still is resident.
+#define PSAMP_PER_ROUND_TRY(RR, UU)                                                             \
+    if (ceil_div(n, kScanThreads * 4 * RR) <= per_round_capacity<RR, UU>())                    \
+        return launch_per_round<RR, UU>(prio, n, alpha, alpha * beta, u, k, new_prio, out_idx, \
+                                        out_w, cdf, total, ws, max_slots, vec_ok, st);
+        if (scan_rows_for(n) == 1) {
+            if (k <= kULds) PSAMP_PER_ROUND_TRY(1, true)
+            PSAMP_PER_ROUND_TRY(1, false)
+        } else {
+            PSAMP_PER_ROUND_TRY(8, false)
+        }
+#undef PSAMP_PER_ROUND_TRY
     }
     // Too large to be resident at once (or nothing to draw): the separate
     // kernels, same results.

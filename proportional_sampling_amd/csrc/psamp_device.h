@@ -126,27 +126,6 @@ __device__ __forceinline__ void status_dec(uint64_t w, double& v) {
 }
 __device__ __forceinline__ void status_dec(uint64_t w, uint64_t& v) { v = w - 1; }
 
-// Wait until the status word of every lane with `need` is non-zero, then
-// return it (0 for lanes without `need`).  The wait is bounded: after
-// `limit` polls the wave records an error bit and gives up, so a broken
-// invariant turns into a reported error instead of a hang.
-__device__ __forceinline__ uint64_t wait_status(const uint64_t* addr, bool need,
-                                                uint64_t* err_word, uint64_t err_bit,
-                                                int limit) {
-    uint64_t v = need ? load_agent(addr) : 0;
-    int polls = 0;
-    while (__any(need && v == 0)) {
-        if (++polls > limit) {
-            if (lane_id() == 0) __hip_atomic_fetch_or(err_word, err_bit, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-            break;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        if (need && v == 0) v = load_agent(addr);
-    }
-    return v;
-}
-
 // ------------------------------------------------------------ fp64 math
 // log2 and exp2 in double, accurate to a few 1e-16 relative (exp2) and a
 // few 1e-16 absolute (log2) -- far below what the sampling contract needs
@@ -163,6 +142,27 @@ __device__ __forceinline__ void math_lds_fill(MathLds* m, int tid, int nthreads)
                                      __longlong_as_double((long long)kLog2Tab[i][1]));
     for (int i = tid; i < 64; i += nthreads)
         m->exp_tab[i] = __longlong_as_double((long long)kExp2Tab[i][0]);
+}
+
+// The same in two steps for blocks of at least 128 threads: math_load()
+// issues the table loads (to be issued together with the kernel's other
+// first loads, so their latencies overlap), math_store() writes LDS.
+struct MathRegs {
+    double2 lg;
+    double ex;
+};
+__device__ __forceinline__ MathRegs math_load(int tid) {
+    // Unconditional loads (indices wrapped): a guarded load would be merged
+    // with its guarded LDS store and waited for on the spot.
+    MathRegs r;
+    r.lg = make_double2(__longlong_as_double((long long)kLog2Tab[tid & 127][0]),
+                        __longlong_as_double((long long)kLog2Tab[tid & 127][1]));
+    r.ex = __longlong_as_double((long long)kExp2Tab[tid & 63][0]);
+    return r;
+}
+__device__ __forceinline__ void math_store(MathLds* m, int tid, const MathRegs& r) {
+    if (tid < 128) m->log_tab[tid] = r.lg;
+    if (tid < 64) m->exp_tab[tid] = r.ex;
 }
 
 constexpr double kLog2e = 1.4426950408889634074;   // 1/ln 2
@@ -190,12 +190,13 @@ __device__ __forceinline__ double log2_sig32(double x, const MathLds* M) {
 
 // 2^y.  y = N/64 + f with N = rint(64 y), |f| <= 1/128 (f exact);
 // 2^f = e^g, g = f ln2, |g| < 0.0055, Taylor to g^5 (truncation < 4e-17);
-// 2^(j/64) from the table; the power of two by ldexp.
+// 2^(j/64) from the table; the power of two by ldexp.  Branch-free: y is
+// clamped to [-1100, 1100] first, where ldexp already saturates to +inf
+// (y >= 1024) or to 0 (y < -1075); a NaN y is passed through.
 __device__ __forceinline__ double exp2_tab(double y, const MathLds* M) {
-    if (!(y < 1025.0)) return (y != y) ? y : __longlong_as_double(0x7FF0000000000000ll);
-    if (y < -1100.0) return 0.0;
-    double N = rint(y * 64.0);
-    double f = fma(N, -1.0 / 64.0, y);
+    const double yc = fmin(fmax(y, -1100.0), 1100.0);
+    double N = rint(yc * 64.0);
+    double f = fma(N, -1.0 / 64.0, yc);
     int Ni = (int)N;
     int j = Ni & 63;
     int n = Ni >> 6;
@@ -206,14 +207,21 @@ __device__ __forceinline__ double exp2_tab(double y, const MathLds* M) {
     q = fma(g, q, 1.0);
     double em1 = g * q;                  // e^g - 1
     double s = M->exp_tab[j];
-    return ldexp(fma(s, em1, s), n);
+    const double r = ldexp(fma(s, em1, s), n);
+    return (y != y) ? y : r;
 }
 
-// p^alpha for a float priority p >= 0 and alpha > 0 (double).
+// p^alpha for a float priority p >= 0 and alpha > 0 (double).  Branch-free:
+// the power is formed for every lane (from 1 where p is not positive and
+// finite) and the special cases are selected: 0 -> 0, +inf -> +inf,
+// negative or NaN -> NaN.
 __device__ __forceinline__ double pow_prio(float p, double alpha, const MathLds* M) {
-    if (!(p > 0.0f)) return (p == 0.0f) ? 0.0 : __longlong_as_double(0x7FF8000000000000ll);
-    if (p == __int_as_float(0x7F800000)) return (double)p;
-    return exp2_tab(alpha * log2_sig32((double)p, M), M);
+    const float inf = __int_as_float(0x7F800000);
+    const bool fin = p > 0.0f && p < inf;
+    const double r = exp2_tab(alpha * log2_sig32((double)(fin ? p : 1.0f), M), M);
+    const uint32_t sp_hi = (p == 0.0f) ? 0u : (p == inf) ? 0x7FF00000u : 0x7FF80000u;
+    const double sp = __hiloint2double((int)sp_hi, 0);
+    return fin ? r : sp;
 }
 
 // e^x for a finite double x (the particle weights).
@@ -296,6 +304,13 @@ __device__ __forceinline__ float is_weight(double pmin, double lpmin, double p, 
     if (!(p > 0.0)) return __int_as_float(0x7FC00000);
     if (!(pmin > 0.0)) return 0.0f;
     return (float)exp2_tab(e * (lpmin - log2_sig32(p, M)), M);
+}
+// The same with lp = log2(p) already known.
+__device__ __forceinline__ float is_weight_lp(double pmin, double lpmin, double p, double lp,
+                                              double e, const MathLds* M) {
+    if (!(p > 0.0)) return __int_as_float(0x7FC00000);
+    if (!(pmin > 0.0)) return 0.0f;
+    return (float)exp2_tab(e * (lpmin - lp), M);
 }
 
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {

@@ -52,8 +52,8 @@ __device__ __forceinline__ void store4<float>(float* p, const float (&o)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
 }
 
-// One workgroup per tile, tiles in blockIdx order.
-template <int IPT, class In, class Out>
+// One workgroup per tile, tiles in blockIdx order.  VEC: see load_tile.
+template <int IPT, bool VEC, class In, class Out>
 __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     const In* __restrict__ in, int64_t n, double alpha, Out* __restrict__ cdf,
     Out* __restrict__ total, uint64_t* __restrict__ ws, int n_tiles,
@@ -68,100 +68,120 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     __shared__ Acc s_wtot[4][R];
     __shared__ double s_wmax[4][R];
     __shared__ Acc s_excl[2];
-    __shared__ uint32_t s_calls;
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int tile = (int)blockIdx.x;
     const int64_t base = (int64_t)tile * TILE;
-    uint64_t* hdr = ws;
-    uint64_t* slots = ws + kWsHeaderWords;
+    const int tlen = (int)min_<int64_t>(TILE, n - base);   // valid elements, >= 1
 
-    // hdr[kHdrCalls] counts calls; its parity selects this call's status
+    // ws[kHdrCalls] counts calls; its parity selects this call's status
     // words.  The workgroup that owns the last tile advances it once its
     // lookback has seen every other tile's sum -- by then every workgroup
-    // has read it.
-    if (tid == 0) s_calls = (uint32_t)load_agent(&hdr[kHdrCalls]);
-    if (kFp) math_lds_fill(&M, tid, kScanThreads);
+    // has read it.  All first loads (counter, high-water mark, pow tables,
+    // priorities) are issued together, so their latencies overlap.
+    // (The priorities go first: the counter words are made uniform, which
+    // makes the compiler wait for them where they are loaded.)
     In v[R][4];
-    load_tile<R, In>(in, n, base, vec_ok, v);
+    load_tile<R, VEC, In>(in + base, tlen, v);
+    asm volatile("" ::: "memory");
+    MathRegs mr;
+    if (kFp) mr = math_load(tid);
+    const uint64_t calls_w = load_agent(&ws[kHdrCalls]);
+    const uint64_t hw_w = load_agent(&ws[kHdrHw]);
+    if (kFp) math_store(&M, tid, mr);
     __syncthreads();
-    const uint32_t calls = s_calls;
+    const uint32_t calls = (uint32_t)calls_w;
     const int par = (int)(calls & 1u);
-    clear_other_parity(hdr, slots, par, n_tiles, max_slots);
 
     // ---- weights and the thread-local prefix of each row
+    // (Each row's values are pinned where they are formed: left to itself
+    // the compiler sinks every pow's tail to the tile scan and keeps all 32
+    // half-done pows live at once.)
     Acc q[R][4];
 #pragma unroll
-    for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const Acc w = to_weight(v[r][c], alpha, &M);
             q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
         }
+        if constexpr (kFp) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(q[r][c]));
+        }
+    }
 
     // ---- tile-local scan: DPP across the wave, LDS across the 4 waves
     Acc X[R];
     Acc A;
     tile_scan_256<R, Acc>(q, X, A, s_wtot);
 
-    // ---- publish the tile sum, then look back (wave 0)
-    if (tid == 0) store_agent(slot_word(slots, (uint64_t)tile, kSlotA, par), status_enc(A));
-    if (wave == 0) lookback<Acc>(tile, n_tiles, par, A, slots, hdr, calls, s_excl);
+    // ---- publish the tile sum; the local values (running max in fp mode)
+    // while it travels; then look back (wave 0) while the other waves clear
+    // the other parity
+    if (tid == 0) store_agent(&ws[a_off((uint32_t)tile, par)], status_enc(A));
+    tile_local_values<R, Acc>(q, X, s_wmax);
+    if (wave == 0)
+        lookback<Acc>(tile, n_tiles, par, A, ws, calls, s_excl);
+    else
+        clear_other_parity(ws, par, n_tiles, max_slots, hw_w, tid - kWave, kScanThreads - kWave);
     __syncthreads();
 
-    // ---- outputs (monotone and tile-consistent in fp mode)
-    TileValues<R, Acc> tv;
-    tv.prepare(q, X, s_excl[0], s_excl[1], tile == n_tiles - 1, s_wmax);
-    const bool full = vec_ok && base + TILE <= n;
-    const int64_t last = n - 1;
+    // ---- outputs (monotone and tile-consistent in fp mode); tile-local
+    // 32-bit offsets
+    const Acc excl = s_excl[0], next = s_excl[1];
+    const bool full = vec_ok && tlen == TILE;
+    Out* __restrict__ tout = cdf + base;
+    const int t4 = 4 * tid;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
+        const int e0 = r * ROW + t4;
         Out o[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) o[k] = to_out<Out>(tv.at(q, X, r, k));
+        for (int k = 0; k < 4; ++k)
+            o[k] = to_out<Out>(tile_value<Acc>(q[r][k], excl, next, e0 + k == tlen - 1));
         if (full) {
-            store4<Out>(cdf + base + r * ROW + 4 * tid, o);
+            store4<Out>(tout + e0, o);
         } else {
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t i = base + r * ROW + 4 * tid + k;
-                if (i < n) cdf[i] = o[k];
-            }
+            for (int k = 0; k < 4; ++k)
+                if (e0 + k < tlen) tout[e0 + k] = o[k];
         }
         // T = C_{n-1}, written by the thread that owns element n-1.
+        if (tile == n_tiles - 1) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (base + r * ROW + 4 * tid + k == last) total[0] = o[k];
+            for (int k = 0; k < 4; ++k)
+                if (e0 + k == tlen - 1) total[0] = o[k];
+        }
     }
 }
-
-static size_t ws_bytes_for_tiles(int64_t tiles) {
-    return (size_t)kWsHeaderWords * 8 + (size_t)tiles * kSlotWords * 8;
-}
-
-constexpr int kScanBigIpt = 32;
 
 template <int IPT, class In, class Out>
 static psamp_status launch_scan(const void* prio, int64_t n, double alpha, void* cdf, void* total,
                                 void* ws, uint64_t max_slots, int vec_ok, hipStream_t st) {
     const int tiles = (int)ceil_div(n, kScanThreads * IPT);
     if (trace_enabled()) trace_launch("k_build_cdf", tiles, kScanThreads, n);
-    hipLaunchKernelGGL((k_build_cdf<IPT, In, Out>), dim3(tiles), dim3(kScanThreads), 0, st,
-                       (const In*)prio, n, alpha, (Out*)cdf, (Out*)total, (uint64_t*)ws, tiles,
-                       max_slots, vec_ok);
+    const bool vec_in = aligned(prio, 16) && n % 4 == 0;
+    if (vec_in)
+        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Out>), dim3(tiles), dim3(kScanThreads), 0,
+                           st, (const In*)prio, n, alpha, (Out*)cdf, (Out*)total, (uint64_t*)ws,
+                           tiles, max_slots, vec_ok);
+    else
+        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Out>), dim3(tiles), dim3(kScanThreads), 0,
+                           st, (const In*)prio, n, alpha, (Out*)cdf, (Out*)total, (uint64_t*)ws,
+                           tiles, max_slots, vec_ok);
     return launch_status();
 }
 
 template <class In, class Out>
 static psamp_status launch_build_cdf(const void* prio, int64_t n, double alpha, void* cdf,
                                      void* total, void* ws, size_t ws_bytes, hipStream_t st) {
-    const uint64_t max_slots = (ws_bytes - (size_t)kWsHeaderWords * 8) / (kSlotWords * 8);
-    const int vec_ok = aligned(prio, 16) && aligned(cdf, 16);
-    if (n <= (int64_t(1) << 20))
+    const uint64_t max_slots = ws_tile_capacity(ws_bytes);
+    const int vec_ok = aligned(cdf, 16);   // 16-byte stores of whole tiles
+    if (scan_rows_for(n) == 1)
         return launch_scan<4, In, Out>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, st);
-    return launch_scan<kScanBigIpt, In, Out>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok,
-                                             st);
+    return launch_scan<32, In, Out>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, st);
 }
 
 }  // namespace psamp

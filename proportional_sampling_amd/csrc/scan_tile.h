@@ -4,20 +4,39 @@
 //
 // The CDF of the pages is one serial prefix sum ("trainer: parallel
 // build_cdf scan + tiled ... mingru backward", "1. Parallel build_cdf").
-// Here it is formed tile by tile (256 threads x 4R elements).  In fp mode
-// the result is made exactly monotone and its tile boundaries are made
-// consistent, at the cost of changes of a few ulps at most:
-//   * tile j's exclusive prefix excl_j = F_g + P_j, where P_j is a DPP tree
-//     over the sums of the earlier tiles of its group (non-decreasing in j)
-//     and F_g = ((GT_0 + GT_1) + ...) + GT_{g-1} is a serial fold of the
-//     group totals, so excl is non-decreasing across group boundaries too;
-//   * inside a tile, a running max removes rounding dips between threads;
-//   * every tile but the last is clamped from above by excl_{j+1} (which it
-//     computes exactly as tile j+1 will) and its last element is set to
-//     excl_{j+1}.  So C[end_j - 1] == excl_{j+1} <= C[end_j], the CDF is
-//     non-decreasing everywhere, and tile j owns exactly the thresholds in
-//     (excl_j, excl_{j+1}] (tile 0 from -inf, the last tile up to +inf).
-// Integer mode is exact and needs none of this.
+// Here it is formed tile by tile (256 threads x 4R elements) in one pass,
+// and in fp mode its value does not depend on timing: every partial sum is
+// a fixed expression of the tile sums A_j.
+//   * Tiles form groups of 64.  P_j (the sum of the earlier tiles of j's
+//     group) is the 64-lane DPP tree over A of those tiles (0 in the other
+//     lanes); the group total GT_g is the same tree over all 64 tiles.
+//   * excl_j = Outer(GT_0, ..., GT_{g-1}, P_j): group h is a leaf in lane
+//     h mod 64, slot h / 64; each lane adds its leaves in slot order, then
+//     the 64 lane sums go through the DPP tree.  Rounding is monotone and
+//     every leaf is >= 0, so excl_j is non-decreasing in j, and
+//     excl_{j+1}, computed by tile j (with P_{j+1}, or GT_g at a group end)
+//     is bit for bit the value tile j+1 computes.
+//   * A tile waits only for sums of tiles near it: it reads A of its own
+//     group and of the previous one (and forms GT_{g-1} itself), and the
+//     published totals of the groups before that, which are 64 or more tiles
+//     older.  One hop, no serial fold.
+//   * Inside a tile, a running max removes rounding dips between threads;
+//     every tile is clamped from above by excl_{j+1} and its last element is
+//     set to excl_{j+1}.  So C[end_j - 1] == excl_{j+1} <= C[end_j], the CDF
+//     is non-decreasing everywhere, tile j owns exactly the thresholds in
+//     (excl_j, excl_{j+1}] (tile 0 from -inf, the last tile up to +inf), and
+//     the total T = C_{n-1} is the Outer tree over all group totals, a value
+//     any tile that has read every A can form.
+// Integer mode is exact and needs none of this, but shares the code.
+//
+// Workspace: a 256-byte header, then one 4 KiB block per 64 tiles (block b
+// holds the words of tiles 64b..64b+63):
+//   [  0,  64) A, parity 0      [ 64, 128) A, parity 1
+//   [128, 192) MIN, parity 0    [192, 256) MIN, parity 1
+//   [256, 512) group totals GT of groups 128b..128b+127, two parities each
+// Consecutive tiles' words are adjacent, so a wave reads 64 of them in a
+// few cache lines.  The layout does not depend on n or on the workspace
+// size, so a workspace can serve calls of any size.
 #pragma once
 
 #include <type_traits>
@@ -27,15 +46,47 @@
 namespace psamp {
 
 constexpr int kScanThreads = 256;
-constexpr int kScanGroup = 64;         // tiles per lookback group
+constexpr int kScanGroup = 64;         // tiles per lookback group (one per lane)
 constexpr int kWsHeaderWords = 32;     // 256-byte header
-constexpr int kSlotWords = 8;          // per tile: {A, GT, MIN} x 2 parities + 2 spare
+constexpr int kBlockWords = 512;       // status words per 64 tiles
 constexpr int kMinTile = kScanThreads * 4;
 constexpr int kSpinLimit = 1 << 21;    // bounded waits (about a second)
-constexpr int kGtWords = 4;            // group totals per lane per round trip
+constexpr int kLbGtWords = 2;          // group totals per lane per round trip (lookback)
+constexpr int kAllWords = 4;           // tile sums per lane per round trip (lookback_all)
 
-enum : int { kSlotA = 0, kSlotGT = 2, kSlotMin = 4 };
-enum : int { kHdrCalls = 0, kHdrHw = 1, kHdrErr = 2, kHdrT = 4 };
+enum : int { kHdrCalls = 0, kHdrHw = 1, kHdrErr = 2, kHdrT = 4, kHdrDummy = 8 };
+
+// Rows of 1024 elements per tile.  The tiling fixes the association of the
+// fp sums, so the scan and the fused update both take it from here.
+constexpr int64_t kSmallScanN = int64_t(1) << 20;
+__host__ __device__ constexpr int scan_rows_for(int64_t n) { return n <= kSmallScanN ? 1 : 8; }
+
+// Bytes of workspace for up to `tiles` tiles, and the tiles a workspace holds.
+__host__ __device__ constexpr size_t ws_bytes_for_tiles(int64_t tiles) {
+    return (size_t)kWsHeaderWords * 8 +
+           (size_t)((tiles + kScanGroup - 1) / kScanGroup) * kBlockWords * 8;
+}
+__host__ __device__ constexpr uint64_t ws_tile_capacity(size_t ws_bytes) {
+    return ws_bytes < (size_t)kWsHeaderWords * 8
+               ? 0
+               : (uint64_t)((ws_bytes - (size_t)kWsHeaderWords * 8) / (kBlockWords * 8)) *
+                     kScanGroup;
+}
+
+// Status words are addressed by their word offset from the start of the
+// workspace (32 bits: a workspace never holds more than 2^31 / 1024 tiles).
+__device__ __forceinline__ uint32_t a_off(uint32_t tile, int par) {
+    return kWsHeaderWords + (tile / kScanGroup) * kBlockWords + par * kScanGroup +
+           tile % kScanGroup;
+}
+__device__ __forceinline__ uint32_t min_off(uint32_t tile, int par) {
+    return kWsHeaderWords + (tile / kScanGroup) * kBlockWords + 2 * kScanGroup +
+           par * kScanGroup + tile % kScanGroup;
+}
+__device__ __forceinline__ uint32_t gt_off(uint32_t group, int par) {
+    return kWsHeaderWords + (group / 128) * kBlockWords + 4 * kScanGroup + 2 * (group % 128) +
+           par;
+}
 
 template <class In> struct ScanAcc;
 template <> struct ScanAcc<float> { using type = double; };
@@ -48,209 +99,296 @@ __device__ __forceinline__ uint64_t to_weight(uint32_t q, double, const MathLds*
     return (uint64_t)q;
 }
 
-__device__ __forceinline__ uint64_t* slot_word(uint64_t* slots, uint64_t tile, int kind, int par) {
-    return &slots[kSlotWords * tile + kind + par];
-}
-
-template <int R, class In>
-__device__ __forceinline__ void load_tile(const In* __restrict__ in, int64_t n, int64_t base,
-                                          bool vec_ok, In (&v)[R][4]) {
+// Loads a tile: tin points at the tile's first element, tlen (>= 1) is the
+// number of valid elements.  VEC: the input is 16-byte aligned and n % 4 ==
+// 0, so every 4-element chunk is wholly valid or wholly invalid and is read
+// with one 16-byte load; otherwise element by element.  Invalid elements
+// read as 0: every load is issued (from the tile's element 0 when invalid)
+// and the value selected afterwards -- a load under a branch would be waited
+// for at the end of the branch, one round trip per load.  Offsets are 32-bit
+// and tile-local, so the addresses stay a uniform base plus a lane offset.
+template <int R, bool VEC, class In>
+__device__ __forceinline__ void load_tile(const In* __restrict__ tin, int tlen, In (&v)[R][4]) {
     constexpr int ROW = kScanThreads * 4;
-    const int tid = threadIdx.x;
-    if (vec_ok && base + (int64_t)R * ROW <= n) {
+    const int t4 = 4 * (int)threadIdx.x;
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-            const uint4 x = *reinterpret_cast<const uint4*>(in + base + r * ROW + 4 * tid);
-            v[r][0] = __builtin_bit_cast(In, x.x);
-            v[r][1] = __builtin_bit_cast(In, x.y);
-            v[r][2] = __builtin_bit_cast(In, x.z);
-            v[r][3] = __builtin_bit_cast(In, x.w);
-        }
-    } else {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
+    for (int r = 0; r < R; ++r) {
+        const int e0 = r * ROW + t4;
+        if constexpr (VEC) {
+            const bool ok = e0 < tlen;
+            const uint4 x = *reinterpret_cast<const uint4*>(tin + (ok ? e0 : 0));
+            v[r][0] = ok ? __builtin_bit_cast(In, x.x) : In(0);
+            v[r][1] = ok ? __builtin_bit_cast(In, x.y) : In(0);
+            v[r][2] = ok ? __builtin_bit_cast(In, x.z) : In(0);
+            v[r][3] = ok ? __builtin_bit_cast(In, x.w) : In(0);
+        } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int64_t i = base + r * ROW + 4 * tid + c;
-                v[r][c] = i < n ? in[i] : In(0);
+                const bool ok = e0 + c < tlen;
+                const In e = tin[ok ? e0 + c : 0];
+                v[r][c] = ok ? e : In(0);
             }
+        }
     }
 }
 
-// Zero the other parity's status words (A, GT, MIN of every slot below the
-// high-water mark, and its T word) so that the next call finds them clean.
-__device__ __forceinline__ void clear_other_parity(uint64_t* hdr, uint64_t* slots, int par,
-                                                   int n_tiles, uint64_t max_slots) {
-    const int tid = threadIdx.x;
-    uint64_t hw = load_agent(&hdr[kHdrHw]);
+// Zero the other parity's status words (A and MIN of every tile below the
+// high-water mark, GT of their groups, and the other T word) so that the
+// next call finds them clean.  The high-water mark is the largest tile count
+// any call on this workspace has used (hw_seen: its value when the kernel
+// started).  Threads t = 0..nt-1 of every workgroup share the work; it is
+// done while wave 0 looks back.
+__device__ __forceinline__ void clear_other_parity(uint64_t* ws, int par, int n_tiles,
+                                                   uint64_t max_tiles, uint64_t hw_seen, int t,
+                                                   int nt) {
+    uint64_t hw = hw_seen;
     if (hw < (uint64_t)n_tiles) hw = (uint64_t)n_tiles;
-    if (hw > max_slots) hw = max_slots;
-    if (blockIdx.x == 0 && tid == 0) {
-        fetch_max_agent(&hdr[kHdrHw], (uint64_t)n_tiles);
-        hdr[kHdrT + (par ^ 1)] = 0;
-    }
+    if (hw > max_tiles) hw = max_tiles;
     const int op = par ^ 1;
-    for (uint64_t s = (uint64_t)blockIdx.x * kScanThreads + tid; s < hw;
-         s += (uint64_t)gridDim.x * kScanThreads) {
-        slots[kSlotWords * s + kSlotA + op] = 0;
-        slots[kSlotWords * s + kSlotGT + op] = 0;
-        slots[kSlotWords * s + kSlotMin + op] = 0;
+    if (blockIdx.x == 0 && t == 0) {
+        fetch_max_agent(&ws[kHdrHw], (uint64_t)n_tiles);
+        ws[kHdrT + op] = 0;
+    }
+    const uint32_t groups = (uint32_t)((hw + kScanGroup - 1) / kScanGroup);
+    for (uint32_t s = blockIdx.x * (uint32_t)nt + t; s < hw; s += gridDim.x * (uint32_t)nt) {
+        ws[a_off(s, op)] = 0;
+        ws[min_off(s, op)] = 0;
+        if (s < groups) ws[gt_off(s, op)] = 0;
     }
 }
 
-// Wait (wave-wide, bounded) until every lane's needed words are non-zero.
+// Wait (wave-wide, bounded) until every lane's needed words ws[off[i]] are
+// non-zero.  Words that are not needed are set to 1, which decodes to 0 in
+// both status encodings.  Two polls are kept in flight: the next one is
+// issued before the previous one is examined, which halves the time between
+// a word being published and the wave seeing it.  A lane whose word is
+// already known (or not needed) reads a dummy header word that all such
+// lanes share, so the loop has no per-word branch.
 template <int NW>
-__device__ __forceinline__ void wait_words(const uint64_t* const (&addr)[NW], const bool (&need)[NW],
-                                           uint64_t (&w)[NW], uint64_t* err_word) {
+__device__ __forceinline__ void wait_words(const uint64_t* ws, const uint32_t (&off)[NW],
+                                           const bool (&need)[NW], uint64_t (&w)[NW]) {
+    uint64_t a[NW];
 #pragma unroll
-    for (int i = 0; i < NW; ++i) w[i] = need[i] ? load_agent(addr[i]) : 0;
+    for (int i = 0; i < NW; ++i) {
+        a[i] = load_agent(&ws[need[i] ? off[i] : (uint32_t)kHdrDummy]);
+        w[i] = need[i] ? 0 : 1;
+    }
+    // The bound is hidden from the optimiser: with a known trip count it
+    // unrolls the poll loop into a hundred copies.
+    int limit = kSpinLimit;
+    asm volatile("" : "+s"(limit));
     int polls = 0;
     for (;;) {
+        uint64_t b[NW];
+        for (int i = 0; i < NW; ++i)
+            b[i] = load_agent(&ws[w[i] == 0 ? off[i] : (uint32_t)kHdrDummy]);
         bool missing = false;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) missing = missing || (need[i] && w[i] == 0);
+        for (int i = 0; i < NW; ++i) {
+            w[i] = w[i] == 0 ? a[i] : w[i];
+            missing = missing || w[i] == 0;
+        }
         if (!__any(missing)) break;
-        if (++polls > kSpinLimit) {
+        if (++polls > limit) {
             if (lane_id() == 0)
-                __hip_atomic_fetch_or(err_word, (uint64_t)1, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_or(const_cast<uint64_t*>(&ws[kHdrErr]), (uint64_t)1,
+                                      __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             break;
         }
         __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-        for (int i = 0; i < NW; ++i)
-            if (need[i] && w[i] == 0) w[i] = load_agent(addr[i]);
+        for (int i = 0; i < NW; ++i) a[i] = b[i];
     }
 }
 
-// Serial (left to right) sum of one value per lane, lanes 0..cnt-1, added to f.
 template <class Acc>
-__device__ __forceinline__ Acc serial_fold(Acc f, Acc x, int cnt) {
-    for (int l = 0; l < cnt; ++l) f = f + readlane(x, l);
-    return f;
+__device__ __forceinline__ Acc status_value(uint64_t w) {
+    Acc x;
+    status_dec(w, x);
+    return x;
 }
 
-// Lookback of one tile, called by wave 0.  Needs the sums A of the earlier
-// tiles of its group and the totals GT of the earlier groups; all words are
-// requested in one round trip, then folded in a fixed order.  Returns
-// excl_j and excl_{j+1} (see the header comment).  The tile that ends a
-// group publishes the group total; the last tile advances the call counter.
+// Lookback of one tile, called by wave 0 after the tile published its sum
+// A.  Reads A of the earlier tiles of its group and of the whole previous
+// group, and the published totals GT_h of the groups h < g - 1, all in one
+// round trip (more only past 64 * kLbGtWords groups); forms P_j, P_{j+1},
+// GT_{g-1} and the two Outer trees of the header comment.  Writes excl_j to
+// s_excl[0] and excl_{j+1} to s_excl[1].  The tile that ends a group
+// publishes GT_g; the last tile advances the call counter.
 template <class Acc>
-__device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, uint64_t* slots,
-                                         uint64_t* hdr, uint32_t calls, Acc* s_excl) {
+__device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, uint64_t* ws,
+                                         uint32_t calls, Acc* s_excl) {
     const int lane = threadIdx.x & 63;
     const int g = tile / kScanGroup;
-    const int first = g * kScanGroup;
-    const int cnt = tile - first;
-    Acc F = Acc(0);
-    Acc P = Acc(0), Pn = Acc(0);
-    bool have_p = false;
-    for (int h0 = 0; h0 < g || !have_p; h0 += kGtWords * kWave) {
-        const uint64_t* addr[kGtWords + 1];
-        bool need[kGtWords + 1];
-        uint64_t w[kGtWords + 1];
-        addr[0] = slot_word(slots, (uint64_t)(first + lane), kSlotA, par);
-        need[0] = !have_p && lane < cnt;
+    const int cnt = tile - g * kScanGroup;
+    const int gp = g > 0 ? g - 1 : 0;
+    Acc base = Acc(0);     // this lane's published leaves h < g - 1, in slot order
+    Acc P = Acc(0), Pn = Acc(0), Gp = Acc(0);
+#pragma nounroll
+    for (int s0 = 0;; s0 += kLbGtWords) {
+        const bool first = s0 == 0;
+        uint32_t off[kLbGtWords + 2];
+        bool need[kLbGtWords + 2];
+        uint64_t w[kLbGtWords + 2];
+        need[0] = first && g > 0;
+        off[0] = a_off((uint32_t)(gp * kScanGroup + lane), par);
+        need[1] = first && lane < cnt;
+        off[1] = a_off((uint32_t)(g * kScanGroup + lane), par);
 #pragma unroll
-        for (int i = 0; i < kGtWords; ++i) {
-            const int h = h0 + i * kWave + lane;
-            addr[i + 1] = slot_word(slots, (uint64_t)h * kScanGroup, kSlotGT, par);
-            need[i + 1] = h < g;
+        for (int i = 0; i < kLbGtWords; ++i) {
+            const int h = (s0 + i) * kWave + lane;
+            need[i + 2] = h < g - 1;
+            off[i + 2] = gt_off((uint32_t)(need[i + 2] ? h : 0), par);
         }
-        wait_words<kGtWords + 1>(addr, need, w, &hdr[kHdrErr]);
-        if (!have_p) {
-            Acc a = Acc(0);
-            if (lane < cnt) status_dec(w[0], a);
+        wait_words<kLbGtWords + 2>(ws, off, need, w);
+        if (first) {
+            const Acc a = need[1] ? status_value<Acc>(w[1]) : Acc(0);
             P = wave_sum(a);
             Pn = wave_sum(lane == cnt ? A : a);
-            have_p = true;
             if (cnt == kScanGroup - 1 && lane == 0)
-                store_agent(slot_word(slots, (uint64_t)first, kSlotGT, par), status_enc(P + A));
+                store_agent(&ws[gt_off((uint32_t)g, par)], status_enc(Pn));
+            if (g > 0) Gp = wave_sum(need[0] ? status_value<Acc>(w[0]) : Acc(0));
         }
 #pragma unroll
-        for (int i = 0; i < kGtWords; ++i) {
-            const int base = h0 + i * kWave;
-            if (base < g) {
-                Acc x = Acc(0);
-                if (need[i + 1]) status_dec(w[i + 1], x);
-                F = serial_fold(F, x, min_(kWave, g - base));
-            }
-        }
+        for (int i = 0; i < kLbGtWords; ++i)
+            if (need[i + 2]) base = base + status_value<Acc>(w[i + 2]);
+        if ((s0 + kLbGtWords) * kWave >= g - 1) break;
     }
+    if (g > 0 && lane == (g - 1) % kWave) base = base + Gp;
+    const bool mine = lane == g % kWave;
+    const Acc excl = wave_sum(mine ? base + P : base);
+    const Acc next = wave_sum(mine ? base + Pn : base);
     if (lane == 0) {
-        const Acc excl = F + P;
-        // excl of the next tile: same group -> F + P_{j+1}; group end ->
-        // F_{g+1} = F_g + GT_g with GT_g = P_j + A_j.
-        const Acc next = (cnt < kScanGroup - 1) ? F + Pn : F + (P + A);
         s_excl[0] = excl;
         s_excl[1] = next;
-        if (tile == n_tiles - 1) store_agent(&hdr[kHdrCalls], (uint64_t)(calls + 1u));
+        if (tile == n_tiles - 1) store_agent(&ws[kHdrCalls], (uint64_t)(calls + 1u));
     }
 }
 
-// The tile's CDF values: excl + local prefix; in fp mode made monotone and
-// clamped to the next tile's exclusive prefix (see the header comment).
-// prepare() runs the block-wide part (one barrier, fp only): pm[r] is the
-// max over all tile values before this thread's 4 elements of row r (row-
-// major order r, thread, column) -- a thread's own 4 values are ordered, so
-// max(value, pm[r]) is the running max.  at() forms one element's value.
-template <int R, class Acc>
-struct TileValues {
-    Acc excl, next;
-    bool last;
-    double pm[R];
-
-    __device__ __forceinline__ void prepare(const Acc (&q)[R][4], const Acc (&X)[R], Acc excl_,
-                                            Acc next_, bool last_, double (*s_wmax)[R]) {
-        excl = excl_;
-        next = next_;
-        last = last_;
-        if constexpr (std::is_same<Acc, double>::value) {
-            const int tid = threadIdx.x;
-            const int wave = tid >> 6;
-            const int lane = tid & 63;
-            double ex[R];
+// Lookback of a tile when the whole grid is resident (the fused update):
+// every tile reads the sums A of all tiles (kAllWords groups per round trip),
+// forms every group total GT_h itself and writes excl_j, excl_{j+1} and the
+// total T = Outer(GT_0, ..., GT_{G-1}) to s_out[0..2].  The association is
+// that of lookback() (lane h mod 64 adds its leaves in increasing h, then
+// the DPP tree), so excl_j and excl_{j+1} are bit for bit the values the
+// standalone scan forms, and T equals the scan's C_{n-1}.  No hop through
+// the last tile is needed to learn T.
+template <class Acc>
+__device__ __forceinline__ void lookback_all(int tile, int n_tiles, int par, Acc A, uint64_t* ws,
+                                             uint32_t calls, Acc* s_out) {
+    const int lane = threadIdx.x & 63;
+    const int g = tile / kScanGroup;
+    const int cnt = tile - g * kScanGroup;
+    const int G = (n_tiles + kScanGroup - 1) / kScanGroup;
+    Acc accx = Acc(0);     // this lane's leaves h < g, in increasing h
+    Acc acct = Acc(0);     // this lane's leaves h < G
+    Acc P = Acc(0), Pn = Acc(0);
+#pragma nounroll
+    for (int h0 = 0; h0 < G; h0 += kAllWords) {
+        uint32_t off[kAllWords];
+        bool need[kAllWords];
+        uint64_t w[kAllWords];
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                double x = excl + (X[r] + q[r][3]);   // values are >= 0: 0 is the max identity
-                x = fmax(x, dpp<kRowShr1, 0xF, true>(x));
-                x = fmax(x, dpp<kRowShr2, 0xF, true>(x));
-                x = fmax(x, dpp<kRowShr4, 0xF, true>(x));
-                x = fmax(x, dpp<kRowShr8, 0xF, true>(x));
-                x = fmax(x, dpp<kRowBcast15, 0xA, false>(x));
-                x = fmax(x, dpp<kRowBcast31, 0xC, false>(x));
-                ex[r] = wave_shr1(x);
-                const double wm = readlane(x, kWave - 1);
-                if (lane == 0) s_wmax[wave][r] = wm;
-            }
-            __syncthreads();
-            double carry = 0.0;                      // max over earlier rows
+        for (int i = 0; i < kAllWords; ++i) {
+            const int t = (h0 + i) * kScanGroup + lane;
+            need[i] = t < n_tiles && t != tile;
+            off[i] = a_off((uint32_t)(need[i] ? t : 0), par);
+        }
+        wait_words<kAllWords>(ws, off, need, w);
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                double p = carry, rm = carry;
-#pragma unroll
-                for (int w2 = 0; w2 < 4; ++w2) {
-                    const double t = s_wmax[w2][r];
-                    if (w2 < wave) p = fmax(p, t);
-                    rm = fmax(rm, t);
+        for (int i = 0; i < kAllWords; ++i) {
+            const int h = h0 + i;
+            if (h < G) {
+                Acc a = need[i] ? status_value<Acc>(w[i]) : Acc(0);
+                if (h == g) {
+                    const Acc below = lane < cnt ? a : Acc(0);
+                    P = wave_sum(below);
+                    Pn = wave_sum(lane == cnt ? A : below);
+                    if (lane == cnt) a = A;
                 }
-                pm[r] = fmax(p, ex[r]);
-                carry = rm;
+                const Acc gt = wave_sum(a);
+                if (lane == h % kWave) {
+                    if (h < g) accx = accx + gt;
+                    acct = acct + gt;
+                }
             }
         }
     }
+    const bool mine = lane == g % kWave;
+    const Acc excl = wave_sum(mine ? accx + P : accx);
+    const Acc next = wave_sum(mine ? accx + Pn : accx);
+    const Acc T = wave_sum(acct);
+    if (lane == 0) {
+        s_out[0] = excl;
+        s_out[1] = next;
+        s_out[2] = T;
+        if (tile == n_tiles - 1) store_agent(&ws[kHdrCalls], (uint64_t)(calls + 1u));
+    }
+}
 
-    __device__ __forceinline__ Acc at(const Acc (&q)[R][4], const Acc (&X)[R], int r, int k) const {
-        Acc x = excl + (X[r] + q[r][k]);
-        if constexpr (std::is_same<Acc, double>::value) {
-            x = fmax(x, pm[r]);
-            if (!last) {
-                x = fmin(x, next);
-                if (r == R - 1 && k == 3 && threadIdx.x == kScanThreads - 1) x = next;
-            }
+// The tile's local values, in place.  On entry q[r][c] is the prefix of the
+// thread's 4 elements of row r and X[r] the sum of the tile's elements
+// before them; on exit q[r][c] = fl(X[r] + q[r][c]), and in fp mode also
+// raised to the running max of all local values before it in memory order
+// (rows, then threads, then columns; a thread's own 4 values are already
+// ordered).  fl(excl + x) is non-decreasing in x, so raising the local
+// values before adding excl gives the same bits as raising the sums:
+// max_i fl(excl + x_i) = fl(excl + max_i x_i).  One barrier (fp only); runs
+// before the lookback, so only q stays live across it.
+template <int R, class Acc>
+__device__ __forceinline__ void tile_local_values(Acc (&q)[R][4], const Acc (&X)[R],
+                                                  double (*s_wmax)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[r][c] = X[r] + q[r][c];
+    if constexpr (std::is_same<Acc, double>::value) {
+        const int tid = threadIdx.x;
+        const int wave = tid >> 6;
+        const int lane = tid & 63;
+        double ex[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            double x = q[r][3];                       // values are >= 0: 0 is the max identity
+            x = fmax(x, dpp<kRowShr1, 0xF, true>(x));
+            x = fmax(x, dpp<kRowShr2, 0xF, true>(x));
+            x = fmax(x, dpp<kRowShr4, 0xF, true>(x));
+            x = fmax(x, dpp<kRowShr8, 0xF, true>(x));
+            x = fmax(x, dpp<kRowBcast15, 0xA, false>(x));
+            x = fmax(x, dpp<kRowBcast31, 0xC, false>(x));
+            ex[r] = wave_shr1(x);
+            const double wm = readlane(x, kWave - 1);
+            if (lane == 0) s_wmax[wave][r] = wm;
         }
-        return x;
+        __syncthreads();
+        double carry = 0.0;                          // max over earlier rows
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            double p = carry, rm = carry;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const double t = s_wmax[w2][r];
+                if (w2 < wave) p = fmax(p, t);
+                rm = fmax(rm, t);
+            }
+            const double pm = fmax(p, ex[r]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) q[r][c] = fmax(q[r][c], pm);
+            carry = rm;
+        }
     }
-};
+}
+
+// One CDF value from a local value x (see tile_local_values): excl + x, in
+// fp mode clamped to excl_{j+1}; the tile's last valid element is
+// excl_{j+1} itself, so in the last tile C_{n-1} = T is the Outer tree over
+// all group totals.
+template <class Acc>
+__device__ __forceinline__ Acc tile_value(Acc x, Acc excl, Acc next, bool last_e) {
+    if constexpr (std::is_same<Acc, double>::value) {
+        const double y = fmin(excl + x, next);
+        return last_e ? next : y;
+    } else {
+        return excl + x;
+    }
+}
 
 }  // namespace psamp

@@ -49,7 +49,10 @@ def test_status_strings_and_version(L):
 
 def test_workspace_sizes(L):
     assert L.psamp_build_cdf_workspace_size(0) == 0
-    assert L.psamp_build_cdf_workspace_size(1) == 256 + 64
+    # 256-byte header + 4 KiB per 64 tiles of 1024 elements
+    assert L.psamp_build_cdf_workspace_size(1) == 256 + 4096
+    assert L.psamp_build_cdf_workspace_size(64 * 1024) == 256 + 4096
+    assert L.psamp_build_cdf_workspace_size(64 * 1024 + 1) == 256 + 2 * 4096
     assert L.psamp_build_cdf_workspace_size(1 << 24) == 256 + 64 * (1 << 14)
     assert L.psamp_per_round_workspace_size(262144, 8192) == 256 + 64 * 256
     assert L.psamp_per_round_workspace_size(1 << 20, 1 << 20) == 256 + 64 * 1024 + 256 + 4 * 256

@@ -271,7 +271,8 @@ def _separate_round(ps, p, U, newp, alpha, beta):
 
 @pytest.mark.parametrize("n,k", [(1, 1), (1000, 7), (1024, 1024), (5000, 300), (8192, 1024),
                                  (262144, 8192), (262147, 8191), (100000, 100000),
-                                 (1 << 20, 4096), ((1 << 22) + 5, 1 << 16)])
+                                 (1 << 20, 4096), (1500001, 8192), (1 << 21, 20000),
+                                 ((1 << 22) + 5, 1 << 16)])
 def test_per_round_equals_separate_calls(ps, n, k):
     say(f"per_round n={n} k={k}")
     p = si.generic_f32(n, n + 13, "exp")
