@@ -178,26 +178,16 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
         if (lane == 0) s_range[0] = (tile == 0) ? 0 : r;
         if (lane == 32) s_range[1] = last_tile ? k : r;
     }
-    const bool vec_out = vec_ok && tlen == TILE;
+    // the tile's CDF values, kept in q; the LDS copy serves the search, the
+    // global stores wait until the local minimum is on its way
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        double c[4];
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc)
-            c[cc] = tile_value<double>(q[r][cc], excl, excl_next, r * ROW + 4 * tid + cc == tlen - 1);
-        if (vec_out) {
-            double2* o = reinterpret_cast<double2*>(cdf + base + r * ROW + 4 * tid);
-            o[0] = make_double2(c[0], c[1]);
-            o[1] = make_double2(c[2], c[3]);
-        }
+    for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int cc = 0; cc < 4; ++cc) {
             const int e = r * ROW + 4 * tid + cc;
-            s_C[e] = c[cc];
-            if (!vec_out && e < tlen) cdf[base + e] = c[cc];
-            if (last_tile && e == tlen - 1) total[0] = c[cc];
+            q[r][cc] = tile_value<double>(q[r][cc], excl, excl_next, e == tlen - 1);
+            s_C[e] = q[r][cc];
         }
-    }
     __syncthreads();
     const int64_t i_lo = s_range[0];
     const int64_t i_hi = s_range[1];
@@ -236,10 +226,30 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     if (lane == 0) atomicMin(&s_min, mn);
     __syncthreads();
 
-    // ---- 4. publish the local minimum; rewrite the last draw of each index
-    // (draws of one index are adjacent and all in this tile, and only this
-    // tile reads that part of the priority array) while the others arrive
+    // ---- 4. publish the local minimum; while the others arrive, store the
+    // CDF and rewrite the last draw of each index (draws of one index are
+    // adjacent and all in this tile, and only this tile reads that part of
+    // the priority array)
     if (tid == 0) store_agent(&ws[min_off((uint32_t)tile, par)], (uint64_t)s_min + 1);
+    const bool vec_out = vec_ok && tlen == TILE;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const int e0 = r * ROW + 4 * tid;
+        if (vec_out) {
+            double2* o = reinterpret_cast<double2*>(cdf + base + e0);
+            o[0] = make_double2(q[r][0], q[r][1]);
+            o[1] = make_double2(q[r][2], q[r][3]);
+        } else {
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                if (e0 + cc < tlen) cdf[base + e0 + cc] = q[r][cc];
+        }
+        if (last_tile) {
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc)
+                if (e0 + cc == tlen - 1) total[0] = q[r][cc];
+        }
+    }
     if (newp != nullptr) {
         if (one_pass) {
             if (i1 < i_hi) {
