@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--eager", action="store_true",
+                    help="launch every kernel from Python instead of replaying a HIP graph")
     ap.add_argument("--only", default="", help="profiling helper: scan:<n> | copy:<MiB>")
     return ap.parse_args()
 
@@ -106,11 +108,11 @@ class PerMid:
 
 
 KERNEL_NAMES = {
-    "build_cdf": "k_build_cdf<4, float, double>",
+    "build_cdf": "k_build_cdf<4, true, float, double>",
     "sample": "k_sample_fp<double>",
     "is_weights": "k_isw_single<float>",
     "scatter_lww": "k_scatter_grouped",
-    "per_round": "k_per_round<1>",
+    "per_round": "k_per_round<1, true, true>",
 }
 
 
@@ -135,6 +137,21 @@ def profiled_traffic(name):
         return int(kv["traffic_bytes_per_launch"])
     except (KeyError, OSError, ValueError):
         return None
+
+
+def capture(torch, fn):
+    """fn's launches as a HIP graph (captured on a side stream after one
+    eager run there, as torch requires)."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()
+    torch.cuda.current_stream().wait_stream(s)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    torch.cuda.synchronize()
+    return g
 
 
 def timed_steps(torch, fn, steps):
@@ -331,13 +348,22 @@ def main():
     for _ in range(args.warmup):
         work.step_fused()
         work.step()
-    gpu_s, wall_s = timed_steps(torch, work.step_fused, args.steps)
+    # A step is 32 launches, each a few microseconds of GPU work: issued one
+    # by one from Python the host cannot keep up, so the step is captured
+    # once as a HIP graph and replayed (the kernels keep their state on the
+    # device, so every replay is a fresh step).  The eager rate is reported
+    # next to it.
+    fused = capture(torch, work.step_fused) if not args.eager else work.step_fused
+    gpu_s, wall_s = timed_steps(torch, fused if args.eager else fused.replay, args.steps)
     ms_per_step = 1e3 * gpu_s / args.steps
     draws = work.rounds * work.k * args.steps
     value = draws / gpu_s
-    log(f"PER mid (fused update): {ms_per_step:.3f} ms/step, {value:.4g} indices/s "
-        f"(wall {wall_s:.3f} s)")
-    sep_s, _ = timed_steps(torch, work.step, args.steps)
+    log(f"PER mid (fused update{'' if args.eager else ', graph'}): {ms_per_step:.3f} ms/step, "
+        f"{value:.4g} indices/s (wall {wall_s:.3f} s)")
+    eager_s, _ = timed_steps(torch, work.step_fused, args.steps)
+    log(f"PER mid (fused update, eager launches): {1e3 * eager_s / args.steps:.3f} ms/step")
+    sep = capture(torch, work.step) if not args.eager else work.step
+    sep_s, _ = timed_steps(torch, work.step if args.eager else sep.replay, args.steps)
     log(f"PER mid (four separate calls): {1e3 * sep_s / args.steps:.3f} ms/step, "
         f"{draws / sep_s:.4g} indices/s")
 
@@ -356,7 +382,10 @@ def main():
                 "avg_launch_us": round(avg_us, 3), "launches_timed": launches}
     log(f"k_per_round: {avg_us:.2f} us/launch, {achieved:.0f} GB/s algorithmic, traffic {traffic}")
 
-    extra = {"separate_calls": {"ms_per_step": round(1e3 * sep_s / args.steps, 4),
+    extra = {"launch": "eager" if args.eager else "hip graph of one step",
+             "fused_eager": {"ms_per_step": round(1e3 * eager_s / args.steps, 4),
+                             "indices_per_s": round(draws / eager_s, 1)},
+             "separate_calls": {"ms_per_step": round(1e3 * sep_s / args.steps, 4),
                                 "indices_per_s": round(draws / sep_s, 1)}}
     if not args.no_extra:
         extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])

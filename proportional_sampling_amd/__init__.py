@@ -81,8 +81,10 @@ def _check(fn: str, code: int):
 
 
 def _stream(stream=None) -> int:
+    """The hipStream_t to launch on: the given stream, else torch's current
+    stream (read without building a Stream object: calls are launch-bound)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return torch._C._cuda_getCurrentRawStream(torch.cuda.current_device())
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 

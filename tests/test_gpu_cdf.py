@@ -312,3 +312,53 @@ def test_per_round_chain_vs_oracle(ps):
         p_o = oracle.scatter_lww(p_o, idx_o, d["v"][r])
         assert np.array_equal(host(Pd), p_o)
     assert ws.errors() == 0
+
+
+def test_per_round_graph_replays(ps):
+    """The fused update captured in a HIP graph (as bench.py runs it): every
+    replay, with eager work and synchronisations in between, gives the same
+    bits as the same updates launched one by one."""
+    d = si.per_mid()
+    rounds = 4
+    n, k = d["p0"].size, d["U"].shape[1]
+    a, b = d["alpha"], d["beta"]
+    U = [dev(d["U"][r]) for r in range(rounds)]
+    V = [dev(d["v"][r]) for r in range(rounds)]
+    p_g, p_e = dev(d["p0"]), dev(d["p0"])
+    ws_g = ps.Workspace(ps.per_round_workspace_size(n, k))
+    ws_e = ps.Workspace(ps.per_round_workspace_size(n, k))
+    out_g = [(torch.empty(k, dtype=torch.int32, device="cuda"),
+              torch.empty(k, dtype=torch.float32, device="cuda")) for _ in range(rounds)]
+    cdf_g = torch.empty(n, dtype=torch.float64, device="cuda")
+    tot_g = torch.empty(1, dtype=torch.float64, device="cuda")
+
+    def graph_rounds():
+        for r in range(rounds):
+            ps.per_round(p_g, U[r], a, b, V[r], out_idx=out_g[r][0], out_w=out_g[r][1],
+                         cdf=cdf_g, total=tot_g, ws=ws_g)
+
+    def check(tag):
+        for r in range(rounds):
+            idx, w, cdf, tot = ps.per_round(p_e, U[r], a, b, V[r], ws=ws_e)
+            assert torch.equal(out_g[r][0], idx), f"{tag} round {r}: indices"
+            assert torch.equal(out_g[r][1], w), f"{tag} round {r}: weights"
+        assert torch.equal(cdf_g, cdf) and torch.equal(tot_g, tot), f"{tag}: cdf"
+        assert torch.equal(p_g, p_e), f"{tag}: priorities"
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        graph_rounds()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    check("warm-up")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        graph_rounds()
+    for rep in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        check(f"replay {rep}")
+        x = torch.randn(1 << 16, device="cuda").sum().item()   # eager work in between
+        assert x == x
+    assert ws_g.errors() == 0 and ws_e.errors() == 0
