@@ -197,6 +197,40 @@ def test_resample_shapes(ps, rows, P):
     _row_check(d["lw"], d["u_row"], anc, f"resample {rows}x{P}")
 
 
+def test_resample_edges(ps):
+    """Rows whose CDF is exact (zero-weight particles, one or two carrying
+    all the mass) and extreme offsets: every ancestor equals the oracle's,
+    including particles with hundreds or thousands of offspring and the k
+    whose threshold is 0."""
+    ninf = np.float32(-np.inf)
+    for P in (4096, 3000):
+        lw = np.full((6, P), ninf, np.float32)
+        lw[0, 123] = 0.0                       # one particle takes every k
+        lw[1, 10] = 0.0
+        lw[1, P - 96] = 0.0                    # two halves
+        lw[2, :] = 0.0                         # uniform, u = 0: t_0 = 0
+        lw[3, :] = 0.0                         # uniform, u just below 1
+        lw[4, 0] = 0.0                         # all mass on the first particle
+        lw[5, P - 1] = 0.0                     # all mass on the last particle
+        u = np.array([0.5, 0.25, 0.0, np.nextafter(np.float32(1), np.float32(0)), 0.75, 0.1],
+                     np.float32)
+        anc = host(ps.resample_rows(dev(lw), dev(u)))
+        anc_o = oracle.resample_rows(lw, u)
+        # rows whose CDF is exact in binary: 0, 1, 4, 5 always; the uniform
+        # rows only when 1/P is (P a power of two) -- otherwise every
+        # threshold sits within rounding of a CDF boundary, and the excuse
+        # rule applies
+        exact = [0, 1, 4, 5] + ([2, 3] if P & (P - 1) == 0 else [])
+        assert np.array_equal(anc[exact], anc_o[exact]), f"P={P}"
+        from parity_util import excuse_counts
+        for b in (2, 3):
+            _, Cc = oracle.row_cdf(lw[b])
+            uk = ((np.arange(P, dtype=np.float32) + u[b]) / np.float32(P)).astype(np.float64)
+            unexc, _ = excuse_counts(anc[b], anc_o[b], uk, Cc, 1.0)
+            assert unexc == 0, f"P={P} row {b}"
+        assert np.all(anc[0] == 123) and np.all(anc[4] == 0) and np.all(anc[5] == P - 1)
+
+
 def test_resample_uniform_identity(ps):
     P = 4096
     lw = np.zeros((8, P), np.float32)
