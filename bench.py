@@ -281,6 +281,8 @@ def per_large_bench(ps, torch, reps=10):
     calls = {
         "build_cdf": lambda: ps.build_cdf(p, d["alpha"], cdf=cdf, total=tot, ws=ws),
         "sample": lambda: ps.sample(cdf, tot, U, out=idx),
+        "build_cdf_sample_fused": lambda: ps.build_cdf_sample(p, U, d["alpha"], cdf=cdf, total=tot,
+                                                              out=idx, ws=ws),
         "is_weights": lambda: ps.is_weights(p, idx, d["alpha"], d["beta"], out=w, ws=iws),
         "tree_build": lambda: ps.segtree_build(tree, p, d["alpha"]),
         "tree_sample": lambda: ps.segtree_sample(tree, p.numel(), U, stratified=True, out=idx),

@@ -114,6 +114,26 @@ psamp_status psamp_sample(const void* cdf, psamp_dtype cdf_t, int64_t n,
                           int64_t k, int stratified, int32_t* out_idx, void* stream);
 
 /* ------------------------------------------------------------------------
+ * (2c) Fused CDF scan + stratified sample: psamp_build_cdf followed by
+ * psamp_sample(stratified = 1), with the same CDF, T and indices bit for bit,
+ * in two passes that never read the CDF back: a pass of tile sums gives
+ * every tile its prefix and T up front, and each tile of the scan then draws
+ * its own samples (stratified thresholds are non-decreasing, and tile j owns
+ * exactly those in (C at the end of tile j-1, C at its own end]).
+ * [PR615] "1. Parallel build_cdf" with [PF] searchsorted.
+ *   Arguments as psamp_build_cdf and psamp_sample; ws as psamp_build_cdf
+ *   (the same workspace may serve both).  cdf_t PSAMP_F64 or PSAMP_U64 is
+ *   fused; PSAMP_F32 (whose rounding breaks the tiles' ownership of the
+ *   thresholds) and k = 0 run the two calls.
+ * Errors: those of psamp_build_cdf and psamp_sample.
+ * ---------------------------------------------------------------------- */
+psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_t n,
+                                    double alpha, const void* u, psamp_dtype u_t, int64_t k,
+                                    void* cdf, psamp_dtype cdf_t, void* total,
+                                    int32_t* out_idx, void* ws, size_t ws_bytes,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------
  * (2b) Importance-sampling weights.  [PER]: P_i = w_{idx_i} / T,
  * v_i = (N P_i)^-beta, IS_i = v_i / max_j v_j over the k sampled entries.
  * N and T cancel, so the kernel evaluates the equal closed form

@@ -40,6 +40,8 @@ SIGNATURES = {
     "psamp_build_cdf_workspace_size": (_sz, [_i64]),
     "psamp_build_cdf": (_int, [_p, _int, _i64, _dbl, _p, _int, _p, _p, _sz, _p]),
     "psamp_sample": (_int, [_p, _int, _i64, _p, _p, _int, _i64, _int, _p, _p]),
+    "psamp_build_cdf_sample": (_int, [_p, _int, _i64, _dbl, _p, _int, _i64, _p, _int, _p, _p, _p,
+                                      _sz, _p]),
     "psamp_is_weights_workspace_size": (_sz, [_i64]),
     "psamp_is_weights": (_int, [_p, _int, _i64, _dbl, _p, _i64, _dbl, _p, _p, _sz, _p]),
     "psamp_segtree_cap_pow2": (_i64, [_i64]),
@@ -168,6 +170,32 @@ def sample(cdf: torch.Tensor, total: torch.Tensor, u: torch.Tensor, *, stratifie
         c, _DT[cdf.dtype], cdf.numel(), t, uu, _DT[u.dtype], k, int(bool(stratified)), o,
         _stream(stream)))
     return out
+
+
+def build_cdf_sample(prio: torch.Tensor, u: torch.Tensor, alpha: float = 1.0, *,
+                     cdf: torch.Tensor | None = None, total: torch.Tensor | None = None,
+                     out: torch.Tensor | None = None, cdf_dtype=None, ws: Workspace | None = None,
+                     stream=None):
+    """build_cdf followed by stratified sample, fused (same results).
+    Returns (idx, cdf, total)."""
+    n, k = prio.numel(), u.numel()
+    p = _dev(prio, "prio", (torch.float32, torch.uint32))
+    if cdf_dtype is None:
+        cdf_dtype = torch.float64 if prio.dtype == torch.float32 else torch.uint64
+    if cdf is None:
+        cdf = torch.empty(n, dtype=cdf_dtype, device=prio.device)
+    if total is None:
+        total = torch.empty(1, dtype=cdf.dtype, device=prio.device)
+    if out is None:
+        out = torch.empty(k, dtype=torch.int32, device=prio.device)
+    if ws is None:
+        ws = Workspace(build_cdf_workspace_size(n), prio.device)
+    uu = _dev(u, "u", (torch.float32, torch.uint32))
+    _check("psamp_build_cdf_sample", lib().psamp_build_cdf_sample(
+        p, _DT[prio.dtype], n, float(alpha), uu, _DT[u.dtype], k, _dev(cdf, "cdf"),
+        _DT[cdf.dtype], _dev(total, "total"), _dev(out, "out", (torch.int32,)), ws.ptr, ws.nbytes,
+        _stream(stream)))
+    return out, cdf, total
 
 
 def is_weights_workspace_size(k: int) -> int:

@@ -30,46 +30,6 @@
 
 namespace psamp {
 
-// Stratified threshold of sample i (same operations as psamp_sample).
-__device__ __forceinline__ double strat_threshold(int64_t i, float u, int64_t k, double T) {
-    const double a = (double)i + (double)u;
-    const double b = a / (double)k;
-    return b * T;
-}
-
-// First i in [0, k] with t_i > B (t_i non-decreasing in i).  Lanes 0..31
-// answer for B0, lanes 32..63 for B1, in one round trip: each half tests a
-// 32-wide window around the stratum estimate B k / T (the answer lies within
-// 2 of it); a binary search covers the case the window misses (T = 0, or
-// inputs outside the preconditions).
-__device__ __forceinline__ int64_t first_above2(double B0, double B1, double T,
-                                                const float* __restrict__ U, int64_t k) {
-    const int lane = lane_id();
-    const bool hi = lane >= 32;
-    const double B = hi ? B1 : B0;
-    int64_t est = 0;
-    if (T > 0.0) {
-        const double e = floor(B / T * (double)k);
-        est = !(e > 0.0) ? 0 : (e > (double)k ? k : (int64_t)e);
-    }
-    const int64_t c0 = est - 8;
-    const int64_t c = c0 + (lane & 31);
-    const bool above = c < 0 ? false : (c >= k ? true : strat_threshold(c, U[c], k, T) > B);
-    const uint64_t bal = __ballot(above);
-    const uint32_t m = hi ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-    if (m != 0 && ((m & 1u) == 0 || c0 <= 0)) {
-        const int64_t r = c0 + (__ffs((int)m) - 1);
-        return r < 0 ? 0 : r;
-    }
-    int64_t lo = 0, hi_i = k;
-    while (lo < hi_i) {
-        const int64_t mid = lo + ((hi_i - lo) >> 1);
-        if (strat_threshold(mid, U[mid], k, T) > B) hi_i = mid;
-        else lo = mid + 1;
-    }
-    return lo;
-}
-
 constexpr int kULds = 8192;   // k up to this: the thresholds' fractions are staged in LDS
 
 // UL: U (k <= kULds values) is copied to LDS at the start, so locating and
@@ -174,7 +134,7 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
 
     // ---- 2. this tile's samples: the thresholds in (excl, excl_next]
     if (wave == 0) {
-        const int64_t r = first_above2(excl, excl_next, T, Us, k);
+        const int64_t r = first_above2(excl, excl_next, T, StratFp{Us, k, T}, k);
         if (lane == 0) s_range[0] = (tile == 0) ? 0 : r;
         if (lane == 32) s_range[1] = last_tile ? k : r;
     }

@@ -52,12 +52,24 @@ __device__ __forceinline__ void store4<float>(float* p, const float (&o)[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(o[0], o[1], o[2], o[3]);
 }
 
+// The draws of the fused scan + stratified sample (unused otherwise).
+struct SampleArgs {
+    const void* u;        // float U_i (fp mode) or uint32 r_i (integer mode)
+    int64_t k;
+    int k_log2;           // log2 k if k is a power of two, else -1 (integer mode)
+    int32_t* out;
+};
+
 // One workgroup per tile, tiles in blockIdx order.  VEC: see load_tile.
-template <int IPT, bool VEC, class In, class Out>
+// SAMPLE: every tile sum and group total and T are already published (by
+// k_tile_sums), so the lookback does not wait; the tile then draws its own
+// stratified samples -- the thresholds in (excl_j, excl_{j+1}] -- from an
+// LDS copy of its CDF values.
+template <int IPT, bool VEC, class In, class Out, bool SAMPLE = false>
 __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     const In* __restrict__ in, int64_t n, double alpha, Out* __restrict__ cdf,
     Out* __restrict__ total, uint64_t* __restrict__ ws, int n_tiles,
-    uint64_t max_slots, int vec_ok) {
+    uint64_t max_slots, int vec_ok, SampleArgs sa) {
     using Acc = typename ScanAcc<In>::type;
     constexpr bool kFp = std::is_same<In, float>::value;
     constexpr int R = IPT / 4;                    // rows per tile
@@ -68,9 +80,13 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     __shared__ Acc s_wtot[4][R];
     __shared__ double s_wmax[4][R];
     __shared__ Acc s_excl[2];
+    __shared__ Acc s_C[SAMPLE ? TILE : 1];
+    __shared__ Acc s_T;
+    __shared__ int64_t s_range[2];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
+    const int lane = tid & 63;
     const int tile = (int)blockIdx.x;
     const int64_t base = (int64_t)tile * TILE;
     const int tlen = (int)min_<int64_t>(TILE, n - base);   // valid elements, >= 1
@@ -89,6 +105,10 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     if (kFp) mr = math_load(tid);
     const uint64_t calls_w = load_agent(&ws[kHdrCalls]);
     const uint64_t hw_w = load_agent(&ws[kHdrHw]);
+    // SAMPLE: T is already published (parity of this call); its word goes
+    // with the first loads
+    const uint64_t t0_w = SAMPLE ? load_agent(&ws[kHdrT + 0]) : 0;
+    const uint64_t t1_w = SAMPLE ? load_agent(&ws[kHdrT + 1]) : 0;
     if (kFp) math_store(&M, tid, mr);
     __syncthreads();
     const uint32_t calls = (uint32_t)calls_w;
@@ -139,8 +159,11 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
         const int e0 = r * ROW + t4;
         Out o[4];
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            o[k] = to_out<Out>(tile_value<Acc>(q[r][k], excl, next, e0 + k == tlen - 1));
+        for (int k = 0; k < 4; ++k) {
+            const Acc c = tile_value<Acc>(q[r][k], excl, next, e0 + k == tlen - 1);
+            o[k] = to_out<Out>(c);
+            if constexpr (SAMPLE) s_C[e0 + k] = c;
+        }
         if (full) {
             store4<Out>(tout + e0, o);
         } else {
@@ -155,6 +178,151 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
                 if (e0 + k == tlen - 1) total[0] = o[k];
         }
     }
+
+    if constexpr (SAMPLE) {
+        // this tile's draws: [first t_i > excl_j, first t_i > excl_{j+1})
+        if (wave == 0) {
+            uint64_t tw = readlane(par ? t1_w : t0_w, 0);   // normally already present
+            const uint32_t off[1] = {(uint32_t)(kHdrT + par)};
+            const bool need[1] = {lane == 0 && tw == 0};
+            uint64_t w[1];
+            wait_words<1>(ws, off, need, w);
+            if (tw == 0) tw = readlane(w[0], 0);
+            Acc T;
+            status_dec(tw, T);
+            int64_t rr;
+            if constexpr (kFp)
+                rr = first_above2(excl, next, T, StratFp{(const float*)sa.u, sa.k, T}, sa.k);
+            else
+                rr = first_above2(excl, next, T,
+                                  StratInt{(const uint32_t*)sa.u, sa.k, T, sa.k_log2}, sa.k);
+            if (lane == 0) {
+                s_range[0] = tile == 0 ? 0 : rr;
+                s_T = T;
+            }
+            if (lane == 32) s_range[1] = tile == n_tiles - 1 ? sa.k : rr;
+        }
+        __syncthreads();
+        const int64_t i_lo = s_range[0], i_hi = s_range[1];
+        const Acc T = s_T;
+        for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
+            Acc t;
+            if constexpr (kFp)
+                t = strat_threshold(i, ((const float*)sa.u)[i], sa.k, T);
+            else
+                t = int_threshold((uint64_t)i, ((const uint32_t*)sa.u)[i], (uint64_t)sa.k, T, 1,
+                                  sa.k_log2);
+            int b = 0, len = tlen;
+            while (len > 1) {
+                const int half = len >> 1;
+                b = (s_C[b + half - 1] < t) ? b + half : b;
+                len -= half;
+            }
+            b += (s_C[b] < t) ? 1 : 0;
+            if (b >= tlen) b = tlen - 1;
+            sa.out[i] = (int32_t)(base + b);
+        }
+    }
+}
+
+// The first pass of the fused scan + sample: the tile sums A_j (the same
+// arithmetic as the scan's), published in the scan's status words.  Tiles
+// count per group of 64 (the group's MIN words of this parity serve as the
+// counters; the next call zeroes them): the tile that completes a group
+// publishes its total GT_g, and the group that completes last forms T with
+// the scan's association and publishes it.  One counter per group keeps the
+// atomics on 64-tile-wide addresses apart instead of serialising all tiles
+// on one word.
+template <int IPT, bool VEC, class In>
+__global__ __launch_bounds__(kScanThreads) void k_tile_sums(const In* __restrict__ in, int64_t n,
+                                                            double alpha,
+                                                            uint64_t* __restrict__ ws,
+                                                            int n_tiles) {
+    using Acc = typename ScanAcc<In>::type;
+    constexpr bool kFp = std::is_same<In, float>::value;
+    constexpr int R = IPT / 4;
+    constexpr int TILE = kScanThreads * 4 * R;
+
+    __shared__ MathLds M;
+    __shared__ Acc s_wtot[4][R];
+    __shared__ int s_role;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const int tile = (int)blockIdx.x;
+    const int g = tile / kScanGroup;
+    const int G = (n_tiles + kScanGroup - 1) / kScanGroup;
+    const int64_t base = (int64_t)tile * TILE;
+    const int tlen = (int)min_<int64_t>(TILE, n - base);
+
+    In v[R][4];
+    load_tile<R, VEC, In>(in + base, tlen, v);
+    asm volatile("" ::: "memory");
+    MathRegs mr;
+    if (kFp) mr = math_load(tid);
+    const uint64_t calls_w = load_agent(&ws[kHdrCalls]);
+    if (kFp) math_store(&M, tid, mr);
+    __syncthreads();
+    const int par = (int)(calls_w & 1u);
+
+    Acc q[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const Acc w = to_weight(v[r][c], alpha, &M);
+            q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
+        }
+        if constexpr (kFp) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) asm volatile("" : "+v"(q[r][c]));
+        }
+    }
+    Acc X[R];
+    Acc A;
+    tile_scan_256<R, Acc>(q, X, A, s_wtot);
+    if (tid == 0) {
+        store_agent(&ws[a_off((uint32_t)tile, par)], status_enc(A));
+        const uint64_t in_group = (uint64_t)min_(kScanGroup, n_tiles - g * kScanGroup);
+        s_role = fetch_add_agent(&ws[min_off((uint32_t)(g * kScanGroup), par)], 1) ==
+                 in_group - 1;
+    }
+    __syncthreads();
+    if (!s_role || wave != 0) return;
+
+    // the tile that completes group g: GT_g = the DPP tree over its sums
+    {
+        const int t = g * kScanGroup + lane;
+        const uint32_t off[1] = {a_off((uint32_t)(t < n_tiles ? t : 0), par)};
+        const bool need[1] = {t < n_tiles};
+        uint64_t w[1];
+        wait_words<1>(ws, off, need, w);
+        const Acc gt = wave_sum(need[0] ? status_value<Acc>(w[0]) : Acc(0));
+        int last = 0;
+        if (lane == 0) {
+            store_agent(&ws[gt_off((uint32_t)g, par)], status_enc(gt));
+            last = fetch_add_agent(&ws[kHdrExit], 1) == (uint64_t)G - 1;
+        }
+        if (!__builtin_amdgcn_readfirstlane(last)) return;
+    }
+    // the group that completes last: T = Outer(GT_0, ..., GT_{G-1}) (lane h
+    // mod 64 adds its leaves in increasing h, then the tree) -- the value the
+    // scan's last tile forms as C_{n-1}
+    Acc acc = Acc(0);
+    for (int s0 = 0; s0 * kWave < G; ++s0) {
+        const int h = s0 * kWave + lane;
+        const uint32_t off[1] = {gt_off((uint32_t)(h < G ? h : 0), par)};
+        const bool need[1] = {h < G};
+        uint64_t w[1];
+        wait_words<1>(ws, off, need, w);
+        if (need[0]) acc = acc + status_value<Acc>(w[0]);
+    }
+    const Acc T = wave_sum(acc);
+    if (lane == 0) {
+        store_agent(&ws[kHdrT + par], status_enc(T));
+        store_agent(&ws[kHdrExit], 0);
+    }
 }
 
 template <int IPT, class In, class Out>
@@ -166,11 +334,11 @@ static psamp_status launch_scan(const void* prio, int64_t n, double alpha, void*
     if (vec_in)
         hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Out>), dim3(tiles), dim3(kScanThreads), 0,
                            st, (const In*)prio, n, alpha, (Out*)cdf, (Out*)total, (uint64_t*)ws,
-                           tiles, max_slots, vec_ok);
+                           tiles, max_slots, vec_ok, SampleArgs{});
     else
         hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Out>), dim3(tiles), dim3(kScanThreads), 0,
                            st, (const In*)prio, n, alpha, (Out*)cdf, (Out*)total, (uint64_t*)ws,
-                           tiles, max_slots, vec_ok);
+                           tiles, max_slots, vec_ok, SampleArgs{});
     return launch_status();
 }
 
@@ -182,6 +350,32 @@ static psamp_status launch_build_cdf(const void* prio, int64_t n, double alpha, 
     if (scan_rows_for(n) == 1)
         return launch_scan<4, In, Out>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, st);
     return launch_scan<32, In, Out>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, st);
+}
+
+// The fused scan + stratified sample: k_tile_sums, then the scan with
+// SAMPLE.  CDF, T and indices are the bits of psamp_build_cdf + psamp_sample.
+template <int IPT, class In>
+static psamp_status launch_scan_sample(const void* prio, int64_t n, double alpha, void* cdf,
+                                       void* total, void* ws, uint64_t max_slots, int vec_ok,
+                                       SampleArgs sa, hipStream_t st) {
+    using Acc = typename ScanAcc<In>::type;
+    const int tiles = (int)ceil_div(n, kScanThreads * IPT);
+    if (trace_enabled()) trace_launch("k_tile_sums+k_build_cdf<sample>", tiles, kScanThreads, n);
+    const bool vec_in = aligned(prio, 16) && n % 4 == 0;
+    if (vec_in) {
+        hipLaunchKernelGGL((k_tile_sums<IPT, true, In>), dim3(tiles), dim3(kScanThreads), 0, st,
+                           (const In*)prio, n, alpha, (uint64_t*)ws, tiles);
+        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Acc, true>), dim3(tiles),
+                           dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Acc*)cdf,
+                           (Acc*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, sa);
+    } else {
+        hipLaunchKernelGGL((k_tile_sums<IPT, false, In>), dim3(tiles), dim3(kScanThreads), 0, st,
+                           (const In*)prio, n, alpha, (uint64_t*)ws, tiles);
+        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Acc, true>), dim3(tiles),
+                           dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Acc*)cdf,
+                           (Acc*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, sa);
+    }
+    return launch_status();
 }
 
 }  // namespace psamp
@@ -212,4 +406,49 @@ extern "C" psamp_status psamp_build_cdf(const void* prio, psamp_dtype prio_t, in
     if (cdf_t == PSAMP_F64)
         return launch_build_cdf<float, double>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
     return launch_build_cdf<float, float>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
+}
+
+extern "C" psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_t n,
+                                               double alpha, const void* u, psamp_dtype u_t,
+                                               int64_t k, void* cdf, psamp_dtype cdf_t,
+                                               void* total, int32_t* out_idx, void* ws,
+                                               size_t ws_bytes, void* stream) {
+    if (!prio || !cdf || !total) return PSAMP_E_NULL;
+    if (n < 1 || n > kMaxN || k < 0 || k > kMaxN) return PSAMP_E_SIZE;
+    const bool fp = prio_t == PSAMP_F32 && u_t == PSAMP_F32 &&
+                    (cdf_t == PSAMP_F64 || cdf_t == PSAMP_F32);
+    const bool in = prio_t == PSAMP_U32 && u_t == PSAMP_U32 && cdf_t == PSAMP_U64;
+    if (!fp && !in) return PSAMP_E_DTYPE;
+    if (fp && !(finite_d(alpha) && alpha > 0.0)) return PSAMP_E_PARAM;
+    if (k > 0 && (!u || !out_idx)) return PSAMP_E_NULL;
+    if (!ws) return PSAMP_E_WORKSPACE;
+    if (ws_bytes < psamp_build_cdf_workspace_size(n)) return PSAMP_E_WORKSPACE;
+    const size_t osz = cdf_t == PSAMP_F32 ? 4 : 8;
+    if (!aligned(prio, 4) || !aligned(cdf, osz) || !aligned(total, osz) || !aligned(ws, 8) ||
+        (k > 0 && (!aligned(u, 4) || !aligned(out_idx, 4))))
+        return PSAMP_E_ALIGN;
+    if (k == 0 || cdf_t == PSAMP_F32) {
+        // nothing to draw, or a float CDF (whose rounding breaks the tiles'
+        // ownership of the thresholds): the two calls, same results
+        psamp_status s = psamp_build_cdf(prio, prio_t, n, alpha, cdf, cdf_t, total, ws, ws_bytes,
+                                         stream);
+        if (s != PSAMP_OK || k == 0) return s;
+        return psamp_sample(cdf, cdf_t, n, total, u, u_t, k, 1, out_idx, stream);
+    }
+    hipStream_t st = as_stream(stream);
+    const uint64_t max_slots = ws_tile_capacity(ws_bytes);
+    const int vec_ok = aligned(cdf, 16);
+    const SampleArgs sa{u, k, is_pow2(k) ? ilog2_exact(k) : -1, out_idx};
+    if (in) {
+        if (scan_rows_for(n) == 1)
+            return launch_scan_sample<4, uint32_t>(prio, n, 0.0, cdf, total, ws, max_slots, vec_ok,
+                                                   sa, st);
+        return launch_scan_sample<32, uint32_t>(prio, n, 0.0, cdf, total, ws, max_slots, vec_ok,
+                                                sa, st);
+    }
+    if (scan_rows_for(n) == 1)
+        return launch_scan_sample<4, float>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, sa,
+                                            st);
+    return launch_scan_sample<32, float>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, sa,
+                                         st);
 }

@@ -54,7 +54,7 @@ constexpr int kSpinLimit = 1 << 21;    // bounded waits (about a second)
 constexpr int kLbGtWords = 2;          // group totals per lane per round trip (lookback)
 constexpr int kAllWords = 4;           // tile sums per lane per round trip (lookback_all)
 
-enum : int { kHdrCalls = 0, kHdrHw = 1, kHdrErr = 2, kHdrT = 4, kHdrDummy = 8 };
+enum : int { kHdrCalls = 0, kHdrHw = 1, kHdrErr = 2, kHdrT = 4, kHdrDummy = 8, kHdrExit = 16 };
 
 // Rows of 1024 elements per tile.  The tiling fixes the association of the
 // fp sums, so the scan and the fused update both take it from here.
@@ -389,6 +389,67 @@ __device__ __forceinline__ Acc tile_value(Acc x, Acc excl, Acc next, bool last_e
     } else {
         return excl + x;
     }
+}
+
+// ------------------------------------------- stratified draws of a tile
+// Stratified threshold of draw i (the same operations as psamp_sample).
+__device__ __forceinline__ double strat_threshold(int64_t i, float u, int64_t k, double T) {
+    const double a = (double)i + (double)u;
+    const double b = a / (double)k;
+    return b * T;
+}
+
+// t_i for fp and integer mode (integer: the exact map onto [1, T]).
+struct StratFp {
+    const float* U;
+    int64_t k;
+    double T;
+    __device__ __forceinline__ double operator()(int64_t i) const {
+        return strat_threshold(i, U[i], k, T);
+    }
+};
+struct StratInt {
+    const uint32_t* r;
+    int64_t k;
+    uint64_t T;
+    int k_log2;
+    __device__ __forceinline__ uint64_t operator()(int64_t i) const {
+        return int_threshold((uint64_t)i, r[i], (uint64_t)k, T, 1, k_log2);
+    }
+};
+
+// First i in [0, k] with t_i > B (t_i non-decreasing in i).  Lanes 0..31
+// answer for B0, lanes 32..63 for B1, in one round trip: each half tests a
+// 32-wide window around the stratum estimate B k / T (the answer lies within
+// 2 of it); a binary search covers the case the window misses (T = 0, or
+// inputs outside the preconditions).  With the exactly monotone CDF, tile j
+// owns the draws [first_above(excl_j), first_above(excl_{j+1})).
+template <class Thr, class V>
+__device__ __forceinline__ int64_t first_above2(V B0, V B1, V T, const Thr& thr, int64_t k) {
+    const int lane = lane_id();
+    const bool hi = lane >= 32;
+    const V B = hi ? B1 : B0;
+    int64_t est = 0;
+    if (T > V(0)) {
+        const double e = floor((double)B / (double)T * (double)k);
+        est = !(e > 0.0) ? 0 : (e > (double)k ? k : (int64_t)e);
+    }
+    const int64_t c0 = est - 8;
+    const int64_t c = c0 + (lane & 31);
+    const bool above = c < 0 ? false : (c >= k ? true : thr(c) > B);
+    const uint64_t bal = __ballot(above);
+    const uint32_t m = hi ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+    if (m != 0 && ((m & 1u) == 0 || c0 <= 0)) {
+        const int64_t r = c0 + (__ffs((int)m) - 1);
+        return r < 0 ? 0 : r;
+    }
+    int64_t lo = 0, hi_i = k;
+    while (lo < hi_i) {
+        const int64_t mid = lo + ((hi_i - lo) >> 1);
+        if (thr(mid) > B) hi_i = mid;
+        else lo = mid + 1;
+    }
+    return lo;
 }
 
 }  // namespace psamp

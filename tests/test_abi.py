@@ -98,6 +98,27 @@ def test_sample_validation(L):
     assert f(FAKE, F64, 10, None, FAKE, F32, 10, 1, FAKE, None) == E_NULL
 
 
+def test_build_cdf_sample_validation(L):
+    ws = L.psamp_build_cdf_workspace_size(1000)
+    f = L.psamp_build_cdf_sample
+    #       prio  pt   n     alpha u     ut   k   cdf   ct   total idx   ws    bytes
+    assert f(None, F32, 1000, 0.6, FAKE, F32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws, None) == E_NULL
+    assert f(FAKE, F32, 0, 0.6, FAKE, F32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws, None) == E_SIZE
+    assert f(FAKE, F32, 1000, 0.6, FAKE, F32, -1, FAKE, F64, FAKE, FAKE, FAKE, ws, None) == E_SIZE
+    assert f(FAKE, F32, 1000, 0.6, FAKE, U32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws, None) == E_DTYPE
+    assert f(FAKE, U32, 1000, 0.6, FAKE, U32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws, None) == E_DTYPE
+    assert f(FAKE, F32, 1000, 0.0, FAKE, F32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws, None) == E_PARAM
+    assert f(FAKE, F32, 1000, 0.6, None, F32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws, None) == E_NULL
+    assert f(FAKE, F32, 1000, 0.6, FAKE, F32, 10, FAKE, F64, FAKE, None, FAKE, ws, None) == E_NULL
+    assert f(FAKE, F32, 1000, 0.6, FAKE, F32, 10, FAKE, F64, FAKE, FAKE, None, ws, None) == E_WS
+    assert f(FAKE, F32, 1000, 0.6, FAKE, F32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws - 8,
+             None) == E_WS
+    assert f(FAKE, F32, 1000, 0.6, FAKE + 2, F32, 10, FAKE, F64, FAKE, FAKE, FAKE, ws,
+             None) == E_ALIGN
+    assert f(FAKE, F32, 1000, 0.6, FAKE, F32, 10, FAKE, F64, FAKE, FAKE + 2, FAKE, ws,
+             None) == E_ALIGN
+
+
 def test_is_weights_validation(L):
     f = L.psamp_is_weights
     assert f(FAKE, F64, 10, 0.6, FAKE, 5, 0.4, FAKE, None, 0, None) == E_DTYPE

@@ -362,3 +362,55 @@ def test_per_round_graph_replays(ps):
         x = torch.randn(1 << 16, device="cuda").sum().item()   # eager work in between
         assert x == x
     assert ws_g.errors() == 0 and ws_e.errors() == 0
+
+
+# ------------------------------------------------- fused scan + sample
+@pytest.mark.parametrize("n,k", [(1, 1), (1000, 7), (8192, 1024), (262144, 8192), (262147, 8191),
+                                 (1 << 20, 4096), ((1 << 20) + 12, 1 << 16),
+                                 ((1 << 22) + 5, 1 << 16), (1 << 22, 1 << 22), (5000, 20000)])
+@pytest.mark.parametrize("mode", ["fp", "int"])
+def test_build_cdf_sample_equals_separate(ps, n, k, mode):
+    """psamp_build_cdf_sample gives the bits of psamp_build_cdf followed by
+    psamp_sample(stratified), on both tilings, ragged sizes and k > n; three
+    calls in a row on one workspace (its parities alternate)."""
+    say(f"build_cdf_sample {mode} n={n} k={k}")
+    ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+    ws2 = ps.Workspace(ps.build_cdf_workspace_size(n))
+    for rep in range(3):
+        rng = np.random.default_rng(n + 7 * k + rep)
+        if mode == "fp":
+            p = si.generic_f32(n, n + rep, "lognormal")
+            p[::13] = 0.0
+            p[0] = max(p[0], np.float32(1e-3))
+            u = si.uniform_f32(rng, k)
+            alpha = 0.7
+        else:
+            p = rng.integers(0, 1 << 20, n, dtype=np.uint32)
+            p[0] = 1
+            u = si.uniform_u32(rng, k)
+            alpha = 1.0
+        P, Ud = dev(p), dev(u)
+        idx, cdf, tot = ps.build_cdf_sample(P, Ud, alpha, ws=ws)
+        c_s, t_s = ps.build_cdf(P, alpha, ws=ws2)
+        i_s = ps.sample(c_s, t_s, Ud, stratified=True)
+        assert torch.equal(cdf, c_s), f"rep {rep}: cdf"
+        assert torch.equal(tot, t_s), f"rep {rep}: total"
+        assert torch.equal(idx, i_s), f"rep {rep}: indices"
+    assert ws.errors() == 0
+
+
+def test_build_cdf_sample_per_large(ps):
+    """PER large (2^24 priorities, 2^20 stratified draws), fp and integer:
+    the fused call equals the two calls, and its integer indices equal the
+    oracle's."""
+    d = si.per_large()
+    P, Ud = dev(d["p"]), dev(d["U"])
+    idx, cdf, tot = ps.build_cdf_sample(P, Ud, d["alpha"])
+    c_s, t_s = ps.build_cdf(P, d["alpha"])
+    assert torch.equal(cdf, c_s) and torch.equal(tot, t_s)
+    assert torch.equal(idx, ps.sample(c_s, t_s, Ud, stratified=True))
+    di = si.per_large_int()
+    Q, R = dev(di["q"]), dev(di["r"])
+    idx_i, _, _ = ps.build_cdf_sample(Q, R)
+    _, _, _, idx_o = oracle.sample_int(di["q"], di["r"], True)
+    assert np.array_equal(host(idx_i), idx_o)
