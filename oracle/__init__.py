@@ -82,6 +82,8 @@ def _declare(L):
         "o_tree_root_u64": (C.c_uint64, [_p]),
         "o_resample_rows": (None, [_p, _i64, _i64, _i64, _p, _p, _i64]),
         "o_row_cdf": (None, [_p, _i64, _p, _p]),
+        "o_pf_step": (None, [_p, _p, _p, _p, _p, _p, C.c_float, C.c_float, _p, _i64, _i64,
+                             _i64, _i64, _p, _p, _p, _p, _p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -292,6 +294,30 @@ def resample_rows(lw, u_row) -> np.ndarray:
     anc = np.empty((rows, P), np.int32)
     lib().o_resample_rows(_ptr(lw), rows, P, P, _ptr(u_row), _ptr(anc), P)
     return anc
+
+
+def pf_step(x, lw, obs, A, Cm, eps, sigma_p: float, sigma_o: float, u_row):
+    """One particle-filter step ([PF]).  x, eps: (rows, P, D); lw: (rows, P);
+    obs: (rows, O); A: (D, D); Cm: (O, D); u_row: (rows,).  Returns
+    (x_out, lw_out, anc, pred, lw_new), all float32 except anc (int32)."""
+    x = _c(x, np.float32)
+    rows, P, D = x.shape
+    lw = _c(lw, np.float32).reshape(rows, P)
+    obs = _c(obs, np.float32).reshape(rows, -1)
+    O = obs.shape[1]
+    A = _c(A, np.float32).reshape(D, D)
+    Cm = _c(Cm, np.float32).reshape(O, D)
+    eps = _c(eps, np.float32).reshape(rows, P, D)
+    u_row = _c(u_row, np.float32).reshape(rows)
+    x_out = np.empty_like(x)
+    lw_out = np.empty((rows, P), np.float32)
+    anc = np.empty((rows, P), np.int32)
+    pred = np.empty_like(x)
+    lwn = np.empty((rows, P), np.float32)
+    lib().o_pf_step(_ptr(x), _ptr(lw), _ptr(obs), _ptr(A), _ptr(Cm), _ptr(eps),
+                    float(sigma_p), float(sigma_o), _ptr(u_row), rows, P, D, O,
+                    _ptr(x_out), _ptr(lw_out), _ptr(anc), _ptr(pred), _ptr(lwn))
+    return x_out, lw_out, anc, pred, lwn
 
 
 def row_cdf(x):

@@ -19,9 +19,12 @@
 //   [SEGT]   "GPU Segment Tree for PER Sampling": sections "Tree Layout",
 //            "Operations" (Update, Sample), "Memory", "Non-Goals".
 //   [PF]     POPCORNBENCH particle-filter trace (Kimi-K2.6, l2_p48): the
-//            reference model's resampling step -- weights = exp(log_w -
-//            logsumexp), cumsum, u = (arange(P) + rand(B,1)) / P,
-//            searchsorted (first index with cumsum >= u), clamp to P-1.
+//            reference model's forward pass -- predict with a linear model
+//            plus process noise, a Gaussian observation log-likelihood, the
+//            log-weight update -- and its resampling step: weights =
+//            exp(log_w - logsumexp), cumsum, u = (arange(P) + rand(B,1)) / P,
+//            searchsorted (first index with cumsum >= u), clamp to P-1,
+//            gather, log-weights reset to -log(P).
 //   [PER]    Prioritized experience replay as named in [SEGT] "Non-Goals"
 //            (alpha, beta, IS weights): P(i) = p_i^alpha / sum_j p_j^alpha,
 //            IS_i = (N * P(i))^-beta normalised by the largest weight of the
@@ -454,6 +457,63 @@ void o_resample_rows(const float* lw, int64_t rows, int64_t P, int64_t ld_in,
             while (j < P && C[(size_t)j] < (double)uk) ++j;
             anc[b * ld_out + kk] = (int32_t)(j < P ? j : P - 1);
         }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// One particle-filter step.  [PF], the reference model's forward pass, per
+// row b (one filter of P particles in D dimensions, O observed values):
+//   pred_j    = A x_j + sigma_p eps_j          (x @ A^T + sigma_p * noise)
+//   y_j       = C pred_j                         (pred @ C^T)
+//   ll_j      = -0.5 * sum_o (obs_o - y_jo)^2 / sigma_o^2
+//   lw'_j     = lw_j + ll_j
+//   anc       = systematic resampling of lw' with u_row[b]  (as above)
+//   x_out_k   = pred_{anc_k},   lw_out_k = -log(P)
+// Reading: every step up to lw' in float32 as the pages' model computes it,
+// each dot product summed in increasing index, the noise term added last,
+// ll = (-0.5 * S) / (sigma_o * sigma_o) in that order; the resampling as
+// o_resample_rows; -log(P) in double, rounded to float.  The noise eps is
+// an input (standard normal draws), like every random number here.
+// pred_out and lwn_out (pred and lw', for the pins) may be null.
+// ---------------------------------------------------------------------------
+void o_pf_step(const float* x, const float* lw, const float* obs, const float* A,
+               const float* Cm, const float* eps, float sigma_p, float sigma_o,
+               const float* u_row, int64_t rows, int64_t P, int64_t D, int64_t O,
+               float* x_out, float* lw_out, int32_t* anc_out, float* pred_out,
+               float* lwn_out) {
+    std::vector<float> pred((size_t)(P * D)), lwn((size_t)P);
+    std::vector<int32_t> anc((size_t)P);
+    const float s2 = sigma_o * sigma_o;
+    const float neg_log_p = (float)(-std::log((double)P));
+    for (int64_t b = 0; b < rows; ++b) {
+        const float* xb = x + b * P * D;
+        const float* eb = eps + b * P * D;
+        const float* ob = obs + b * O;
+        for (int64_t j = 0; j < P; ++j) {
+            for (int64_t d = 0; d < D; ++d) {
+                float acc = 0.0f;
+                for (int64_t k = 0; k < D; ++k) acc = acc + A[d * D + k] * xb[j * D + k];
+                pred[(size_t)(j * D + d)] = acc + sigma_p * eb[j * D + d];
+            }
+            float S = 0.0f;
+            for (int64_t o = 0; o < O; ++o) {
+                float y = 0.0f;
+                for (int64_t d = 0; d < D; ++d) y = y + Cm[o * D + d] * pred[(size_t)(j * D + d)];
+                const float diff = ob[o] - y;
+                S = S + diff * diff;
+            }
+            const float ll = (-0.5f * S) / s2;
+            lwn[(size_t)j] = lw[b * P + j] + ll;
+        }
+        o_resample_rows(lwn.data(), 1, P, P, u_row + b, anc.data(), P);
+        for (int64_t k = 0; k < P; ++k) {
+            const int64_t a = anc[(size_t)k];
+            for (int64_t d = 0; d < D; ++d) x_out[(b * P + k) * D + d] = pred[(size_t)(a * D + d)];
+            lw_out[b * P + k] = neg_log_p;
+            if (anc_out) anc_out[b * P + k] = (int32_t)a;
+        }
+        if (pred_out) std::memcpy(pred_out + b * P * D, pred.data(), sizeof(float) * (size_t)(P * D));
+        if (lwn_out) std::memcpy(lwn_out + b * P, lwn.data(), sizeof(float) * (size_t)P);
     }
 }
 

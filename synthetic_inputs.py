@@ -30,6 +30,8 @@ PER_MID = dict(seed=1002, n=262144, k=8192, rounds=32, alpha=0.6, beta=0.4)
 SUMTREE = dict(seed=1003, n_valid=500000, cap=1 << 19, m=1024, k=1024,
                rounds=1000, alpha=0.6)
 RESAMPLE = dict(seed=1004, rows=1024, P=4096)
+PF_STEP = dict(seed=1008, rows=1024, P=4096, D=4, O=2, sigma_p=0.1, sigma_o=0.5)
+PF_SMALL = dict(seed=1009, rows=16, P=1024, D=4, O=2, sigma_p=0.1, sigma_o=0.5)
 PER_LARGE = dict(seed=1005, n=1 << 24, k=1 << 20, alpha=0.7, beta=0.5)
 PER_LARGE_INT = dict(seed=1006, n=1 << 24, k=1 << 20, qmax=1 << 20, beta=0.5)
 SWEEP_SEED = 1007
@@ -90,6 +92,31 @@ def resample(seed: int = RESAMPLE["seed"], rows: int = RESAMPLE["rows"],
     lw = (rng.standard_normal((rows, P)) * sigma).astype(np.float32)
     u_row = uniform_f32(rng, rows)
     return dict(lw=lw, u_row=u_row)
+
+
+def pf_step(seed: int = PF_STEP["seed"], rows: int = PF_STEP["rows"], P: int = PF_STEP["P"],
+            D: int = PF_STEP["D"], O: int = PF_STEP["O"], sigma_p: float = PF_STEP["sigma_p"],
+            sigma_o: float = PF_STEP["sigma_o"]):
+    """One particle-filter step's inputs: states x ~ N(0, 1) (rows, P, D),
+    log-weights ~ N(0, 1), observations ~ N(0, 1) (rows, O), A = 0.9 I,
+    C ~ 0.5 N(0, 1) (O, D), standard normal process noise eps (rows, P, D),
+    one u_row per row; all float32."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((rows, P, D)).astype(np.float32)
+    lw = rng.standard_normal((rows, P)).astype(np.float32)
+    obs = rng.standard_normal((rows, O)).astype(np.float32)
+    A = (0.9 * np.eye(D)).astype(np.float32)
+    Cm = (0.5 * rng.standard_normal((O, D))).astype(np.float32)
+    eps = rng.standard_normal((rows, P, D)).astype(np.float32)
+    u_row = uniform_f32(rng, rows)
+    return dict(x=x, lw=lw, obs=obs, A=A, C=Cm, eps=eps, u_row=u_row, sigma_p=sigma_p,
+                sigma_o=sigma_o)
+
+
+def pf_small(seed: int = PF_SMALL["seed"]):
+    """The pages' filter shape: 16 filters of 1024 particles, D = 4, O = 2."""
+    c = PF_SMALL
+    return pf_step(seed, c["rows"], c["P"], c["D"], c["O"], c["sigma_p"], c["sigma_o"])
 
 
 def per_large(seed: int = PER_LARGE["seed"], n: int = PER_LARGE["n"],

@@ -391,3 +391,73 @@ def test_resample_offspring_counts(orc):
         W, _ = orc.row_cdf(d["lw"][b])
         cnt = np.bincount(anc[b], minlength=1024)
         assert np.all(np.abs(cnt - 1024 * W) < 1 + 1e-9)
+
+
+# ------------------------------------------------------ particle-filter step
+def _pf_golden():
+    with open(os.path.join(os.path.dirname(__file__), "golden", "pf_step_worked.json")) as f:
+        return json.load(f)
+
+
+def test_pf_step_worked_example(orc):
+    g = _pf_golden()
+    f = lambda k, dt=np.float32: np.array(g[k], dt)
+    x_out, lw_out, anc, pred, lwn = orc.pf_step(f("x"), f("lw"), f("obs"), f("A"), f("C"),
+                                               f("eps"), g["sigma_p"], g["sigma_o"], f("u_row"))
+    assert np.array_equal(pred, f("pred"))
+    assert np.array_equal(lwn, f("lw_new"))
+    assert np.array_equal(anc, f("anc", np.int32))
+    assert np.array_equal(x_out, f("x_out"))
+    assert np.all(lw_out == np.float32(-np.log(4.0)))
+
+
+def test_pf_step_vs_library_gaussian(orc):
+    """pred against a float64 matmul, the log-likelihood against scipy's
+    multivariate normal density (its normalising constant is the same for
+    every particle and is added back here)."""
+    d = si.pf_step(rows=3, P=64, D=4, O=2)
+    A = np.array([[0.9, 0.1, 0.0, -0.2], [0.0, 0.8, 0.3, 0.0], [0.1, 0.0, 0.7, 0.0],
+                  [0.0, -0.4, 0.0, 1.1]], np.float32)          # not symmetric
+    _, _, _, pred, lwn = orc.pf_step(d["x"], d["lw"], d["obs"], A, d["C"], d["eps"],
+                                     d["sigma_p"], d["sigma_o"], d["u_row"])
+    x64, e64 = d["x"].astype(np.float64), d["eps"].astype(np.float64)
+    ref = x64 @ A.astype(np.float64).T + d["sigma_p"] * e64
+    assert np.allclose(pred, ref, rtol=1e-5, atol=1e-6)
+    so = d["sigma_o"]
+    const = -0.5 * 2 * np.log(2 * np.pi * so * so)
+    for b in range(3):
+        mean = pred[b].astype(np.float64) @ d["C"].astype(np.float64).T
+        ll = np.array([stats.multivariate_normal(mean=m, cov=so * so * np.eye(2))
+                       .logpdf(d["obs"][b].astype(np.float64)) for m in mean]) - const
+        assert np.allclose(lwn[b], d["lw"][b] + ll, rtol=1e-5, atol=1e-4)
+
+
+def test_pf_step_reduces_to_resampling(orc):
+    """A = I, no process noise, C = 0, obs = 0: pred = x and lw' = lw
+    exactly, so the step is the resampler followed by a gather."""
+    d = si.pf_step(rows=8, P=1024, D=4, O=2)
+    A = np.eye(4, dtype=np.float32)
+    Cm = np.zeros((2, 4), np.float32)
+    obs = np.zeros((8, 2), np.float32)
+    x_out, lw_out, anc, pred, lwn = orc.pf_step(d["x"], d["lw"], obs, A, Cm, d["eps"], 0.0,
+                                               d["sigma_o"], d["u_row"])
+    assert np.array_equal(pred, d["x"])
+    assert np.array_equal(lwn, d["lw"])
+    assert np.array_equal(anc, orc.resample_rows(d["lw"], d["u_row"]))
+    assert np.array_equal(x_out, np.take_along_axis(d["x"], anc[:, :, None].astype(np.int64),
+                                                    axis=1))
+    assert np.all(lw_out == np.float32(-np.log(1024.0)))
+
+
+def test_pf_step_offspring_counts(orc):
+    """Systematic resampling gives particle j floor or ceil of P W_j
+    offspring, W = softmax of the updated log-weights (scipy)."""
+    d = si.pf_step(rows=16, P=1024, D=4, O=2)
+    x_out, _, anc, pred, lwn = orc.pf_step(d["x"], d["lw"], d["obs"], d["A"], d["C"], d["eps"],
+                                          d["sigma_p"], d["sigma_o"], d["u_row"])
+    for b in range(16):
+        W = special.softmax(lwn[b].astype(np.float64))
+        cnt = np.bincount(anc[b], minlength=1024)
+        assert np.all(np.abs(cnt - 1024 * W) < 1 + 1e-6)
+        assert np.all(np.diff(anc[b]) >= 0)
+        assert np.array_equal(x_out[b], pred[b][anc[b]])
