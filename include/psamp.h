@@ -215,6 +215,34 @@ psamp_status psamp_resample_rows(const float* logw, int64_t rows, int64_t P,
                                  int64_t ld_out, void* stream);
 
 /* ------------------------------------------------------------------------
+ * (4b) One particle-filter step, fused ([PF], the reference model's forward
+ * pass around its resampling step).  Per filter b of P particles in D
+ * dimensions with O observed values:
+ *   pred_j  = A x_j + sigma_p eps_j
+ *   ll_j    = -0.5 * sum_o (obs_o - (C pred_j)_o)^2 / sigma_o^2
+ *   lw'_j   = logw_j + ll_j
+ *   anc     = psamp_resample_rows(lw', u_row[b])        (same rule, same bits)
+ *   x_out_k = pred_{anc_k},  logw_out_k = (float)(-log P)
+ * Up to lw' all arithmetic is float32: each dot product summed in increasing
+ * index from +0, the noise term added last, ll = (-0.5 * S) / (sigma_o *
+ * sigma_o) with a correctly rounded division.
+ *   x, eps, x_out : rows x P x D floats (particle-major, contiguous),
+ *                   16-byte aligned.  eps holds standard normal draws.
+ *   logw, logw_out: rows x P floats.  obs: rows x O floats.
+ *   A: D x D, C: O x D floats, row-major, in device memory.
+ *   u_row: rows floats in [0, 1).  anc_out: rows x P int32 or NULL.
+ *   x_out may be x and logw_out may be logw (in-place update).
+ *   1 <= P <= 8192, D in {1, 2, 4, 8}, P * D <= 16384, 1 <= O <= 8,
+ *   1 <= rows <= 2^31 - 1.  sigma_o > 0 and finite, sigma_p finite.
+ * Errors: E_NULL, E_SIZE, E_PARAM, E_ALIGN, E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+psamp_status psamp_pf_step(const float* x, const float* logw, const float* obs,
+                           const float* A, const float* C, const float* eps, float sigma_p,
+                           float sigma_o, const float* u_row, int64_t rows, int64_t P,
+                           int64_t D, int64_t O, float* x_out, float* logw_out,
+                           int32_t* anc_out, void* stream);
+
+/* ------------------------------------------------------------------------
  * Priority rewrite (the scatter of [SEGT] "Integration" --
  * update_priorities_gpu): prio[idx_j] = vals_j for j = 0..m-1, the largest
  * j winning on repeated indices; indices outside [0, n) are ignored.

@@ -50,6 +50,8 @@ SIGNATURES = {
     "psamp_segtree_update": (_int, [_p, _int, _i64, _p, _p, _int, _i64, _dbl, _p, _sz, _p]),
     "psamp_segtree_sample": (_int, [_p, _int, _i64, _i64, _p, _int, _i64, _int, _p, _p]),
     "psamp_resample_rows": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p]),
+    "psamp_pf_step": (_int, [_p, _p, _p, _p, _p, _p, C.c_float, C.c_float, _p, _i64, _i64, _i64,
+                             _i64, _p, _p, _p, _p]),
     "psamp_scatter_workspace_size": (_sz, [_i64, _i64]),
     "psamp_scatter_lww": (_int, [_p, _int, _i64, _p, _p, _i64, _int, _p, _sz, _p]),
     "psamp_per_round_workspace_size": (_sz, [_i64, _i64]),
@@ -290,6 +292,42 @@ def resample_rows(logw: torch.Tensor, u_row: torch.Tensor, *, out: torch.Tensor 
     _check("psamp_resample_rows", lib().psamp_resample_rows(
         lw, rows, P, P, ur, o, P, _stream(stream)))
     return out
+
+
+def pf_step(x: torch.Tensor, logw: torch.Tensor, obs: torch.Tensor, A: torch.Tensor,
+            C_obs: torch.Tensor, eps: torch.Tensor, sigma_p: float, sigma_o: float,
+            u_row: torch.Tensor, *, x_out: torch.Tensor | None = None,
+            logw_out: torch.Tensor | None = None, anc_out: torch.Tensor | None = None,
+            stream=None):
+    """One particle-filter step (predict, likelihood, resample, gather) on
+    rows x P x D particles.  Returns (x_out, logw_out); x_out=x and
+    logw_out=logw update in place; anc_out (rows x P int32) is optional."""
+    if x.dim() != 3:
+        raise ValueError("x must be rows x P x D")
+    rows, P, D = x.shape
+    O = C_obs.shape[0] if C_obs.dim() == 2 else 0
+    if x_out is None:
+        x_out = torch.empty_like(x)
+    if logw_out is None:
+        logw_out = torch.empty(rows, P, dtype=torch.float32, device=x.device)
+    f32 = (torch.float32,)
+    for t, nm, shape in ((logw, "logw", (rows, P)), (obs, "obs", (rows, O)),
+                         (A, "A", (D, D)), (C_obs, "C_obs", (O, D)), (eps, "eps", (rows, P, D)),
+                         (u_row, "u_row", (rows,)), (x_out, "x_out", (rows, P, D)),
+                         (logw_out, "logw_out", (rows, P))):
+        if tuple(t.shape) != shape:
+            raise ValueError(f"{nm} must have shape {shape}, got {tuple(t.shape)}")
+    a_ptr = 0
+    if anc_out is not None:
+        if tuple(anc_out.shape) != (rows, P):
+            raise ValueError("anc_out must be rows x P")
+        a_ptr = _dev(anc_out, "anc_out", (torch.int32,))
+    _check("psamp_pf_step", lib().psamp_pf_step(
+        _dev(x, "x", f32), _dev(logw, "logw", f32), _dev(obs, "obs", f32), _dev(A, "A", f32),
+        _dev(C_obs, "C_obs", f32), _dev(eps, "eps", f32), float(sigma_p), float(sigma_o),
+        _dev(u_row, "u_row", f32), rows, P, D, O, _dev(x_out, "x_out", f32),
+        _dev(logw_out, "logw_out", f32), a_ptr or None, _stream(stream)))
+    return x_out, logw_out
 
 
 # ------------------------------------------------------------ rewrite

@@ -1,80 +1,20 @@
-// resample.hip -- row-batched systematic resampling.
-//
-// POPCORNBENCH particle-filter trace (Kimi-K2.6, l2_p48), the reference
-// model's resampling step, per row of P log-weights:
-//   new_log_w = log_w - logsumexp(log_w);  weights = exp(new_log_w);
-//   cumsum;  u_k = (k + u_row) / P  (float);  anc_k = searchsorted(cumsum,
-//   u_k) (first index with cumsum >= u_k), clamped to P-1.
-// Here: the max in float (exact), exp and the sums in double (the weights
-// must be good to ~1e-9 for the ancestors to agree with an exact-arithmetic
-// reading), W_j = exp(lw_j - m) / s with s = sum_j exp(lw_j - m) (equal to
-// exp(lw_j - lse) with lse = m + log s, one exp per particle instead of
-// two), thresholds in float exactly as the page computes them.
-//
-// One 256-thread workgroup per row; reads and writes are 16-byte vectors.
-// No search: the thresholds are non-decreasing in k, so particle j is the
-// ancestor of exactly the k with M_{j-1} < t_k <= M_j, where M is the
-// running max of the row CDF ("first j with C_j >= t" is "first j with
-// M_j >= t"), and the last particle also of every k with t_k > M_{P-1}.
-// The number of thresholds <= x comes from its estimate x P - u, checked on
-// the exact float thresholds.  Each particle with a non-empty range marks
-// its first k (the first k's of non-empty ranges are distinct) and a
-// block-wide max-scan over k fills every k with its particle: one heavy
-// particle (hundreds of offspring are common here) costs no serial loop.
+// resample.hip -- row-batched systematic resampling (the per-row ancestor
+// computation is in resample_row.h).
 #include "psamp_device.h"
 #include "psamp_host.h"
-#include "scan_tile.h"
+#include "resample_row.h"
 
 namespace psamp {
 
-constexpr int kResThreads = 256;
-
-__device__ __forceinline__ float wave_max_f32(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
-// Threshold k of a row, in float exactly as the page forms it: fl(fl(k + u)
-// / P).  For P a power of two, fl(a * (1/P)) is the same float (1/P is exact
-// and both round the same exact quotient), without the division sequence.
-template <bool POW2>
-__device__ __forceinline__ double res_threshold(int k, float ub, float Pf, float invP) {
-    const float a = __fadd_rn((float)k, ub);
-    return (double)(POW2 ? __fmul_rn(a, invP) : __fdiv_rn(a, Pf));
-}
-
-// #{k in [0, P) : t_k <= x}.  fl(k + u) is within 2^-11 of k + u (k < 2^13)
-// and the division or scaling adds one more rounding, so t_k P lies within
-// about 2^-11 of k + u: at most one k can be counted differently by the
-// estimate floor(x P - u) + 1, and one check on each side fixes it.
-template <bool POW2>
-__device__ __forceinline__ int res_count_le(double x, float ub, float Pf, float invP, int P) {
-    const double e = floor(x * (double)P - (double)ub);
-    const int k = !(e >= 0.0) ? 0 : (e >= (double)P ? P : (int)e + 1);
-    const bool over = k > 0 && res_threshold<POW2>(k - 1, ub, Pf, invP) > x;
-    const bool under = k < P && res_threshold<POW2>(k, ub, Pf, invP) <= x;
-    return k - (over ? 1 : 0) + (under ? 1 : 0);
-}
-
-// POW2: P is a power of two (see res_threshold).
 template <int R, bool POW2>
 __global__ __launch_bounds__(kResThreads) void k_resample_rows(
     const float* __restrict__ lw, int64_t P, int64_t ld_in, const float* __restrict__ u_row,
     int32_t* __restrict__ anc, int64_t ld_out, int vec_ok) {
     constexpr int ROW = kResThreads * 4;
-    __shared__ __attribute__((aligned(16))) uint32_t O[R * ROW];
-    __shared__ uint32_t s_wm[4][R];
-    __shared__ double s_last[4][R];
-    __shared__ double s_wtot[4][R];
-    __shared__ double s_wmax[4][R];
-    __shared__ float s_max[4];
-    __shared__ double s_sum[4];
+    __shared__ ResLds<R> L;
     __shared__ MathLds M;
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
     const int64_t b = blockIdx.x;
     const float* x = lw + b * ld_in;
     const MathRegs mr = math_load(tid);
@@ -101,129 +41,21 @@ __global__ __launch_bounds__(kResThreads) void k_resample_rows(
     }
     math_store(&M, tid, mr);
 
-    // max (float, exact)
-    float mx = ninf;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) mx = fmaxf(mx, v[r][c]);
-    mx = wave_max_f32(mx);
-    if (lane == 0) s_max[wave] = mx;
-    __syncthreads();
-    const double m = (double)fmaxf(fmaxf(s_max[0], s_max[1]), fmaxf(s_max[2], s_max[3]));
-
-    // e_j = exp(lw_j - m) in double, thread-local prefixes, row sum s
-    double q[R][4];
-    double ssum = 0.0;
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const double e = (v[r][c] == ninf) ? 0.0 : exp_d((double)v[r][c] - m, &M);
-            q[r][c] = e;
-            ssum = ssum + e;
-        }
-    ssum = wave_sum(ssum);
-    if (lane == 0) s_sum[wave] = ssum;
-    __syncthreads();
-    const double s = ((s_sum[0] + s_sum[1]) + s_sum[2]) + s_sum[3];
-    const double inv_s = 1.0 / s;
-
-    // W_j = e_j / s; inclusive scan of W (double); M = its running max
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const double w = q[r][c] * inv_s;
-            q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
-        }
-    double X[R];
-    double A;
-    tile_scan_256<R, double>(q, X, A, s_wtot);
-    tile_local_values<R, double>(q, X, s_wmax);
-
-    // ancestors: particle j takes k in [#{t <= M_{j-1}}, #{t <= M_j}); the
-    // last particle also every k above.  O[k] = j + 1 at the first k of each
-    // non-empty range, 0 elsewhere.  prev[r]: M of the element before this
-    // thread's first element of row r.
-    double prev[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        prev[r] = wave_shr1(q[r][3]);
-        if (lane == kWave - 1) s_last[wave][r] = q[r][3];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) O[r * ROW + 4 * tid + c] = 0u;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (lane == 0) prev[r] = wave > 0 ? s_last[wave - 1][r] : (r > 0 ? s_last[3][r - 1] : 0.0);
-    const float Pf = (float)P;
     const int Pi = (int)P;
-    const float invP = 1.0f / Pf;              // exact when POW2
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const int j0 = r * ROW + 4 * tid;
-        int k0 = j0 == 0 ? 0 : res_count_le<POW2>(prev[r], ub, Pf, invP, Pi);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int j = j0 + c;
-            const int k1 = (j >= Pi - 1) ? Pi : res_count_le<POW2>(q[r][c], ub, Pf, invP, Pi);
-            if (j < Pi && k1 > k0) O[k0] = (uint32_t)j + 1u;
-            k0 = k1 > k0 ? k1 : k0;
-        }
-    }
-    __syncthreads();
-
-    // inclusive max-scan over k (rows, then threads, then columns): the
-    // particle of every k
     uint32_t a[R][4];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const uint4 t4 = *reinterpret_cast<const uint4*>(&O[r * ROW + 4 * tid]);
-        a[r][0] = t4.x;
-        a[r][1] = max_(a[r][0], t4.y);
-        a[r][2] = max_(a[r][1], t4.z);
-        a[r][3] = max_(a[r][2], t4.w);
-    }
-    uint32_t ex[R];
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        uint32_t y = a[r][3];
-        y = max_(y, dpp32<kRowShr1, 0xF, true>(y));
-        y = max_(y, dpp32<kRowShr2, 0xF, true>(y));
-        y = max_(y, dpp32<kRowShr4, 0xF, true>(y));
-        y = max_(y, dpp32<kRowShr8, 0xF, true>(y));
-        y = max_(y, dpp32<kRowBcast15, 0xA, false>(y));
-        y = max_(y, dpp32<kRowBcast31, 0xC, false>(y));
-        ex[r] = dpp32<kWaveShr1, 0xF, true>(y);
-        const uint32_t wm = (uint32_t)__builtin_amdgcn_readlane((int)y, kWave - 1);
-        if (lane == 0) s_wm[wave][r] = wm;
-    }
-    __syncthreads();
-    uint32_t carry = 0u;
+    res_ancestors<R, POW2>(v, Pi, ub, &M, L, a);
+
     int32_t* out = anc + b * ld_out;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        uint32_t pm = carry, rm = carry;
-#pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-            const uint32_t t = s_wm[w2][r];
-            if (w2 < wave) pm = max_(pm, t);
-            rm = max_(rm, t);
-        }
-        pm = max_(pm, ex[r]);
-        carry = rm;
-        int32_t o[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = (int32_t)max_(a[r][c], pm) - 1;
         const int e0 = r * ROW + 4 * tid;
         if (full && vec_ok) {
-            *reinterpret_cast<int4*>(out + e0) = make_int4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<int4*>(out + e0) =
+                make_int4((int)a[r][0], (int)a[r][1], (int)a[r][2], (int)a[r][3]);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)
-                if (e0 + c < Pi) out[e0 + c] = o[c];
+                if (e0 + c < Pi) out[e0 + c] = (int32_t)a[r][c];
         }
     }
 }

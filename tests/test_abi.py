@@ -168,6 +168,32 @@ def test_resample_and_scatter_validation(L):
     assert pr(FAKE, 1000, 0.6, 0.4, FAKE, 10, None, FAKE, FAKE, FAKE, FAKE, FAKE + 8, wsz, None) == E_ALIGN
 
 
+def test_pf_step_validation(L):
+    f = L.psamp_pf_step
+    ok = (FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.1, 0.5, FAKE)
+
+    def call(*, args=ok, rows=16, P=1024, D=4, O=2, xo=FAKE, lo=FAKE, an=None):
+        return f(*args, rows, P, D, O, xo, lo, an, None)
+
+    assert call(args=(None,) + ok[1:]) == E_NULL
+    assert call(lo=None) == E_NULL
+    assert call(rows=0) == E_SIZE
+    assert call(P=0) == E_SIZE
+    assert call(P=8193, D=1) == E_SIZE
+    assert call(D=3) == E_SIZE
+    assert call(D=16, P=64) == E_SIZE
+    assert call(P=4097, D=4) == E_SIZE          # P * D over 16384
+    assert call(P=2049, D=8) == E_SIZE
+    assert call(O=0) == E_SIZE
+    assert call(O=9) == E_SIZE
+    assert call(args=ok[:7] + (0.0, FAKE)) == E_PARAM
+    assert call(args=ok[:7] + (float("inf"), FAKE)) == E_PARAM
+    assert call(args=ok[:6] + (float("nan"), 0.5, FAKE)) == E_PARAM
+    assert call(xo=FAKE + 8) == E_ALIGN
+    assert call(args=(FAKE + 4,) + ok[1:]) == E_ALIGN
+    assert call(an=FAKE + 2) == E_ALIGN
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     import proportional_sampling_amd as ps
