@@ -53,7 +53,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a HIP graph")
-    ap.add_argument("--only", default="", help="profiling helper: scan:<n> | copy:<MiB>")
+    ap.add_argument("--only", default="",
+                    help="profiling helper: scan:<n> | copy:<MiB> | pf | per_large")
     return ap.parse_args()
 
 
@@ -108,7 +109,7 @@ class PerMid:
 
 
 KERNEL_NAMES = {
-    "build_cdf": "k_build_cdf<4, true, float, double>",
+    "build_cdf": "k_build_cdf<4, true, float, double, false>",
     "sample": "k_sample_fp<double>",
     "is_weights": "k_isw_single<float>",
     "scatter_lww": "k_scatter_grouped",
@@ -266,6 +267,46 @@ def resample_bench(ps, torch, reps=50):
     return {"us": round(us, 2), "GB/s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
+def pf_bench(ps, torch, reps=50):
+    """The fused particle-filter step at 1024 filters x 4096 particles (D = 4,
+    O = 2) and at 16 x 1024; HBM bytes per particle: x, eps, x_out (3 D
+    floats), lw in and out, the ancestor out (4 + 4 + 4)."""
+    import synthetic_inputs as si
+    res = {}
+    flush = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    for name, d in (("1024x4096", si.pf_step()), ("16x1024", si.pf_small())):
+        t = {k: torch.from_numpy(d[k]).cuda() for k in ("x", "lw", "obs", "A", "C", "eps",
+                                                         "u_row")}
+        rows, P, D = d["x"].shape
+        xo = torch.empty_like(t["x"])
+        lo = torch.empty_like(t["lw"])
+        an = torch.empty(rows, P, dtype=torch.int32, device="cuda")
+        fn = lambda: ps.pf_step(t["x"], t["lw"], t["obs"], t["A"], t["C"], t["eps"],
+                                d["sigma_p"], d["sigma_o"], t["u_row"], x_out=xo, logw_out=lo,
+                                anc_out=an)
+        warm = loop_us(torch, fn, reps)
+        # median of single calls, each after a write that evicts the
+        # Infinity Cache (inputs come from HBM)
+        ts = []
+        for _ in range(max(5, reps // 4)):
+            flush_cache(torch, flush)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(1e3 * e0.elapsed_time(e1))
+        us = statistics.median(ts)
+        nbytes = rows * P * (3 * 4 * D + 12) + rows * 4 * (1 + d["obs"].shape[1])
+        gbs = nbytes / (us * 1e-6) / 1e9
+        log(f"pf_step {name}: {us:.1f} us cold, {warm:.1f} us back-to-back, {gbs:.0f} GB/s")
+        res[name] = {"us": round(us, 2), "us_back_to_back": round(warm, 2),
+                     "GB/s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4),
+                     "particles_per_s": round(rows * P / (us * 1e-6), 1)}
+    return res
+
+
 def per_large_bench(ps, torch, reps=10):
     """PER large: B = 2^24, 2^20 stratified draws, CDF path and tree path."""
     import synthetic_inputs as si
@@ -335,6 +376,12 @@ def main():
         n = int(args.only.split(":")[1])
         scan_sweep(ps, torch, [n], reps=20)
         return
+    if args.only == "pf":
+        log(json.dumps(pf_bench(ps, torch, reps=20)))
+        return
+    if args.only == "per_large":
+        log(json.dumps(per_large_bench(ps, torch)))
+        return
     if args.only.startswith("copy:"):
         mib = int(args.only.split(":")[1])
         a = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
@@ -393,6 +440,7 @@ def main():
         extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])
         extra["sumtree"] = sumtree_bench(ps, torch)
         extra["resample_rows"] = resample_bench(ps, torch)
+        extra["pf_step"] = pf_bench(ps, torch)
         extra["per_large"] = per_large_bench(ps, torch)
 
     cpu = None
