@@ -286,6 +286,47 @@ class Tree:
         return fn(self._h)
 
 
+# ------------------------------------------------------ replay priorities
+class Replay:
+    """[SEGT] "Integration with GpuReplayBuffer": a ring of `capacity`
+    slots whose priorities live in the pointer sum tree (F32 leaves =
+    p^alpha).  insert_batch writes each item at the cursor and advances it
+    (mod capacity), one item after the other; update_priorities sets leaves;
+    sample_proportional descends over the filled slots; IS weights take the
+    textbook (N P_i)^-beta / max form with P_i = leaf_i / root, N = filled
+    slots; total_priority is the root."""
+
+    def __init__(self, capacity: int, alpha: float):
+        self.capacity = int(capacity)
+        self.cap = cap_pow2(self.capacity)
+        self.alpha = float(alpha)
+        self.tree = Tree("f32", self.cap)
+        self.cursor = 0
+        self.size = 0
+
+    def insert(self, prio) -> np.ndarray:
+        prio = _c(prio, np.float32)
+        slots = np.empty(prio.size, np.int32)
+        for i in range(prio.size):
+            slots[i] = self.cursor
+            self.tree.update(slots[i:i + 1], prio[i:i + 1], self.alpha)
+            self.cursor = (self.cursor + 1) % self.capacity
+            self.size = min(self.size + 1, self.capacity)
+        return slots
+
+    def update(self, slots, prio):
+        self.tree.update(slots, prio, self.alpha)
+
+    def sample(self, u, beta: float, stratified: bool = True):
+        idx = self.tree.sample(u, self.size, stratified)
+        leaves = self.tree.flat()[self.cap:self.cap + self.size]
+        w = is_weights(leaves, 1.0, float(self.tree.root()), idx, beta, N=self.size)
+        return idx, w
+
+    def total(self) -> float:
+        return self.tree.root()
+
+
 # --------------------------------------------------------------- resampling
 def resample_rows(lw, u_row) -> np.ndarray:
     lw = _c(lw, np.float32)

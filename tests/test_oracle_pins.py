@@ -461,3 +461,65 @@ def test_pf_step_offspring_counts(orc):
         assert np.all(np.abs(cnt - 1024 * W) < 1 + 1e-6)
         assert np.all(np.diff(anc[b]) >= 0)
         assert np.array_equal(x_out[b], pred[b][anc[b]])
+
+
+# ------------------------------------------------------ replay priorities
+def test_replay_ring_slots_and_leaves_dict_replay(orc):
+    """Inserting 2.5 rings' worth in uneven batches: the slots walk the ring
+    in order and every leaf is the correctly rounded p^alpha of the last item
+    written to that slot (a dict replay of the same writes)."""
+    cap, alpha = 1000, 0.6
+    rb = orc.Replay(cap, alpha)
+    rng = np.random.default_rng(5)
+    last = {}
+    n = 0
+    for m in (1, 7, 300, 999, 1000, 193):
+        p = (rng.random(m) + 0.01).astype(np.float32)
+        slots = rb.insert(p)
+        assert np.array_equal(slots, (n + np.arange(m)) % cap)
+        for s_, v in zip(slots, p):
+            last[int(s_)] = v
+        n += m
+    assert rb.cursor == n % cap and rb.size == cap
+    leaves = rb.tree.flat()[orc.cap_pow2(cap):]
+    for s_, v in last.items():
+        assert leaves[s_] == orc.leaf_f32(float(v), alpha)
+    assert np.all(leaves[cap:] == 0)
+
+
+def test_replay_total_and_descent_integer_leaves(orc):
+    """alpha = 1 and integer priorities: leaves and sums are exact, so the
+    root is the integer sum and each descent is the exact lower bound of its
+    threshold over the integer CDF of the filled slots (brute force)."""
+    cap = 300
+    rb = orc.Replay(cap, 1.0)
+    rng = np.random.default_rng(6)
+    p = rng.integers(0, 50, 200).astype(np.float32)
+    rb.insert(p)
+    upd = rng.integers(0, 200, 40).astype(np.int32)
+    val = rng.integers(1, 50, 40).astype(np.float32)
+    rb.update(upd, val)
+    cur = p.copy()
+    for i, v in zip(upd, val):
+        cur[i] = v
+    assert rb.total() == float(cur.sum())
+    U = (np.arange(64, dtype=np.float32) + 0.5) / np.float32(64)
+    idx, w = rb.sample(U, 0.4, stratified=False)
+    Cc = np.cumsum(cur.astype(np.float64))
+    t = (U * np.float32(rb.total())).astype(np.float64)     # iid: t = U * root in float
+    ref = np.minimum(np.searchsorted(Cc, t, "left"), 199)
+    assert np.array_equal(idx, ref)
+    # IS: (N P_i)^-beta / max equals (L_min / L_i)^beta
+    L = cur[idx].astype(np.float64)
+    assert np.allclose(w, (L.min() / L) ** 0.4, rtol=1e-6)
+
+
+def test_replay_partial_ring_samples_only_filled_slots(orc):
+    rb = orc.Replay(4096, 0.6)
+    rb.insert(np.full(100, 2.0, np.float32))
+    U = np.random.default_rng(7).random(4096, dtype=np.float32)
+    idx, w = rb.sample(U, 0.4, stratified=True)
+    assert idx.min() >= 0 and idx.max() <= 99
+    assert np.all(w == 1.0)                 # equal priorities
+    counts = np.bincount(idx, minlength=100)
+    assert np.all(np.abs(counts - 4096 / 100) <= 2)
