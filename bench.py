@@ -255,6 +255,35 @@ def sumtree_bench(ps, torch, rounds=200):
     return res
 
 
+def replay_bench(ps, torch, rounds=200):
+    """Replay priorities at capacity 500000 (a full ring): per round, insert
+    1024 new items, update the priorities of 1024 sampled slots, sample 1024
+    stratified slots with IS weights."""
+    import synthetic_inputs as si
+    d = si.sumtree(rounds=rounds)
+    rb = ps.ReplayPriorities(500000, d["alpha"], max_batch=1024)
+    p0 = torch.from_numpy(d["p0"]).cuda()
+    for j in range(0, p0.numel(), 1024):
+        rb.insert(p0[j:j + 1024])
+    v = torch.from_numpy(d["v"]).cuda()
+    U = torch.from_numpy(d["U"]).cuda()
+    slots_in = torch.empty(1024, dtype=torch.int32, device="cuda")
+    slots = torch.empty(1024, dtype=torch.int32, device="cuda")
+    w = torch.empty(1024, dtype=torch.float32, device="cuda")
+    it = {"r": 0}
+
+    def one_round():
+        r = it["r"] % rounds
+        it["r"] += 1
+        rb.insert(v[r], out=slots_in)
+        rb.sample(U[r], 0.4, out=slots, out_w=w)
+        rb.update(slots, v[(r + 1) % rounds])
+
+    res = {"round_us": round(loop_us(torch, one_round, rounds), 2)}
+    log(f"replay: {res}")
+    return res
+
+
 def resample_bench(ps, torch, reps=50):
     import synthetic_inputs as si
     d = si.resample()
@@ -439,6 +468,7 @@ def main():
     if not args.no_extra:
         extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])
         extra["sumtree"] = sumtree_bench(ps, torch)
+        extra["replay"] = replay_bench(ps, torch)
         extra["resample_rows"] = resample_bench(ps, torch)
         extra["pf_step"] = pf_bench(ps, torch)
         extra["per_large"] = per_large_bench(ps, torch)

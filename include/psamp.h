@@ -198,6 +198,62 @@ psamp_status psamp_segtree_sample(const void* tree, psamp_dtype tree_t, int64_t 
                                   int64_t k, int stratified, int32_t* out_idx, void* stream);
 
 /* ------------------------------------------------------------------------
+ * (3b) Replay priorities on the sum tree ([SEGT] "Integration with
+ * GpuReplayBuffer": insert_batch writes the new priorities and updates the
+ * tree at the inserted slots, update_priorities is the tree's batched
+ * update, sample_proportional is the descent, total_priority is the root).
+ * A ring of `capacity` slots: insert writes slots cursor, cursor+1, ...
+ * (mod capacity) in batch order; the filled slots are [0, size).  The tree
+ * is F32 (leaf = p^alpha rounded to float), 2 * cap_pow2 floats of device
+ * memory, zero-filled by the caller before psamp_replay_init.  The struct is
+ * host memory owned by the caller; insert advances cursor and size when it
+ * enqueues.  ws: psamp_replay_workspace_size(capacity, largest batch) bytes
+ * of device memory, zero-filled once (may be NULL when that size is 0).
+ * Calls are stream-ordered like the rest of the library; two streams must
+ * not use one psamp_replay at the same time.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+    int64_t capacity;   /* slots in the ring                              */
+    int64_t cap_pow2;   /* psamp_segtree_cap_pow2(capacity)               */
+    int64_t cursor;     /* next slot an insert writes, in [0, capacity)   */
+    int64_t size;       /* filled slots, in [0, capacity]                 */
+    double alpha;       /* leaf = p^alpha                                 */
+    float* tree;        /* device, 2 * cap_pow2 floats                    */
+    void* ws;           /* device workspace                               */
+    size_t ws_bytes;
+} psamp_replay;
+
+size_t psamp_replay_workspace_size(int64_t capacity, int64_t max_batch);
+/* Fills *rb for an empty ring.  Errors: E_NULL, E_SIZE (capacity < 1 or
+ * over 2^30), E_PARAM (alpha <= 0 or not finite), E_ALIGN (tree not 16-byte aligned). */
+psamp_status psamp_replay_init(psamp_replay* rb, int64_t capacity, double alpha, float* tree,
+                               void* ws, size_t ws_bytes);
+/* insert_batch: out_slots[i] = (cursor + i) mod capacity, leaf of that slot
+ * <- prio[i]^alpha (a slot written twice in one batch keeps the later
+ * value), then cursor += m (mod capacity), size = min(size + m, capacity).
+ * prio: m floats >= 0.  out_slots: m int32 (device), required: the caller
+ * stores its items there.  Errors: E_NULL, E_SIZE, E_PARAM (bad *rb),
+ * E_ALIGN, E_WORKSPACE, E_LAUNCH. */
+psamp_status psamp_replay_insert(psamp_replay* rb, const float* prio, int64_t m,
+                                 int32_t* out_slots, void* stream);
+/* update_priorities: leaf of slots[j] <- prio[j]^alpha, later j winning on
+ * repeats.  Slots must be filled ones ([0, size)); others are ignored when
+ * outside [0, cap_pow2).  Errors: as insert. */
+psamp_status psamp_replay_update(psamp_replay* rb, const int32_t* slots, const float* prio,
+                                 int64_t m, void* stream);
+/* sample_proportional: k descents over the filled slots with the thresholds
+ * of psamp_segtree_sample (F32 tree; stratified 0 or 1), and, when out_w is
+ * not NULL, the IS weights of psamp_is_weights on the leaves:
+ * (L_min / L_i)^beta = (N P_i)^-beta / max over the batch.
+ * Errors: E_NULL, E_SIZE (empty ring), E_PARAM, E_WORKSPACE, E_LAUNCH. */
+psamp_status psamp_replay_sample(const psamp_replay* rb, const float* u, int64_t k,
+                                 int stratified, double beta, int32_t* out_slots, float* out_w,
+                                 void* stream);
+/* total_priority: the device address of the root (the sum of all leaves);
+ * NULL if rb or its tree is NULL. */
+const float* psamp_replay_total(const psamp_replay* rb);
+
+/* ------------------------------------------------------------------------
  * (4) Row-batched systematic resampling ([PF], the reference model's
  * resampling step).  Per row b of P float log-weights:
  *   lse  = m + log(sum_j exp(lw_j - m)),  m = max_j lw_j

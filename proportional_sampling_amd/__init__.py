@@ -49,6 +49,12 @@ SIGNATURES = {
     "psamp_segtree_update_workspace_size": (_sz, [_i64, _i64]),
     "psamp_segtree_update": (_int, [_p, _int, _i64, _p, _p, _int, _i64, _dbl, _p, _sz, _p]),
     "psamp_segtree_sample": (_int, [_p, _int, _i64, _i64, _p, _int, _i64, _int, _p, _p]),
+    "psamp_replay_workspace_size": (_sz, [_i64, _i64]),
+    "psamp_replay_init": (_int, [_p, _i64, _dbl, _p, _p, _sz]),
+    "psamp_replay_insert": (_int, [_p, _p, _i64, _p, _p]),
+    "psamp_replay_update": (_int, [_p, _p, _p, _i64, _p]),
+    "psamp_replay_sample": (_int, [_p, _p, _i64, _int, _dbl, _p, _p, _p]),
+    "psamp_replay_total": (_p, [_p]),
     "psamp_resample_rows": (_int, [_p, _i64, _i64, _i64, _p, _p, _i64, _p]),
     "psamp_pf_step": (_int, [_p, _p, _p, _p, _p, _p, C.c_float, C.c_float, _p, _i64, _i64, _i64,
                              _i64, _p, _p, _p, _p]),
@@ -292,6 +298,87 @@ def resample_rows(logw: torch.Tensor, u_row: torch.Tensor, *, out: torch.Tensor 
     _check("psamp_resample_rows", lib().psamp_resample_rows(
         lw, rows, P, P, ur, o, P, _stream(stream)))
     return out
+
+
+class _ReplayStruct(C.Structure):
+    """Mirror of psamp_replay (include/psamp.h)."""
+    _fields_ = [("capacity", C.c_int64), ("cap_pow2", C.c_int64), ("cursor", C.c_int64),
+                ("size", C.c_int64), ("alpha", C.c_double), ("tree", C.c_void_p),
+                ("ws", C.c_void_p), ("ws_bytes", C.c_size_t)]
+
+
+class ReplayPriorities:
+    """Priorities of a replay ring of `capacity` slots on an F32 sum tree:
+    insert (insert_batch), update (update_priorities), sample
+    (sample_proportional, with IS weights) and total (total_priority).
+    The tree and workspace are device tensors owned by this object."""
+
+    def __init__(self, capacity: int, alpha: float = 0.6, max_batch: int = 8192, device=None):
+        dev = device if device is not None else "cuda"
+        cp = int(lib().psamp_segtree_cap_pow2(int(capacity)))
+        if cp == 0:
+            raise ValueError("capacity must be in [1, 2^30]")
+        self.tree = torch.zeros(2 * cp, dtype=torch.float32, device=dev)
+        self.max_batch = int(max_batch)
+        self.ws = Workspace(lib().psamp_replay_workspace_size(int(capacity), self.max_batch),
+                            device=dev)
+        self._rb = _ReplayStruct()
+        _check("psamp_replay_init", lib().psamp_replay_init(
+            C.byref(self._rb), int(capacity), float(alpha), self.tree.data_ptr(), self.ws.ptr,
+            self.ws.nbytes))
+
+    @property
+    def capacity(self) -> int:
+        return int(self._rb.capacity)
+
+    @property
+    def size(self) -> int:
+        return int(self._rb.size)
+
+    @property
+    def cursor(self) -> int:
+        return int(self._rb.cursor)
+
+    def insert(self, prio: torch.Tensor, *, out: torch.Tensor | None = None,
+               stream=None) -> torch.Tensor:
+        m = prio.numel()
+        if out is None:
+            out = torch.empty(m, dtype=torch.int32, device=self.tree.device)
+        _check("psamp_replay_insert", lib().psamp_replay_insert(
+            C.byref(self._rb), _dev(prio, "prio", (torch.float32,)), m,
+            _dev(out, "out", (torch.int32,)), _stream(stream)))
+        return out
+
+    def update(self, slots: torch.Tensor, prio: torch.Tensor, stream=None):
+        m = slots.numel()
+        if prio.numel() != m:
+            raise ValueError("slots and prio must have the same length")
+        _check("psamp_replay_update", lib().psamp_replay_update(
+            C.byref(self._rb), _dev(slots, "slots", (torch.int32,)),
+            _dev(prio, "prio", (torch.float32,)), m, _stream(stream)))
+
+    def sample(self, u: torch.Tensor, beta: float | None = 0.4, *, stratified: bool = True,
+               out: torch.Tensor | None = None, out_w: torch.Tensor | None = None,
+               stream=None):
+        """Returns slots, or (slots, IS weights) when beta is not None."""
+        k = u.numel()
+        if out is None:
+            out = torch.empty(k, dtype=torch.int32, device=self.tree.device)
+        w_ptr = None
+        if beta is not None:
+            if out_w is None:
+                out_w = torch.empty(k, dtype=torch.float32, device=self.tree.device)
+            w_ptr = _dev(out_w, "out_w", (torch.float32,))
+        _check("psamp_replay_sample", lib().psamp_replay_sample(
+            C.byref(self._rb), _dev(u, "u", (torch.float32,)), k, int(stratified),
+            float(beta or 0.0), _dev(out, "out", (torch.int32,)), w_ptr, _stream(stream)))
+        return out if beta is None else (out, out_w)
+
+    def total(self) -> torch.Tensor:
+        """The root of the tree (a view: it follows later updates)."""
+        addr = lib().psamp_replay_total(C.byref(self._rb))
+        assert addr == self.tree.data_ptr() + 4
+        return self.tree[1]
 
 
 def pf_step(x: torch.Tensor, logw: torch.Tensor, obs: torch.Tensor, A: torch.Tensor,

@@ -194,6 +194,35 @@ def test_pf_step_validation(L):
     assert call(an=FAKE + 2) == E_ALIGN
 
 
+def test_replay_validation(L):
+    import proportional_sampling_amd as ps
+    rb = ps._ReplayStruct()
+    ref = C.byref(rb)
+    assert L.psamp_replay_init(None, 10, 0.6, FAKE, None, 0) == E_NULL
+    assert L.psamp_replay_init(ref, 10, 0.6, None, None, 0) == E_NULL
+    assert L.psamp_replay_init(ref, 0, 0.6, FAKE, None, 0) == E_SIZE
+    assert L.psamp_replay_init(ref, (1 << 30) + 1, 0.6, FAKE, None, 0) == E_SIZE
+    assert L.psamp_replay_init(ref, 10, 0.0, FAKE, None, 0) == E_PARAM
+    assert L.psamp_replay_init(ref, 10, 0.6, FAKE + 2, None, 0) == E_ALIGN
+    assert L.psamp_replay_init(ref, 1000, 0.6, FAKE, None, 0) == OK
+    assert (rb.capacity, rb.cap_pow2, rb.cursor, rb.size) == (1000, 1024, 0, 0)
+    assert L.psamp_replay_total(ref) == FAKE + 4
+    assert L.psamp_replay_insert(ref, FAKE, 0, FAKE, None) == OK      # nothing enqueued
+    assert (rb.cursor, rb.size) == (0, 0)
+    assert L.psamp_replay_insert(ref, None, 5, FAKE, None) == E_NULL
+    assert L.psamp_replay_insert(ref, FAKE, -1, FAKE, None) == E_SIZE
+    assert L.psamp_replay_insert(ref, FAKE, 5, FAKE + 1, None) == E_ALIGN
+    assert L.psamp_replay_sample(ref, FAKE, 8, 1, 0.4, FAKE, FAKE, None) == E_SIZE   # empty
+    rb.size = 10
+    assert L.psamp_replay_sample(ref, FAKE, 8, 2, 0.4, FAKE, FAKE, None) == E_PARAM
+    assert L.psamp_replay_sample(ref, FAKE, 8, 1, -0.5, FAKE, FAKE, None) == E_PARAM
+    assert L.psamp_replay_sample(ref, FAKE, 1 << 20, 1, 0.4, FAKE, FAKE, None) == E_WS
+    rb.cursor = 1000                                                    # corrupted state
+    assert L.psamp_replay_update(ref, FAKE, FAKE, 4, None) == E_PARAM
+    assert L.psamp_replay_workspace_size(1000, 8192) == 0
+    assert L.psamp_replay_workspace_size(1000, 1 << 20) > 0
+
+
 def test_binding_fails_loudly_without_gpu_tensors():
     import torch
     import proportional_sampling_amd as ps
