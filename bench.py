@@ -169,14 +169,31 @@ def timed_steps(torch, fn, steps):
     return e0.elapsed_time(e1) / 1000.0, wall
 
 
-def flush_cache(torch, buf):
-    buf.add_(1)      # a 512 MiB read-modify-write evicts the 256 MB Infinity Cache
+class CacheFlush:
+    """Evicts the 256 MB Infinity Cache before a cold-cache timing: a 512 MiB
+    read-modify-write pushes everything out, then a 512 MiB read replaces the
+    dirty lines it leaves with clean ones (otherwise the timed kernel would
+    also pay for writing the flush buffer back)."""
+
+    def __init__(self, torch):
+        self.w = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        self.r = torch.ones(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+        self.torch = torch
+
+    def __call__(self):
+        self.w.add_(1)
+        self.torch.sum(self.r, dim=0, out=self.sink)
+
+
+def flush_cache(torch, flush):
+    flush()
 
 
 def scan_sweep(ps, torch, sizes, reps=8):
     """Median launch time of psamp_build_cdf per size, cache flushed."""
     out = []
-    flush = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    flush = CacheFlush(torch)
     for n in sizes:
         g = torch.Generator(device="cuda").manual_seed(n)
         p = torch.exp(2.0 * torch.randn(n, device="cuda", generator=g)).float()
@@ -302,7 +319,7 @@ def pf_bench(ps, torch, reps=50):
     floats), lw in and out, the ancestor out (4 + 4 + 4)."""
     import synthetic_inputs as si
     res = {}
-    flush = torch.zeros(128 * 1024 * 1024, dtype=torch.float32, device="cuda")
+    flush = CacheFlush(torch)
     for name, d in (("1024x4096", si.pf_step()), ("16x1024", si.pf_small())):
         t = {k: torch.from_numpy(d[k]).cuda() for k in ("x", "lw", "obs", "A", "C", "eps",
                                                          "u_row")}

@@ -141,7 +141,8 @@ psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_
  * (q_min / q_i)^beta (integer mode), with w_min the smallest sampled weight.
  *   prio   : the n priorities the CDF was built from (F32 or U32).
  *   idx    : k indices from psamp_sample (clamped into [0, n) on use).
- *   out_w  : k float weights in (0, 1]; the largest is exactly 1.
+ *   out_w  : k float weights in (0, 1]; the largest is exactly 1.  Must not
+ *            overlap prio (large batches park the gathered priorities there).
  *   ws     : psamp_is_weights_workspace_size(k) bytes (may be 0 bytes and
  *            NULL when that size is 0).
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (beta < 0 or not finite,

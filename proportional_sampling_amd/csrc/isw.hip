@@ -10,8 +10,9 @@
 // largest weight comes out as exactly 1.
 //
 // Small batches (k <= 8192) run in one 1024-thread workgroup.  Larger ones
-// use two kernels: per-block minima with a last-block reduction, then the
-// weights.
+// use two kernels: per-block minima with a last-block reduction (the
+// gathered priorities are parked in the output array), then the weights
+// from the parked values -- the priority array is gathered once.
 #include "psamp_device.h"
 #include "psamp_host.h"
 
@@ -83,11 +84,13 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_single(const P* __restrict_
 }
 
 // Pass 1: per-block minimum; the last block to finish reduces them into
-// hdr[1] and rearms the block counter hdr[0] for the next call.
+// hdr[1] and rearms the block counter hdr[0] for the next call.  Each
+// gathered priority's bits are parked in out[i] for pass 2.
 template <class P>
 __global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ prio, int64_t n,
                                                          const int32_t* __restrict__ idx, int64_t k,
-                                                         uint32_t* __restrict__ ws, int nblocks) {
+                                                         uint32_t* __restrict__ ws, int nblocks,
+                                                         uint32_t* __restrict__ park) {
     __shared__ uint32_t s_min;
     __shared__ int s_last;
     const int tid = threadIdx.x;
@@ -98,7 +101,11 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ p
 #pragma unroll
     for (int j = 0; j < kIswPerThread; ++j) {
         const int64_t i = b0 + j * kIswThreads + tid;
-        if (i < k) mn = min_(mn, prio_key<P>(prio[clamp_idx(idx[i], n)]));
+        if (i < k) {
+            const uint32_t key = prio_key<P>(prio[clamp_idx(idx[i], n)]);
+            park[i] = key;
+            mn = min_(mn, key);
+        }
     }
     atomicMin(&s_min, mn);
     __syncthreads();
@@ -125,10 +132,11 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ p
     }
 }
 
+// Pass 2: the weights from the parked priorities (read and overwritten in
+// place, each by its own thread).
 template <class P>
-__global__ __launch_bounds__(kIswThreads) void k_isw_apply(const P* __restrict__ prio, int64_t n,
-                                                           const int32_t* __restrict__ idx, int64_t k,
-                                                           double e, const uint32_t* __restrict__ ws,
+__global__ __launch_bounds__(kIswThreads) void k_isw_apply(int64_t k, double e,
+                                                           const uint32_t* __restrict__ ws,
                                                            float* __restrict__ out) {
     __shared__ MathLds M;
     const int tid = threadIdx.x;
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_apply(const P* __restrict__
     for (int j = 0; j < kIswPerThread; ++j) {
         const int64_t i = b0 + j * kIswThreads + tid;
         if (i < k) {
-            const double p = prio_val<P>(prio_key<P>(prio[clamp_idx(idx[i], n)]));
+            const double p = prio_val<P>(__float_as_uint(out[i]));
             out[i] = is_weight(pmin, lpmin, p, e, &M);
         }
     }
@@ -159,11 +167,11 @@ static psamp_status launch_isw(const void* prio, int64_t n, const int32_t* idx, 
     const int nb = (int)ceil_div(k, kIswBlock);
     if (trace_enabled()) trace_launch("k_isw_min+apply", nb, kIswThreads, k);
     hipLaunchKernelGGL(k_isw_min<P>, dim3(nb), dim3(kIswThreads), 0, st, (const P*)prio, n, idx, k,
-                       (uint32_t*)ws, nb);
+                       (uint32_t*)ws, nb, reinterpret_cast<uint32_t*>(out));
     psamp_status s = launch_status();
     if (s != PSAMP_OK) return s;
-    hipLaunchKernelGGL(k_isw_apply<P>, dim3(nb), dim3(kIswThreads), 0, st, (const P*)prio, n, idx,
-                       k, e, (const uint32_t*)ws, out);
+    hipLaunchKernelGGL(k_isw_apply<P>, dim3(nb), dim3(kIswThreads), 0, st, k, e,
+                       (const uint32_t*)ws, out);
     return launch_status();
 }
 
