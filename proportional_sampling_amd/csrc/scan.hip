@@ -62,7 +62,8 @@ struct SampleArgs {
 
 // One workgroup per tile, tiles in blockIdx order.  VEC: see load_tile.
 // SAMPLE: every tile sum and group total and T are already published (by
-// k_tile_sums), so the lookback does not wait; the tile then draws its own
+// k_tile_sums, which also advanced the call counter), so the lookback's
+// words are fetched up front and never waited for; the tile then draws its own
 // stratified samples -- the thresholds in (excl_j, excl_{j+1}] -- from an
 // LDS copy of its CDF values.
 template <int IPT, bool VEC, class In, class Out, bool SAMPLE = false>
@@ -111,8 +112,15 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     const uint64_t t1_w = SAMPLE ? load_agent(&ws[kHdrT + 1]) : 0;
     if (kFp) math_store(&M, tid, mr);
     __syncthreads();
-    const uint32_t calls = (uint32_t)calls_w;
+    // SAMPLE: k_tile_sums has already advanced the call counter, so this
+    // call's parity is that of calls - 1; every sum is published, so wave 0
+    // fetches its lookback words now, behind the tile's own loads
+    const uint32_t calls = SAMPLE ? (uint32_t)calls_w - 1u : (uint32_t)calls_w;
     const int par = (int)(calls & 1u);
+    uint64_t pre[kLbGtWords + 2];
+    if constexpr (SAMPLE) {
+        if (wave == 0) lb_preload(tile, par, ws, pre);
+    }
 
     // ---- weights and the thread-local prefix of each row
     // (Each row's values are pinned where they are formed: left to itself
@@ -143,7 +151,7 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     if (tid == 0) store_agent(&ws[a_off((uint32_t)tile, par)], status_enc(A));
     tile_local_values<R, Acc>(q, X, s_wmax);
     if (wave == 0)
-        lookback<Acc>(tile, n_tiles, par, A, ws, calls, s_excl);
+        lookback<Acc, SAMPLE>(tile, n_tiles, par, A, ws, calls, s_excl, pre);
     else
         clear_other_parity(ws, par, n_tiles, max_slots, hw_w, tid - kWave, kScanThreads - kWave);
     __syncthreads();
@@ -225,12 +233,13 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     }
 }
 
-// The first pass of the fused scan + sample: the tile sums A_j (the same
+// The first pass of a reduce-then-scan: the tile sums A_j (the same
 // arithmetic as the scan's), published in the scan's status words.  Tiles
 // count per group of 64 (the group's MIN words of this parity serve as the
 // counters; the next call zeroes them): the tile that completes a group
 // publishes its total GT_g, and the group that completes last forms T with
-// the scan's association and publishes it.  One counter per group keeps the
+// the scan's association, publishes it and advances the call counter (every
+// tile has read it by then: each counted itself in after reading it).  One counter per group keeps the
 // atomics on 64-tile-wide addresses apart instead of serialising all tiles
 // on one word.
 template <int IPT, bool VEC, class In>
@@ -322,6 +331,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_sums(const In* __restrict
     if (lane == 0) {
         store_agent(&ws[kHdrT + par], status_enc(T));
         store_agent(&ws[kHdrExit], 0);
+        store_agent(&ws[kHdrCalls], (uint64_t)((uint32_t)calls_w + 1u));
     }
 }
 

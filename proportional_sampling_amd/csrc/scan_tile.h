@@ -206,20 +206,61 @@ __device__ __forceinline__ Acc status_value(uint64_t w) {
     return x;
 }
 
+// The words of the first lookback round of a tile (see lookback): A of
+// every tile of the previous group (slot 0), A of the earlier tiles of its
+// own group (slot 1), the published totals GT_h of groups h < g - 1, 64 per
+// slot (slots 2..).  Words not needed are marked so.
+__device__ __forceinline__ void lb_round(int tile, int par, int s0, uint32_t (&off)[kLbGtWords + 2],
+                                         bool (&need)[kLbGtWords + 2]) {
+    const int lane = threadIdx.x & 63;
+    const int g = tile / kScanGroup;
+    const int cnt = tile - g * kScanGroup;
+    const int gp = g > 0 ? g - 1 : 0;
+    const bool first = s0 == 0;
+    need[0] = first && g > 0;
+    off[0] = a_off((uint32_t)(gp * kScanGroup + lane), par);
+    need[1] = first && lane < cnt;
+    off[1] = a_off((uint32_t)(g * kScanGroup + lane), par);
+#pragma unroll
+    for (int i = 0; i < kLbGtWords; ++i) {
+        const int h = (s0 + i) * kWave + lane;
+        need[i + 2] = h < g - 1;
+        off[i + 2] = gt_off((uint32_t)(need[i + 2] ? h : 0), par);
+    }
+}
+
+// Issues the loads of the first lookback round ahead of time (wave 0, when
+// every sum is known to be published already: the second pass of a
+// reduce-then-scan); lookback<Acc, true> then uses them instead of polling.
+__device__ __forceinline__ void lb_preload(int tile, int par, const uint64_t* ws,
+                                           uint64_t (&pre)[kLbGtWords + 2]) {
+    uint32_t off[kLbGtWords + 2];
+    bool need[kLbGtWords + 2];
+    lb_round(tile, par, 0, off, need);
+#pragma unroll
+    for (int i = 0; i < kLbGtWords + 2; ++i) pre[i] = load_agent(&ws[need[i] ? off[i] : kHdrDummy]);
+}
+
 // Lookback of one tile, called by wave 0 after the tile published its sum
 // A.  Reads A of the earlier tiles of its group and of the whole previous
 // group, and the published totals GT_h of the groups h < g - 1, all in one
 // round trip (more only past 64 * kLbGtWords groups); forms P_j, P_{j+1},
 // GT_{g-1} and the two Outer trees of the header comment.  Writes excl_j to
 // s_excl[0] and excl_{j+1} to s_excl[1].  The tile that ends a group
-// publishes GT_g; the last tile advances the call counter.
-template <class Acc>
+// publishes GT_g; the last tile advances the call counter -- by then every
+// workgroup has read it, since the last tile's lookback needs every tile's
+// sum.  PRE: the first round's words were loaded by lb_preload; they are
+// used if every needed one is there (otherwise the round polls as usual).
+// A PRE lookback does not advance the counter: its tiles' sums were
+// published by an earlier kernel, so the last tile can finish before other
+// workgroups have even started (the earlier kernel advances it instead).
+template <class Acc, bool PRE = false>
 __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, uint64_t* ws,
-                                         uint32_t calls, Acc* s_excl) {
+                                         uint32_t calls, Acc* s_excl,
+                                         const uint64_t* pre = nullptr) {
     const int lane = threadIdx.x & 63;
     const int g = tile / kScanGroup;
     const int cnt = tile - g * kScanGroup;
-    const int gp = g > 0 ? g - 1 : 0;
     Acc base = Acc(0);     // this lane's published leaves h < g - 1, in slot order
     Acc P = Acc(0), Pn = Acc(0), Gp = Acc(0);
 #pragma nounroll
@@ -228,17 +269,20 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
         uint32_t off[kLbGtWords + 2];
         bool need[kLbGtWords + 2];
         uint64_t w[kLbGtWords + 2];
-        need[0] = first && g > 0;
-        off[0] = a_off((uint32_t)(gp * kScanGroup + lane), par);
-        need[1] = first && lane < cnt;
-        off[1] = a_off((uint32_t)(g * kScanGroup + lane), par);
+        lb_round(tile, par, s0, off, need);
+        bool have = false;
+        if constexpr (PRE) {
+            if (first) {
+                bool miss = false;
 #pragma unroll
-        for (int i = 0; i < kLbGtWords; ++i) {
-            const int h = (s0 + i) * kWave + lane;
-            need[i + 2] = h < g - 1;
-            off[i + 2] = gt_off((uint32_t)(need[i + 2] ? h : 0), par);
+                for (int i = 0; i < kLbGtWords + 2; ++i) {
+                    w[i] = pre[i];
+                    miss = miss || (need[i] && w[i] == 0);
+                }
+                have = !__any(miss);
+            }
         }
-        wait_words<kLbGtWords + 2>(ws, off, need, w);
+        if (!have) wait_words<kLbGtWords + 2>(ws, off, need, w);
         if (first) {
             const Acc a = need[1] ? status_value<Acc>(w[1]) : Acc(0);
             P = wave_sum(a);
@@ -259,7 +303,7 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
     if (lane == 0) {
         s_excl[0] = excl;
         s_excl[1] = next;
-        if (tile == n_tiles - 1) store_agent(&ws[kHdrCalls], (uint64_t)(calls + 1u));
+        if (!PRE && tile == n_tiles - 1) store_agent(&ws[kHdrCalls], (uint64_t)(calls + 1u));
     }
 }
 

@@ -414,3 +414,32 @@ def test_build_cdf_sample_per_large(ps):
     idx_i, _, _ = ps.build_cdf_sample(Q, R)
     _, _, _, idx_o = oracle.sample_int(di["q"], di["r"], True)
     assert np.array_equal(host(idx_i), idx_o)
+
+
+@pytest.mark.parametrize("mode", ["fp", "int"])
+def test_build_cdf_sample_mixed_calls_one_workspace(ps, mode):
+    """The fused call and the plain scan alternate on one workspace at 2^24
+    (2048 tiles: more workgroups than fit at once), six calls: the parity
+    stays in step (each result equals a fresh-workspace reference and no
+    bounded wait runs out).  A regression test: the second pass must not
+    advance the call counter itself, since its last tile can finish before
+    other workgroups have started."""
+    n, k = 1 << 24, 1 << 16
+    rng = np.random.default_rng(11)
+    if mode == "fp":
+        p, u, alpha = si.generic_f32(n, 12, "lognormal"), si.uniform_f32(rng, k), 0.7
+    else:
+        p = rng.integers(1, 1 << 20, n, dtype=np.uint32)
+        u, alpha = si.uniform_u32(rng, k), 1.0
+    P, Ud = dev(p), dev(u)
+    c_ref, t_ref = ps.build_cdf(P, alpha)
+    i_ref = ps.sample(c_ref, t_ref, Ud, stratified=True)
+    ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+    for rep in range(6):
+        if rep % 2 == 0:
+            idx, cdf, tot = ps.build_cdf_sample(P, Ud, alpha, ws=ws)
+            assert torch.equal(idx, i_ref), f"rep {rep}: indices"
+        else:
+            cdf, tot = ps.build_cdf(P, alpha, ws=ws)
+        assert torch.equal(cdf, c_ref) and torch.equal(tot, t_ref), f"rep {rep}"
+    assert ws.errors() == 0
