@@ -63,6 +63,29 @@ def test_scan_fp(ps, n):
     assert ws.errors() == 0
 
 
+def test_scan_many_groups(ps):
+    """2^27 + 12345 elements: 16386 tiles in 257 groups of 64, more than one
+    lookback round (128 group totals per round) -- integer mode bit for bit,
+    fp within the tolerance, T = C_{n-1}."""
+    n = (1 << 27) + 12345
+    say(f"scan int+fp n={n}")
+    q = si.sweep_u32(n)
+    C_o, T_o = oracle.build_cdf_int(q)
+    cdf, tot = ps.build_cdf(dev(q))
+    assert np.array_equal(host(cdf), C_o)
+    assert int(host(tot)[0]) == T_o
+    del cdf, C_o, q
+    p = si.sweep_f32(n)
+    C_o, T_o = oracle.build_cdf(p, 0.7)
+    cdf, tot = ps.build_cdf(dev(p), 0.7)
+    C_g = host(cdf)
+    e = rel_err(C_g, C_o)
+    say(f"  max rel CDF err {e:.3e}")
+    assert e <= 1e-12
+    assert np.all(np.diff(C_g) >= 0)
+    assert host(tot)[0] == C_g[-1]
+
+
 def test_scan_all_ones_exact(ps):
     n = (1 << 21) + 5
     cdf, tot = ps.build_cdf(torch.ones(n, dtype=torch.float32, device="cuda"), 0.6)
