@@ -33,8 +33,9 @@ namespace psamp {
 constexpr int kULds = 8192;   // k up to this: the thresholds' fractions are staged in LDS
 
 // UL: U (k <= kULds values) is copied to LDS at the start, so locating and
-// searching the draws touches no global memory.  VEC: see load_tile.
-template <int R, bool UL, bool VEC>
+// searching the draws touches no global memory.  VEC: see load_tile.  FAST:
+// p^alpha from per-workgroup tables, as the scan does on the same tiles.
+template <int R, bool UL, bool VEC, bool FAST = false>
 __global__ __launch_bounds__(kScanThreads) void k_per_round(
     float* __restrict__ prio, int64_t n, double alpha, double ab, const float* __restrict__ U,
     int64_t k, const float* __restrict__ newp, int32_t* __restrict__ out_idx,
@@ -44,6 +45,7 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     constexpr int TILE = ROW * R;
 
     __shared__ MathLds M;
+    __shared__ PowLds PL;
     __shared__ double s_wtot[4][R];
     __shared__ double s_wmax[4][R];
     __shared__ double s_lb[3];
@@ -67,15 +69,26 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     // (The priorities go first: the counter words are made uniform, which
     // makes the compiler wait for them where they are loaded.)
     float v[R][4];
+    MathRegs mr;
+    if constexpr (FAST) {
+        mr = math_load(tid);
+        asm volatile("" ::: "memory");
+    }
     load_tile<R, VEC, float>(prio + base, tlen, v);
     asm volatile("" ::: "memory");
-    const MathRegs mr = math_load(tid);
+    if constexpr (!FAST) mr = math_load(tid);
     const uint64_t calls_w = load_agent(&ws[kHdrCalls]);
     const uint64_t hw_w = load_agent(&ws[kHdrHw]);
     math_store(&M, tid, mr);
     if (tid == 0) s_min = 0xFFFFFFFFu;
     const float* Us = UL ? s_U : U;
     __syncthreads();
+    PowCoef pc;
+    if constexpr (FAST) {
+        pow_tables_build(&PL, &M, alpha, tid, kScanThreads);
+        pc = pow_coef(alpha);
+        __syncthreads();
+    }
     const uint32_t calls = (uint32_t)calls_w;
     const int par = (int)(calls & 1u);
 
@@ -85,7 +98,9 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const double w = pow_prio(v[r][c], alpha, &M);
+            double w;
+            if constexpr (FAST) w = pow_prio_fast(v[r][c], &PL, pc);
+            else w = pow_prio(v[r][c], alpha, &M);
             q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
             s_p[r * ROW + 4 * tid + c] = v[r][c];
         }
@@ -263,13 +278,14 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     }
 }
 
-template <int R, bool UL>
+template <int R, bool UL, bool FAST>
 static int per_round_capacity() {
     // VEC does not change the resources.
-    return resident_grid(reinterpret_cast<const void*>(&k_per_round<R, UL, true>), kScanThreads);
+    return resident_grid(reinterpret_cast<const void*>(&k_per_round<R, UL, true, FAST>),
+                         kScanThreads);
 }
 
-template <int R, bool UL>
+template <int R, bool UL, bool FAST>
 static psamp_status launch_per_round(void* prio, int64_t n, double alpha, double ab,
                                      const float* u, int64_t k, const float* newp,
                                      int32_t* out_idx, float* out_w, double* cdf, double* total,
@@ -277,11 +293,11 @@ static psamp_status launch_per_round(void* prio, int64_t n, double alpha, double
     const int tiles = (int)ceil_div(n, kScanThreads * 4 * R);
     if (trace_enabled()) trace_launch("k_per_round", tiles, kScanThreads, n);
     if (aligned(prio, 16) && n % 4 == 0)
-        hipLaunchKernelGGL((k_per_round<R, UL, true>), dim3(tiles), dim3(kScanThreads), 0, st,
+        hipLaunchKernelGGL((k_per_round<R, UL, true, FAST>), dim3(tiles), dim3(kScanThreads), 0, st,
                            (float*)prio, n, alpha, ab, u, k, newp, out_idx, out_w, cdf, total,
                            (uint64_t*)ws, tiles, max_slots, vec_ok);
     else
-        hipLaunchKernelGGL((k_per_round<R, UL, false>), dim3(tiles), dim3(kScanThreads), 0, st,
+        hipLaunchKernelGGL((k_per_round<R, UL, false, FAST>), dim3(tiles), dim3(kScanThreads), 0, st,
                            (float*)prio, n, alpha, ab, u, k, newp, out_idx, out_w, cdf, total,
                            (uint64_t*)ws, tiles, max_slots, vec_ok);
     return launch_status();
@@ -319,15 +335,21 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
     if (k > 0) {
         // The scan's own tiling (so the CDF is the same bits as psamp_build_cdf's);
         // U in LDS when it fits and the grid still is resident.
-#define PSAMP_PER_ROUND_TRY(RR, UU)                                                             \
-    if (ceil_div(n, kScanThreads * 4 * RR) <= per_round_capacity<RR, UU>())                    \
-        return launch_per_round<RR, UU>(prio, n, alpha, alpha * beta, u, k, new_prio, out_idx, \
-                                        out_w, cdf, total, ws, max_slots, vec_ok, st);
+#define PSAMP_PER_ROUND_TRY(RR, UU, FF)                                                     \
+    if (ceil_div(n, kScanThreads * 4 * RR) <= per_round_capacity<RR, UU, FF>())            \
+        return launch_per_round<RR, UU, FF>(prio, n, alpha, alpha * beta, u, k, new_prio,  \
+                                            out_idx, out_w, cdf, total, ws, max_slots,     \
+                                            vec_ok, st);
         if (scan_rows_for(n) == 1) {
-            if (k <= kULds) PSAMP_PER_ROUND_TRY(1, true)
-            PSAMP_PER_ROUND_TRY(1, false)
+            if (k <= kULds) PSAMP_PER_ROUND_TRY(1, true, false)
+            PSAMP_PER_ROUND_TRY(1, false, false)
         } else {
-            PSAMP_PER_ROUND_TRY(8, false)
+            // the scan's pow on these tiles (same bits as psamp_build_cdf)
+            if (alpha <= kFastPowMaxAlpha) {
+                PSAMP_PER_ROUND_TRY(8, false, true)
+            } else {
+                PSAMP_PER_ROUND_TRY(8, false, false)
+            }
         }
 #undef PSAMP_PER_ROUND_TRY
     }

@@ -224,6 +224,84 @@ __device__ __forceinline__ double pow_prio(float p, double alpha, const MathLds*
     return fin ? r : sp;
 }
 
+// p^alpha with per-workgroup tables for one alpha (large tiles).  A float
+// p > 0 is 2^e m with m in [1, 2) and e in [-149, 127] (subnormals
+// normalised by the conversion to double); k = the top 7 fraction bits of m
+// and c_k the table's 21-bit reciprocal, so r = m c_k - 1 is exact and
+// |r| < 2^-8 + 2^-21.  Then p^alpha = 2^(alpha e) * c_k^(-alpha) * (1 + r)^alpha
+// with the first two factors from the tables and (1 + r)^alpha from the
+// binomial series to r^7 (truncation below 7e-16 relative for alpha <= 16).
+// Tables, formed once per workgroup with pow_prio's own log2 / exp2:
+// gk[k] = (c_k, c_k^(-alpha)), ex[e + 149] = 2^(alpha e) (alpha e split
+// exactly into a rounded part and its remainder).  About 10 fp64 operations
+// per element instead of ~27, and no rounding of alpha log2(p) (the main
+// error of pow_prio, up to ~1e-14 relative): ~5e-16 relative.
+constexpr double kFastPowMaxAlpha = 16.0;
+constexpr int kPowExpMin = -149;
+constexpr int kPowExpCount = 277;                 // e in [-149, 127]
+
+struct PowLds {
+    double2 gk[128];
+    double ex[kPowExpCount];
+};
+
+struct PowCoef {
+    double b[8];                                  // b[i] = binomial(alpha, i), i = 1..7
+};
+
+__device__ __forceinline__ PowCoef pow_coef(double alpha) {
+    PowCoef c;
+    c.b[0] = 1.0;
+    c.b[1] = alpha;
+    const double inv[8] = {0.0, 1.0, 0.5, 1.0 / 3.0, 0.25, 0.2, 1.0 / 6.0, 1.0 / 7.0};
+#pragma unroll
+    for (int i = 2; i < 8; ++i) c.b[i] = c.b[i - 1] * (alpha - (double)(i - 1)) * inv[i];
+    return c;
+}
+
+// Every thread of the workgroup takes part; M must be filled and visible.
+// A barrier must follow before the tables are read.
+__device__ __forceinline__ void pow_tables_build(PowLds* P, const MathLds* M, double alpha,
+                                                 int tid, int nthreads) {
+    for (int i = tid; i < 128 + kPowExpCount; i += nthreads) {
+        if (i < 128) {
+            const double2 ct = M->log_tab[i];           // (c_k, -log2 c_k)
+            P->gk[i] = make_double2(ct.x, exp2_tab(alpha * ct.y, M));
+        } else {
+            const double e = (double)(i - 128 + kPowExpMin);
+            const double hi = alpha * e;
+            const double lo = fma(alpha, e, -hi);         // alpha e = hi + lo exactly
+            const double E = exp2_tab(hi, M);
+            P->ex[i - 128] = fma(E, lo * kLn2, E);        // 2^lo = 1 + lo ln2 (|lo| <= 2^-41)
+        }
+    }
+}
+
+__device__ __forceinline__ double pow_prio_fast(float p, const PowLds* P, const PowCoef& c) {
+    const float inf = __int_as_float(0x7F800000);
+    const bool fin = p > 0.0f && p < inf;
+    const double d = (double)(fin ? p : 1.0f);
+    const uint32_t hi = (uint32_t)__double2hiint(d);
+    const int e = (int)(hi >> 20) - 1023;
+    const int k = (int)(hi >> 13) & 127;
+    const double m = __hiloint2double((int)((hi & 0x000FFFFFu) | 0x3FF00000u), __double2loint(d));
+    const double2 g = P->gk[k];
+    const double E = P->ex[e - kPowExpMin];
+    const double r = fma(m, g.x, -1.0);
+    double s = fma(c.b[7], r, c.b[6]);
+    s = fma(s, r, c.b[5]);
+    s = fma(s, r, c.b[4]);
+    s = fma(s, r, c.b[3]);
+    s = fma(s, r, c.b[2]);
+    s = fma(s, r, c.b[1]);
+    const double t = r * s;                              // (1 + r)^alpha - 1
+    const double ge = g.y * E;
+    const double w = fma(ge, t, ge);
+    const uint32_t sp_hi = (p == 0.0f) ? 0u : (p == inf) ? 0x7FF00000u : 0x7FF80000u;
+    const double sp = __hiloint2double((int)sp_hi, 0);
+    return fin ? w : sp;
+}
+
 // e^x for a finite double x (the particle weights).
 __device__ __forceinline__ double exp_d(double x, const MathLds* M) {
     return exp2_tab(x * kLog2e, M);

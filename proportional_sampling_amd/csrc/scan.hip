@@ -66,7 +66,9 @@ struct SampleArgs {
 // words are fetched up front and never waited for; the tile then draws its own
 // stratified samples -- the thresholds in (excl_j, excl_{j+1}] -- from an
 // LDS copy of its CDF values.
-template <int IPT, bool VEC, class In, class Out, bool SAMPLE = false>
+// FAST (fp mode, 8-row tiles, alpha <= kFastPowMaxAlpha): p^alpha from
+// per-workgroup tables (pow_prio_fast), built while the tile's loads travel.
+template <int IPT, bool VEC, class In, class Out, bool SAMPLE = false, bool FAST = false>
 __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     const In* __restrict__ in, int64_t n, double alpha, Out* __restrict__ cdf,
     Out* __restrict__ total, uint64_t* __restrict__ ws, int n_tiles,
@@ -77,7 +79,9 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     constexpr int ROW = kScanThreads * 4;         // elements per row
     constexpr int TILE = ROW * R;
 
+    static_assert(!FAST || std::is_same<In, float>::value, "FAST is for fp mode");
     __shared__ MathLds M;
+    __shared__ PowLds PL;
     __shared__ Acc s_wtot[4][R];
     __shared__ double s_wmax[4][R];
     __shared__ Acc s_excl[2];
@@ -98,12 +102,18 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     // has read it.  All first loads (counter, high-water mark, pow tables,
     // priorities) are issued together, so their latencies overlap.
     // (The priorities go first: the counter words are made uniform, which
-    // makes the compiler wait for them where they are loaded.)
+    // makes the compiler wait for them where they are loaded.  FAST: the
+    // small pow tables go first instead, so the per-workgroup tables can be
+    // built while the priorities are on their way.)
     In v[R][4];
+    MathRegs mr;
+    if constexpr (FAST) {
+        mr = math_load(tid);
+        asm volatile("" ::: "memory");
+    }
     load_tile<R, VEC, In>(in + base, tlen, v);
     asm volatile("" ::: "memory");
-    MathRegs mr;
-    if (kFp) mr = math_load(tid);
+    if (kFp && !FAST) mr = math_load(tid);
     const uint64_t calls_w = load_agent(&ws[kHdrCalls]);
     const uint64_t hw_w = load_agent(&ws[kHdrHw]);
     // SAMPLE: T is already published (parity of this call); its word goes
@@ -112,6 +122,12 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     const uint64_t t1_w = SAMPLE ? load_agent(&ws[kHdrT + 1]) : 0;
     if (kFp) math_store(&M, tid, mr);
     __syncthreads();
+    PowCoef pc;
+    if constexpr (FAST) {
+        pow_tables_build(&PL, &M, alpha, tid, kScanThreads);
+        pc = pow_coef(alpha);
+        __syncthreads();
+    }
     // SAMPLE: k_tile_sums has already advanced the call counter, so this
     // call's parity is that of calls - 1; every sum is published, so wave 0
     // fetches its lookback words now, behind the tile's own loads
@@ -131,7 +147,9 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const Acc w = to_weight(v[r][c], alpha, &M);
+            Acc w;
+            if constexpr (FAST) w = pow_prio_fast(v[r][c], &PL, pc);
+            else w = to_weight(v[r][c], alpha, &M);
             q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
         }
         if constexpr (kFp) {
@@ -242,7 +260,7 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
 // tile has read it by then: each counted itself in after reading it).  One counter per group keeps the
 // atomics on 64-tile-wide addresses apart instead of serialising all tiles
 // on one word.
-template <int IPT, bool VEC, class In>
+template <int IPT, bool VEC, class In, bool FAST = false>
 __global__ __launch_bounds__(kScanThreads) void k_tile_sums(const In* __restrict__ in, int64_t n,
                                                             double alpha,
                                                             uint64_t* __restrict__ ws,
@@ -253,6 +271,7 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_sums(const In* __restrict
     constexpr int TILE = kScanThreads * 4 * R;
 
     __shared__ MathLds M;
+    __shared__ PowLds PL;
     __shared__ Acc s_wtot[4][R];
     __shared__ int s_role;
 
@@ -266,13 +285,23 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_sums(const In* __restrict
     const int tlen = (int)min_<int64_t>(TILE, n - base);
 
     In v[R][4];
+    MathRegs mr;
+    if constexpr (FAST) {
+        mr = math_load(tid);
+        asm volatile("" ::: "memory");
+    }
     load_tile<R, VEC, In>(in + base, tlen, v);
     asm volatile("" ::: "memory");
-    MathRegs mr;
-    if (kFp) mr = math_load(tid);
+    if (kFp && !FAST) mr = math_load(tid);
     const uint64_t calls_w = load_agent(&ws[kHdrCalls]);
     if (kFp) math_store(&M, tid, mr);
     __syncthreads();
+    PowCoef pc;
+    if constexpr (FAST) {
+        pow_tables_build(&PL, &M, alpha, tid, kScanThreads);
+        pc = pow_coef(alpha);
+        __syncthreads();
+    }
     const int par = (int)(calls_w & 1u);
 
     Acc q[R][4];
@@ -280,7 +309,9 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_sums(const In* __restrict
     for (int r = 0; r < R; ++r) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const Acc w = to_weight(v[r][c], alpha, &M);
+            Acc w;
+            if constexpr (FAST) w = pow_prio_fast(v[r][c], &PL, pc);
+            else w = to_weight(v[r][c], alpha, &M);
             q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
         }
         if constexpr (kFp) {
@@ -335,21 +366,40 @@ __global__ __launch_bounds__(kScanThreads) void k_tile_sums(const In* __restrict
     }
 }
 
-template <int IPT, class In, class Out>
-static psamp_status launch_scan(const void* prio, int64_t n, double alpha, void* cdf, void* total,
-                                void* ws, uint64_t max_slots, int vec_ok, hipStream_t st) {
+// The table-driven pow for fp mode on 8-row tiles when alpha allows it.
+template <int IPT, class In>
+static bool use_fast_pow(double alpha) {
+    return IPT == 32 && std::is_same<In, float>::value && alpha <= kFastPowMaxAlpha;
+}
+
+template <int IPT, class In, class Out, bool FAST>
+static psamp_status launch_scan_t(const void* prio, int64_t n, double alpha, void* cdf,
+                                  void* total, void* ws, uint64_t max_slots, int vec_ok,
+                                  hipStream_t st) {
     const int tiles = (int)ceil_div(n, kScanThreads * IPT);
     if (trace_enabled()) trace_launch("k_build_cdf", tiles, kScanThreads, n);
     const bool vec_in = aligned(prio, 16) && n % 4 == 0;
     if (vec_in)
-        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Out>), dim3(tiles), dim3(kScanThreads), 0,
-                           st, (const In*)prio, n, alpha, (Out*)cdf, (Out*)total, (uint64_t*)ws,
-                           tiles, max_slots, vec_ok, SampleArgs{});
+        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Out, false, FAST>), dim3(tiles),
+                           dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Out*)cdf,
+                           (Out*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, SampleArgs{});
     else
-        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Out>), dim3(tiles), dim3(kScanThreads), 0,
-                           st, (const In*)prio, n, alpha, (Out*)cdf, (Out*)total, (uint64_t*)ws,
-                           tiles, max_slots, vec_ok, SampleArgs{});
+        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Out, false, FAST>), dim3(tiles),
+                           dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Out*)cdf,
+                           (Out*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, SampleArgs{});
     return launch_status();
+}
+
+template <int IPT, class In, class Out>
+static psamp_status launch_scan(const void* prio, int64_t n, double alpha, void* cdf, void* total,
+                                void* ws, uint64_t max_slots, int vec_ok, hipStream_t st) {
+    if constexpr (IPT == 32 && std::is_same<In, float>::value) {
+        if (use_fast_pow<IPT, In>(alpha))
+            return launch_scan_t<IPT, In, Out, true>(prio, n, alpha, cdf, total, ws, max_slots,
+                                                     vec_ok, st);
+    }
+    return launch_scan_t<IPT, In, Out, false>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok,
+                                              st);
 }
 
 template <class In, class Out>
@@ -364,28 +414,41 @@ static psamp_status launch_build_cdf(const void* prio, int64_t n, double alpha, 
 
 // The fused scan + stratified sample: k_tile_sums, then the scan with
 // SAMPLE.  CDF, T and indices are the bits of psamp_build_cdf + psamp_sample.
-template <int IPT, class In>
-static psamp_status launch_scan_sample(const void* prio, int64_t n, double alpha, void* cdf,
-                                       void* total, void* ws, uint64_t max_slots, int vec_ok,
-                                       SampleArgs sa, hipStream_t st) {
+template <int IPT, class In, bool FAST>
+static psamp_status launch_scan_sample_t(const void* prio, int64_t n, double alpha, void* cdf,
+                                         void* total, void* ws, uint64_t max_slots, int vec_ok,
+                                         SampleArgs sa, hipStream_t st) {
     using Acc = typename ScanAcc<In>::type;
     const int tiles = (int)ceil_div(n, kScanThreads * IPT);
     if (trace_enabled()) trace_launch("k_tile_sums+k_build_cdf<sample>", tiles, kScanThreads, n);
     const bool vec_in = aligned(prio, 16) && n % 4 == 0;
     if (vec_in) {
-        hipLaunchKernelGGL((k_tile_sums<IPT, true, In>), dim3(tiles), dim3(kScanThreads), 0, st,
-                           (const In*)prio, n, alpha, (uint64_t*)ws, tiles);
-        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Acc, true>), dim3(tiles),
+        hipLaunchKernelGGL((k_tile_sums<IPT, true, In, FAST>), dim3(tiles), dim3(kScanThreads), 0,
+                           st, (const In*)prio, n, alpha, (uint64_t*)ws, tiles);
+        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Acc, true, FAST>), dim3(tiles),
                            dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Acc*)cdf,
                            (Acc*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, sa);
     } else {
-        hipLaunchKernelGGL((k_tile_sums<IPT, false, In>), dim3(tiles), dim3(kScanThreads), 0, st,
-                           (const In*)prio, n, alpha, (uint64_t*)ws, tiles);
-        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Acc, true>), dim3(tiles),
+        hipLaunchKernelGGL((k_tile_sums<IPT, false, In, FAST>), dim3(tiles), dim3(kScanThreads), 0,
+                           st, (const In*)prio, n, alpha, (uint64_t*)ws, tiles);
+        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Acc, true, FAST>), dim3(tiles),
                            dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Acc*)cdf,
                            (Acc*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, sa);
     }
     return launch_status();
+}
+
+template <int IPT, class In>
+static psamp_status launch_scan_sample(const void* prio, int64_t n, double alpha, void* cdf,
+                                       void* total, void* ws, uint64_t max_slots, int vec_ok,
+                                       SampleArgs sa, hipStream_t st) {
+    if constexpr (IPT == 32 && std::is_same<In, float>::value) {
+        if (use_fast_pow<IPT, In>(alpha))
+            return launch_scan_sample_t<IPT, In, true>(prio, n, alpha, cdf, total, ws, max_slots,
+                                                       vec_ok, sa, st);
+    }
+    return launch_scan_sample_t<IPT, In, false>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok,
+                                                sa, st);
 }
 
 }  // namespace psamp

@@ -86,6 +86,34 @@ def test_scan_many_groups(ps):
     assert host(tot)[0] == C_g[-1]
 
 
+@pytest.mark.parametrize("alpha", [0.05, 0.6, 1.0, 2.0, 7.5, 16.0, 17.0])
+def test_scan_pow_extremes_large_tiles(ps, alpha):
+    """8-row tiles (n > 2^20), where p^alpha comes from per-workgroup tables
+    for alpha <= 16 (17 takes the general pow): subnormal, tiny, huge, zero
+    and unit priorities.  The first 4096 elements are all tiny, so the CDF
+    there checks the relative accuracy of small weights; the rest spans the
+    whole float range alpha allows without overflow."""
+    n = (1 << 20) + 1000
+    rng = np.random.default_rng(int(alpha * 100))
+    hi = min(38.0, 300.0 / alpha)
+    lo = max(-44.5, -300.0 / alpha)
+    e = rng.uniform(lo, hi, n)
+    e[:4096] = rng.uniform(lo, min(lo + 4.0, hi), 4096)
+    p = (10.0 ** e).astype(np.float32)
+    p[5000::97] = 0.0
+    p[6001::89] = 1.0
+    p[7002::83] = np.float32(1.4e-45)              # the smallest subnormal
+    C_o, T_o = oracle.build_cdf(p, alpha)
+    cdf, tot = ps.build_cdf(dev(p), alpha)
+    C_g = host(cdf)
+    pos = C_o > 0
+    e_rel = float(np.max(np.abs(C_g[pos] - C_o[pos]) / C_o[pos]))
+    say(f"pow extremes alpha={alpha}: max rel CDF err {e_rel:.3e}")
+    assert np.all(C_g[~pos] == 0)
+    assert e_rel <= 1e-12
+    assert np.all(np.diff(C_g) >= 0)
+
+
 def test_scan_all_ones_exact(ps):
     n = (1 << 21) + 5
     cdf, tot = ps.build_cdf(torch.ones(n, dtype=torch.float32, device="cuda"), 0.6)
