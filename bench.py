@@ -410,7 +410,8 @@ def main():
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              "(this build runs on a single MI355X; see the sharding notes in DESIGN.md)",
+              "(the library runs on a single MI355X; a sharded run would use these "
+              "kernels per shard, with an all-gather of the shard totals)",
               file=sys.stderr)
         sys.exit(2)
     import torch
