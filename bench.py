@@ -354,7 +354,8 @@ def pf_bench(ps, torch, reps=50):
 
 
 def per_large_bench(ps, torch, reps=10):
-    """PER large: B = 2^24, 2^20 stratified draws, CDF path and tree path."""
+    """PER large: B = 2^24, 2^20 stratified draws, CDF path and tree path, and
+    the whole update through psamp_per_round."""
     import synthetic_inputs as si
     d = si.per_large()
     p = torch.from_numpy(d["p"]).cuda()
@@ -365,12 +366,18 @@ def per_large_bench(ps, torch, reps=10):
     tree = torch.zeros(2 * p.numel(), dtype=torch.float32, device="cuda")
     ws = ps.Workspace(ps.build_cdf_workspace_size(p.numel()))
     iws = ps.Workspace(ps.is_weights_workspace_size(U.numel()))
+    # the whole update (CDF, draws, IS, rewrite) on a copy that it rewrites
+    p_pr = p.clone()
+    newp = torch.from_numpy(si.generic_f32(U.numel(), 77, "lognormal")).cuda()
+    pws = ps.Workspace(ps.per_round_workspace_size(p.numel(), U.numel()))
     calls = {
         "build_cdf": lambda: ps.build_cdf(p, d["alpha"], cdf=cdf, total=tot, ws=ws),
         "sample": lambda: ps.sample(cdf, tot, U, out=idx),
         "build_cdf_sample_fused": lambda: ps.build_cdf_sample(p, U, d["alpha"], cdf=cdf, total=tot,
                                                               out=idx, ws=ws),
         "is_weights": lambda: ps.is_weights(p, idx, d["alpha"], d["beta"], out=w, ws=iws),
+        "per_round": lambda: ps.per_round(p_pr, U, d["alpha"], d["beta"], newp, out_idx=idx,
+                                          out_w=w, cdf=cdf, total=tot, ws=pws),
         "tree_build": lambda: ps.segtree_build(tree, p, d["alpha"]),
         "tree_sample": lambda: ps.segtree_sample(tree, p.numel(), U, stratified=True, out=idx),
     }

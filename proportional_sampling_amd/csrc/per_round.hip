@@ -353,13 +353,12 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
         }
 #undef PSAMP_PER_ROUND_TRY
     }
-    // Too large to be resident at once (or nothing to draw): the separate
-    // kernels, same results.
-    psamp_status s = psamp_build_cdf(prio, PSAMP_F32, n, alpha, cdf, PSAMP_F64, total, ws, scan_ws,
-                                     stream);
+    // Too large to be resident at once (or nothing to draw): the fused scan +
+    // stratified sample, then the IS weights and the rewrite -- the same
+    // results as the four separate calls.
+    psamp_status s = psamp_build_cdf_sample(prio, PSAMP_F32, n, alpha, u, PSAMP_F32, k, cdf,
+                                            PSAMP_F64, total, out_idx, ws, scan_ws, stream);
     if (s != PSAMP_OK || k == 0) return s;
-    s = psamp_sample(cdf, PSAMP_F64, n, total, u, PSAMP_F32, k, 1, out_idx, stream);
-    if (s != PSAMP_OK) return s;
     const size_t off = ((scan_ws + 255) / 256) * 256;
     s = psamp_is_weights(prio, PSAMP_F32, n, alpha, out_idx, k, beta, out_w,
                          (char*)ws + off, ws_bytes - off, stream);
