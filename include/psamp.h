@@ -328,8 +328,9 @@ psamp_status psamp_scatter_lww(void* prio, psamp_dtype prio_t, int64_t n,
  * (the per-update hot loop of the PER trainers on the pages: [PR615] runs
  * the CDF rebuild 32-128 times per train call; [SEGT] "Problem" samples
  * from the rebuilt prefix sum every step).  Same results, bit for bit, as
- * the four calls; in one kernel when one workgroup per 1024 (or 4096)
- * priorities can be resident at once, else as the four kernels.
+ * the four calls; in one kernel when one workgroup per 1024 (or 8192)
+ * priorities can be resident at once, else in three kernels (tile sums;
+ * scan, draws, drawn priorities and rewrite; IS weights).
  *   prio     : n float priorities, read, then rewritten at the drawn indices
  *              with new_prio (skipped when new_prio is NULL).
  *   u        : k float fractions in [0,1) (stratified thresholds).

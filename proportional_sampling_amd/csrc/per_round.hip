@@ -353,16 +353,11 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
         }
 #undef PSAMP_PER_ROUND_TRY
     }
-    // Too large to be resident at once (or nothing to draw): the fused scan +
-    // stratified sample, then the IS weights and the rewrite -- the same
-    // results as the four separate calls.
-    psamp_status s = psamp_build_cdf_sample(prio, PSAMP_F32, n, alpha, u, PSAMP_F32, k, cdf,
-                                            PSAMP_F64, total, out_idx, ws, scan_ws, stream);
-    if (s != PSAMP_OK || k == 0) return s;
-    const size_t off = ((scan_ws + 255) / 256) * 256;
-    s = psamp_is_weights(prio, PSAMP_F32, n, alpha, out_idx, k, beta, out_w,
-                         (char*)ws + off, ws_bytes - off, stream);
-    if (s != PSAMP_OK || !new_prio) return s;
-    return psamp_scatter_lww(prio, PSAMP_F32, n, out_idx, new_prio, k, PSAMP_SCATTER_GROUPED,
-                             nullptr, 0, stream);
+    // Too large to be resident at once: three kernels (the tile sums; the
+    // scan with the draws, the drawn priorities and the rewrite; the IS
+    // weights), the same results as the four separate calls.
+    if (k > 0)
+        return launch_per_update((float*)prio, n, alpha, beta, u, k, new_prio, out_idx, out_w,
+                                 cdf, total, ws, scan_ws, st);
+    return psamp_build_cdf(prio, PSAMP_F32, n, alpha, cdf, PSAMP_F64, total, ws, scan_ws, stream);
 }

@@ -38,6 +38,16 @@ constexpr int64_t kMaxN = 0x7FFFFFFFll;   // int32 indices
 // device at once (CUs x resident per CU).  Cached per (kernel, device).
 int resident_grid(const void* fn, int block);
 
+// One PER update (CDF, stratified draws, IS weights, rewrite of the drawn
+// priorities) whose grid need not be resident: the tile sums, the scan with
+// the draws, the drawn priorities and the rewrite, then the IS weights --
+// three kernels, the bits of the separate calls (scan.hip).  ws: the scan's
+// workspace.
+psamp_status launch_per_update(float* prio, int64_t n, double alpha, double beta, const float* u,
+                               int64_t k, const float* newp, int32_t* out_idx, float* out_w,
+                               double* cdf, double* total, void* ws, size_t ws_bytes,
+                               hipStream_t st);
+
 // Optional launch trace: PSAMP_TRACE=1 prints one line per launch.
 bool trace_enabled();
 void trace_launch(const char* kernel, int64_t grid, int block, int64_t n);

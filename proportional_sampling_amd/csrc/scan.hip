@@ -58,6 +58,12 @@ struct SampleArgs {
     int64_t k;
     int k_log2;           // log2 k if k is a power of two, else -1 (integer mode)
     int32_t* out;
+    // PER (the fused update, fp mode): the priorities (read, then rewritten),
+    // the new priorities (may be null), the weights (the drawn priorities'
+    // bits are parked there for k_isw_from_slots)
+    float* prio = nullptr;
+    const float* newp = nullptr;
+    float* out_w = nullptr;
 };
 
 // One workgroup per tile, tiles in blockIdx order.  VEC: see load_tile.
@@ -68,7 +74,11 @@ struct SampleArgs {
 // LDS copy of its CDF values.
 // FAST (fp mode, 8-row tiles, alpha <= kFastPowMaxAlpha): p^alpha from
 // per-workgroup tables (pow_prio_fast), built while the tile's loads travel.
-template <int IPT, bool VEC, class In, class Out, bool SAMPLE = false, bool FAST = false>
+// PER (with SAMPLE, fp mode): the rest of a PER update for this tile's draws
+// -- park each drawn priority's bits in out_w, fold the smallest into this
+// call's draw-minimum slots, then rewrite the last draw of each index.
+template <int IPT, bool VEC, class In, class Out, bool SAMPLE = false, bool FAST = false,
+          bool PER = false>
 __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     const In* __restrict__ in, int64_t n, double alpha, Out* __restrict__ cdf,
     Out* __restrict__ total, uint64_t* __restrict__ ws, int n_tiles,
@@ -88,6 +98,7 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
     __shared__ Acc s_C[SAMPLE ? TILE : 1];
     __shared__ Acc s_T;
     __shared__ int64_t s_range[2];
+    __shared__ uint32_t s_mn[4];
 
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -231,6 +242,7 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
         __syncthreads();
         const int64_t i_lo = s_range[0], i_hi = s_range[1];
         const Acc T = s_T;
+        uint32_t mn = 0xFFFFFFFFu;
         for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
             Acc t;
             if constexpr (kFp)
@@ -247,6 +259,38 @@ __global__ __launch_bounds__(kScanThreads) void k_build_cdf(
             b += (s_C[b] < t) ? 1 : 0;
             if (b >= tlen) b = tlen - 1;
             sa.out[i] = (int32_t)(base + b);
+            if constexpr (PER) {
+                // the drawn priority, as read before any rewrite of this tile
+                const uint32_t key = __float_as_uint(sa.prio[base + b]);
+                reinterpret_cast<uint32_t*>(sa.out_w)[i] = key;
+                mn = key < mn ? key : mn;
+            }
+        }
+        if constexpr (PER) {
+            mn = wave_min_u32(mn);
+            if (lane == 0) s_mn[wave] = mn;
+            __syncthreads();          // every drawn priority has been read
+            if (tid == 0) {
+                const uint32_t m = min_(min_(s_mn[0], s_mn[1]), min_(s_mn[2], s_mn[3]));
+                if (m != 0xFFFFFFFFu)
+                    fetch_max_agent(&ws[kHdrDrawMin + kDrawMinSlots * par + (tile & 3)],
+                                    (uint64_t)(~m));
+            }
+            // rewrite: draw i is the last of its index unless draw i + 1 (in
+            // this tile) lands on the same element -- the search's own test
+            if (sa.newp != nullptr) {
+                for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
+                    const int b = sa.out[i] - (int32_t)base;
+                    // (draw i + 1 lands on b or later; on the tile's last
+                    // element it can only land on b)
+                    bool last = i + 1 >= i_hi;
+                    if (!last && b < tlen - 1) {
+                        const Acc tn = strat_threshold(i + 1, ((const float*)sa.u)[i + 1], sa.k, T);
+                        last = s_C[b] < tn;
+                    }
+                    if (last) sa.prio[base + b] = sa.newp[i];
+                }
+            }
         }
     }
 }
@@ -449,6 +493,89 @@ static psamp_status launch_scan_sample(const void* prio, int64_t n, double alpha
     }
     return launch_scan_sample_t<IPT, In, false>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok,
                                                 sa, st);
+}
+
+// The IS weights of a fused update whose draws parked their priorities in
+// out_w (k_build_cdf with PER): the smallest drawn priority is read from
+// this call's draw-minimum slots, then IS_i = (p_min / p_i)^(alpha beta) with
+// the arithmetic of psamp_is_weights.
+constexpr int kIswSlotThreads = 1024;
+constexpr int kIswSlotPer = 4;
+__global__ __launch_bounds__(kIswSlotThreads) void k_isw_from_slots(int64_t k, double e,
+                                                                   const uint64_t* __restrict__ ws,
+                                                                   float* __restrict__ out) {
+    __shared__ MathLds M;
+    const int tid = threadIdx.x;
+    math_lds_fill(&M, tid, kIswSlotThreads);
+    __syncthreads();
+    // k_tile_sums of this call has advanced the counter
+    const int par = (int)((load_agent(&ws[kHdrCalls]) - 1u) & 1u);
+    uint64_t mx = 0;
+#pragma unroll
+    for (int q = 0; q < kDrawMinSlots; ++q)
+        mx = max_(mx, load_agent(&ws[kHdrDrawMin + kDrawMinSlots * par + q]));
+    const double pmin = (double)__uint_as_float(~(uint32_t)mx);
+    const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
+    const int64_t b0 = (int64_t)blockIdx.x * kIswSlotThreads * kIswSlotPer;
+#pragma unroll
+    for (int j = 0; j < kIswSlotPer; ++j) {
+        const int64_t i = b0 + j * kIswSlotThreads + tid;
+        if (i < k) {
+            const double p = (double)__uint_as_float(reinterpret_cast<const uint32_t*>(out)[i]);
+            out[i] = is_weight(pmin, lpmin, p, e, &M);
+        }
+    }
+}
+
+template <int IPT, bool FAST>
+static psamp_status launch_per_update_t(float* prio, int64_t n, double alpha, double ab,
+                                        const float* u, int64_t k, const float* newp,
+                                        int32_t* out_idx, float* out_w, double* cdf,
+                                        double* total, uint64_t* ws, uint64_t max_slots,
+                                        int vec_ok, hipStream_t st) {
+    const int tiles = (int)ceil_div(n, kScanThreads * IPT);
+    if (trace_enabled()) trace_launch("k_tile_sums+k_build_cdf<per>+k_isw", tiles, kScanThreads, n);
+    SampleArgs sa{u, k, -1, out_idx};
+    sa.prio = prio;
+    sa.newp = newp;
+    sa.out_w = out_w;
+    if (aligned(prio, 16) && n % 4 == 0) {
+        hipLaunchKernelGGL((k_tile_sums<IPT, true, float, FAST>), dim3(tiles), dim3(kScanThreads),
+                           0, st, prio, n, alpha, ws, tiles);
+        hipLaunchKernelGGL((k_build_cdf<IPT, true, float, double, true, FAST, true>), dim3(tiles),
+                           dim3(kScanThreads), 0, st, prio, n, alpha, cdf, total, ws, tiles,
+                           max_slots, vec_ok, sa);
+    } else {
+        hipLaunchKernelGGL((k_tile_sums<IPT, false, float, FAST>), dim3(tiles), dim3(kScanThreads),
+                           0, st, prio, n, alpha, ws, tiles);
+        hipLaunchKernelGGL((k_build_cdf<IPT, false, float, double, true, FAST, true>), dim3(tiles),
+                           dim3(kScanThreads), 0, st, prio, n, alpha, cdf, total, ws, tiles,
+                           max_slots, vec_ok, sa);
+    }
+    psamp_status s = launch_status();
+    if (s != PSAMP_OK) return s;
+    const int64_t g = ceil_div(k, (int64_t)kIswSlotThreads * kIswSlotPer);
+    hipLaunchKernelGGL(k_isw_from_slots, dim3((unsigned)g), dim3(kIswSlotThreads), 0, st, k, ab,
+                       ws, out_w);
+    return launch_status();
+}
+
+psamp_status launch_per_update(float* prio, int64_t n, double alpha, double beta, const float* u,
+                               int64_t k, const float* newp, int32_t* out_idx, float* out_w,
+                               double* cdf, double* total, void* ws, size_t ws_bytes,
+                               hipStream_t st) {
+    const uint64_t max_slots = ws_tile_capacity(ws_bytes);
+    const int vec_ok = aligned(cdf, 16);
+    uint64_t* w = (uint64_t*)ws;
+    const double ab = alpha * beta;
+    if (scan_rows_for(n) == 1)
+        return launch_per_update_t<4, false>(prio, n, alpha, ab, u, k, newp, out_idx, out_w, cdf,
+                                             total, w, max_slots, vec_ok, st);
+    if (use_fast_pow<32, float>(alpha))
+        return launch_per_update_t<32, true>(prio, n, alpha, ab, u, k, newp, out_idx, out_w, cdf,
+                                             total, w, max_slots, vec_ok, st);
+    return launch_per_update_t<32, false>(prio, n, alpha, ab, u, k, newp, out_idx, out_w, cdf,
+                                          total, w, max_slots, vec_ok, st);
 }
 
 }  // namespace psamp

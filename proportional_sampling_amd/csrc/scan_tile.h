@@ -54,7 +54,11 @@ constexpr int kSpinLimit = 1 << 21;    // bounded waits (about a second)
 constexpr int kLbGtWords = 2;          // group totals per lane per round trip (lookback)
 constexpr int kAllWords = 4;           // tile sums per lane per round trip (lookback_all)
 
-enum : int { kHdrCalls = 0, kHdrHw = 1, kHdrErr = 2, kHdrT = 4, kHdrDummy = 8, kHdrExit = 16 };
+enum : int {
+    kHdrCalls = 0, kHdrHw = 1, kHdrErr = 2, kHdrT = 4, kHdrDummy = 8, kHdrExit = 16,
+    kHdrDrawMin = 20     // 2 parities x kDrawMinSlots: max of ~(smallest drawn priority bits)
+};
+constexpr int kDrawMinSlots = 4;
 
 // Rows of 1024 elements per tile.  The tiling fixes the association of the
 // fp sums, so the scan and the fused update both take it from here.
@@ -149,6 +153,7 @@ __device__ __forceinline__ void clear_other_parity(uint64_t* ws, int par, int n_
         fetch_max_agent(&ws[kHdrHw], (uint64_t)n_tiles);
         ws[kHdrT + op] = 0;
     }
+    if (blockIdx.x == 0 && t < kDrawMinSlots) ws[kHdrDrawMin + kDrawMinSlots * op + t] = 0;
     const uint32_t groups = (uint32_t)((hw + kScanGroup - 1) / kScanGroup);
     for (uint32_t s = blockIdx.x * (uint32_t)nt + t; s < hw; s += gridDim.x * (uint32_t)nt) {
         ws[a_off(s, op)] = 0;

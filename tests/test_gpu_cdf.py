@@ -323,7 +323,8 @@ def _separate_round(ps, p, U, newp, alpha, beta):
 @pytest.mark.parametrize("n,k", [(1, 1), (1000, 7), (1024, 1024), (5000, 300), (8192, 1024),
                                  (262144, 8192), (262147, 8191), (100000, 100000),
                                  (1 << 20, 4096), (1500001, 8192), (1 << 21, 20000),
-                                 ((1 << 22) + 5, 1 << 16)])
+                                 ((1 << 22) + 5, 1 << 16), (3 * (1 << 21) + 7, 8192),
+                                 ((1 << 23) + 1, 1 << 18)])
 def test_per_round_equals_separate_calls(ps, n, k):
     say(f"per_round n={n} k={k}")
     p = si.generic_f32(n, n + 13, "exp")
@@ -493,4 +494,25 @@ def test_build_cdf_sample_mixed_calls_one_workspace(ps, mode):
         else:
             cdf, tot = ps.build_cdf(P, alpha, ws=ws)
         assert torch.equal(cdf, c_ref) and torch.equal(tot, t_ref), f"rep {rep}"
+    assert ws.errors() == 0
+
+
+def test_per_round_large_chain(ps):
+    """Beyond a resident grid (2^23 priorities, three kernels per update):
+    four chained updates on one workspace, each equal to the separate calls
+    on the previous update's rewritten priorities."""
+    n, k = 1 << 23, 1 << 16
+    p = si.generic_f32(n, 21, "lognormal")
+    Pd = dev(p)
+    ws = ps.Workspace(ps.per_round_workspace_size(n, k))
+    p_ref = p.copy()
+    for r in range(4):
+        U = si.uniform_f32(np.random.default_rng(100 + r), k)
+        newp = si.generic_f32(k, 200 + r, "exp")
+        C_s, T_s, idx_s, w_s, p_ref = _separate_round(ps, p_ref, U, newp, 0.7, 0.5)
+        idx, w, cdf, tot = ps.per_round(Pd, dev(U), 0.7, 0.5, dev(newp), ws=ws)
+        assert np.array_equal(host(cdf), C_s), f"update {r}: cdf"
+        assert np.array_equal(host(idx), idx_s), f"update {r}: indices"
+        assert np.array_equal(host(w), w_s), f"update {r}: weights"
+        assert np.array_equal(host(Pd), p_ref), f"update {r}: rewritten priorities"
     assert ws.errors() == 0
