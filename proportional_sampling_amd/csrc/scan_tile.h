@@ -29,8 +29,10 @@
 //     any tile that has read every A can form.
 // Integer mode is exact and needs none of this, but shares the code.
 //
-// Workspace: a 256-byte header, then one 4 KiB block per 64 tiles (block b
-// holds the words of tiles 64b..64b+63):
+// Workspace: a 256-byte header (call counter, high-water mark, error bits,
+// T per parity, a dummy word for polls, the tile-sum pass's exit counter,
+// the large fused update's draw-minimum slots per parity), then one 4 KiB
+// block per 64 tiles (block b holds the words of tiles 64b..64b+63):
 //   [  0,  64) A, parity 0      [ 64, 128) A, parity 1
 //   [128, 192) MIN, parity 0    [192, 256) MIN, parity 1
 //   [256, 512) group totals GT of groups 128b..128b+127, two parities each
