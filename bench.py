@@ -109,11 +109,11 @@ class PerMid:
 
 
 KERNEL_NAMES = {
-    "build_cdf": "k_build_cdf<4, true, float, double, false>",
+    "build_cdf": "k_build_cdf<4, true, float, double, false, false, false>",
     "sample": "k_sample_fp<double>",
     "is_weights": "k_isw_single<float>",
     "scatter_lww": "k_scatter_grouped",
-    "per_round": "k_per_round<1, true, true>",
+    "per_round": "k_per_round<1, true, true, false>",
 }
 
 
