@@ -50,8 +50,7 @@ __global__ __launch_bounds__(kResThreads) void k_resample_rows(
     for (int r = 0; r < R; ++r) {
         const int e0 = r * ROW + 4 * tid;
         if (full && vec_ok) {
-            *reinterpret_cast<int4*>(out + e0) =
-                make_int4((int)a[r][0], (int)a[r][1], (int)a[r][2], (int)a[r][3]);
+            store_nt(out + e0, (int)a[r][0], (int)a[r][1], (int)a[r][2], (int)a[r][3]);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c)

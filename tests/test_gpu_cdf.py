@@ -114,6 +114,44 @@ def test_scan_pow_extremes_large_tiles(ps, alpha):
     assert np.all(np.diff(C_g) >= 0)
 
 
+# Large-tile sizes (8192-element tiles) past what one round of workgroups
+# covers on 256 CUs: a one-element tail, whole tiles only, a ragged tail,
+# several rounds.
+LARGE_SIZES = [512 * 8192 + 1, 1 << 23, 513 * 8192 + 4, 3 * (1 << 22) + 4100, (1 << 24) + 12]
+
+
+@pytest.mark.parametrize("n", LARGE_SIZES)
+def test_scan_large_sizes(ps, n):
+    """Integer mode bit for bit against the oracle; fp mode within 1e-12 of
+    the oracle and bit for bit equal to the CDF of the fused scan + sample
+    (a different pair of kernels over the same tiles); T = C_{n-1}; one
+    workspace shared with a small scan in between."""
+    say(f"scan large n={n}")
+    ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+    q = si.sweep_u32(n)
+    C_o, T_o = oracle.build_cdf_int(q)
+    cdf, tot = ps.build_cdf(dev(q), ws=ws)
+    assert np.array_equal(host(cdf), C_o)
+    assert int(host(tot)[0]) == T_o
+    del cdf, C_o
+    small, _ = ps.build_cdf(dev(q[:5000]), ws=ws)
+    assert np.array_equal(host(small), np.cumsum(q[:5000].astype(np.uint64)))
+    p = si.sweep_f32(n)
+    C_o, T_o = oracle.build_cdf(p, 0.7)
+    P = dev(p)
+    cdf, tot = ps.build_cdf(P, 0.7, ws=ws)
+    C_g = host(cdf)
+    e = rel_err(C_g, C_o)
+    say(f"  max rel CDF err {e:.3e}")
+    assert e <= 1e-12
+    assert host(tot)[0] == C_g[-1]
+    _, cdf_f, tot_f = ps.build_cdf_sample(P, dev(si.uniform_f32(np.random.default_rng(n), 64)),
+                                          0.7, ws=ws)
+    assert np.array_equal(host(cdf_f), C_g)
+    assert np.array_equal(host(tot_f), host(tot))
+    assert ws.errors() == 0
+
+
 def test_scan_all_ones_exact(ps):
     n = (1 << 21) + 5
     cdf, tot = ps.build_cdf(torch.ones(n, dtype=torch.float32, device="cuda"), 0.6)
