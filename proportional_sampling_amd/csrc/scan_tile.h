@@ -117,11 +117,12 @@ template <int R, bool VEC, class In>
 __device__ __forceinline__ void load_tile(const In* __restrict__ tin, int tlen, In (&v)[R][4]) {
     constexpr int ROW = kScanThreads * 4;
     const int t4 = 4 * (int)threadIdx.x;
+    const int lim = tlen - t4;           // element (r, c) is valid iff r*ROW + c < lim
 #pragma unroll
     for (int r = 0; r < R; ++r) {
         const int e0 = r * ROW + t4;
         if constexpr (VEC) {
-            const bool ok = e0 < tlen;
+            const bool ok = r * ROW < lim;
             const uint4 x = *reinterpret_cast<const uint4*>(tin + (ok ? e0 : 0));
             v[r][0] = ok ? __builtin_bit_cast(In, x.x) : In(0);
             v[r][1] = ok ? __builtin_bit_cast(In, x.y) : In(0);
@@ -130,7 +131,7 @@ __device__ __forceinline__ void load_tile(const In* __restrict__ tin, int tlen, 
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const bool ok = e0 + c < tlen;
+                const bool ok = r * ROW + c < lim;
                 const In e = tin[ok ? e0 + c : 0];
                 v[r][c] = ok ? e : In(0);
             }
