@@ -248,6 +248,67 @@ def test_sample_edges(ps):
     assert list(host(ps.sample(cdf, tot, dev(np.array([0.0, 0.7], np.float32))))) == [0, 0]
 
 
+def _host_search(C, t):
+    """min(first j with C_j >= t, n - 1) -- numpy's left searchsorted."""
+    return np.searchsorted(C, t, side="left").clip(0, C.size - 1).astype(np.int32)
+
+
+# (n, k, CDF dtype, weights): the draws placed from the CDF's side (small
+# CDFs, dense draws) and by binary search (otherwise) must both be the
+# lower bound of the definition on the same CDF, bit for bit.  The CDF is
+# built on the host (a plain cumulative sum), so only the search runs on the
+# GPU; the thresholds are the same IEEE double operations on both sides.
+SEARCH_CASES = [(1000, 100000, "f64", "exp"), (262147, 8191, "f64", "exp"),
+                (65539, 1 << 16, "f32", "exp"), (10000, 8192, "f64", "heavy"),
+                (4096, 4096, "f64", "ones"), (300000, 5000, "f64", "zeros"),
+                (1 << 20, 1 << 14, "f64", "exp"), (3, 7, "f64", "exp"), (1, 5, "f32", "exp"),
+                ((1 << 20) + 4, 1 << 15, "f64", "exp"), (5000, 10, "f64", "exp")]
+
+
+@pytest.mark.parametrize("n,k,dt,kind", SEARCH_CASES)
+def test_stratified_search_host_cdf(ps, n, k, dt, kind):
+    say(f"stratified search n={n} k={k} {dt} {kind}")
+    rng = np.random.default_rng(n + k)
+    if kind == "ones":
+        w = np.ones(n)
+    elif kind == "heavy":
+        w = np.full(n, 1e-3)
+        w[n // 3] = 1e6                         # most draws land on one element
+    elif kind == "zeros":
+        w = rng.exponential(1.0, n)
+        w[rng.random(n) < 0.7] = 0.0            # long runs of equal CDF values
+    else:
+        w = rng.exponential(1.0, n)
+    C = np.cumsum(w)
+    if dt == "f32":
+        C = C.astype(np.float32)
+    U = si.uniform_f32(rng, k)
+    U[0] = 0.0
+    T = float(C[-1])
+    t = ((np.arange(k, dtype=np.float64) + U.astype(np.float64)) / k) * T
+    expect = _host_search(C.astype(np.float64), t)
+    cdf = dev(C)
+    idx = host(ps.sample(cdf, cdf[-1:].clone(), dev(U), stratified=True))
+    assert np.array_equal(idx, expect)
+
+
+def test_stratified_search_int_host_cdf(ps):
+    """Integer mode: exact thresholds from Python integers, host CDF."""
+    for n, k in [(4097, 5000), (300007, 1 << 16), (17, 64), (1 << 20, 1 << 14)]:
+        rng = np.random.default_rng(n)
+        q = rng.integers(0, 1 << 20, n, dtype=np.uint64)
+        q[0] = max(int(q[0]), 1)
+        C = np.cumsum(q, dtype=np.uint64)
+        r = rng.integers(0, 1 << 32, k, dtype=np.uint64).astype(np.uint32)
+        T = int(C[-1])
+        t = np.array([(((i << 32) + int(r[i])) * T) // (k << 32) + 1 for i in range(k)],
+                     dtype=np.uint64)
+        expect = _host_search(C, t)
+        cdf = dev(C)
+        idx = host(ps.sample(cdf, cdf[-1:].clone(), dev(r), stratified=True))
+        assert np.array_equal(idx, expect), (n, k)
+
+
 @pytest.mark.parametrize("k,strat", [(1, True), (1000, True), (1 << 16, True), (1000, False),
                                      (4099, False)])
 def test_sample_int_bit_exact(ps, k, strat):
