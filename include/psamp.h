@@ -99,7 +99,10 @@ psamp_status psamp_build_cdf(const void* prio, psamp_dtype prio_t, int64_t n,
  *   iid:        t_i = U_i * T
  * and the index idx_i = min(first j with C_j >= t_i, n - 1) -- [PF]
  * searchsorted with right=False, then clamp to n-1.
- *   cdf, total : from psamp_build_cdf (PSAMP_F64, PSAMP_F32 or PSAMP_U64).
+ *   cdf, total : from psamp_build_cdf (PSAMP_F64, PSAMP_F32 or PSAMP_U64),
+ *                or any non-decreasing CDF with total = its last value
+ *                (device memory; for a CDF that decreases somewhere every
+ *                index is still written, in [0, n), but unspecified).
  *   u          : k fractions.  fp CDF: PSAMP_F32 values in [0,1).  Integer
  *                CDF: PSAMP_U32 values r_i (U_i = r_i / 2^32), and
  *                  stratified: t_i = floor(((i 2^32 + r_i) T) / (k 2^32)) + 1
