@@ -78,6 +78,7 @@ class PerMid:
         self.w = torch.empty(self.k, dtype=torch.float32, device="cuda")
         self.ws = ps.Workspace(ps.build_cdf_workspace_size(self.n))
         self.rws = ps.Workspace(ps.per_round_workspace_size(self.n, self.k))
+        self.iws = ps.Workspace(ps.is_weights_workspace_size(self.k))
 
     def step_fused(self):
         """One step through the fused update entry point (one kernel per
@@ -93,7 +94,7 @@ class PerMid:
         for r in range(self.rounds):
             ps.build_cdf(self.p, self.alpha, cdf=self.cdf, total=self.tot, ws=self.ws)
             ps.sample(self.cdf, self.tot, self.U[r], stratified=True, out=self.idx)
-            ps.is_weights(self.p, self.idx, self.alpha, self.beta, out=self.w)
+            ps.is_weights(self.p, self.idx, self.alpha, self.beta, out=self.w, ws=self.iws)
             ps.scatter_lww(self.p, self.idx, self.v[r], grouped=True)
 
     def algo_bytes(self, name):
@@ -110,8 +111,8 @@ class PerMid:
 
 KERNEL_NAMES = {
     "build_cdf": "k_build_cdf<4, true, float, double, false, false, false>",
-    "sample": "k_sample_fp<double>",
-    "is_weights": "k_isw_single<float>",
+    "sample": "k_sample_strat_fp<true, double>",
+    "is_weights": "k_isw_small<float>",
     "scatter_lww": "k_scatter_grouped",
     "per_round": "k_per_round<1, true, true, false>",
 }

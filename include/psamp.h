@@ -145,9 +145,11 @@ psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_
  *   prio   : the n priorities the CDF was built from (F32 or U32).
  *   idx    : k indices from psamp_sample (clamped into [0, n) on use).
  *   out_w  : k float weights in (0, 1]; the largest is exactly 1.  Must not
- *            overlap prio (large batches park the gathered priorities there).
- *   ws     : psamp_is_weights_workspace_size(k) bytes (may be 0 bytes and
- *            NULL when that size is 0).
+ *            overlap prio (the gathered priorities are parked there).
+ *   ws     : psamp_is_weights_workspace_size(k) bytes (256 B + 4 B per 1024
+ *            samples up to 8192, per 4096 above; 0 for k = 0), zero-filled
+ *            once after allocation; the calls keep it consistent.  One ws
+ *            must not serve two calls that may run at the same time.
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (beta < 0 or not finite,
  * alpha <= 0), E_WORKSPACE, E_LAUNCH.
  * ---------------------------------------------------------------------- */
