@@ -47,8 +47,8 @@ __device__ __forceinline__ int64_t clamp_idx(int32_t i, int64_t n) {
 // k <= 8192: one sample per thread in blocks of 1024.  Each block gathers its
 // priorities (one round trip for the indices, one for the priorities),
 // parks their bits in out, folds its minimum into part[b] and counts itself
-// in on hdr[0]; the last block to arrive forms the minimum over all blocks
-// and writes every weight from the parked values, then rearms the counter.
+// in on hdr[0] (a wrapping counter); the last block to arrive forms the
+// minimum over all blocks and writes every weight from the parked values.
 // (One workgroup gathering all 8192 took 12 us: a single CU's request rate
 // bounds 8192 scattered gathers.)
 template <class P>
@@ -86,7 +86,10 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_small(const P* __restrict__
     if (tid == 0) {
         part[blockIdx.x] = s_min;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t t = __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        // counts 0 .. nblocks-1 and wraps back to 0 on the last block, so the
+        // counter is rearmed by the same atomic (and a stray value heals)
+        const uint32_t t = __builtin_amdgcn_atomic_inc32(&hdr[0], (uint32_t)(nblocks - 1),
+                                                         __ATOMIC_RELAXED, "agent");
         s_last = (t == (uint32_t)(nblocks - 1));
     }
     __syncthreads();
@@ -100,11 +103,10 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_small(const P* __restrict__
     const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
     for (int64_t j = tid; j < k; j += kIswThreads)
         out[j] = is_weight(pmin, lpmin, prio_val<P>(park[j]), e, &M);
-    if (tid == 0) __hip_atomic_store(&hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Pass 1: per-block minimum; the last block to finish reduces them into
-// hdr[1] and rearms the block counter hdr[0] for the next call.  Each
+// hdr[1] (the block counter hdr[0] wraps back to 0 on the last block).  Each
 // gathered priority's bits are parked in out[i] for pass 2.
 template <class P>
 __global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ prio, int64_t n,
@@ -134,7 +136,8 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ p
     if (tid == 0) {
         part[blockIdx.x] = s_min;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t t = __hip_atomic_fetch_add(&hdr[0], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint32_t t = __builtin_amdgcn_atomic_inc32(&hdr[0], (uint32_t)(nblocks - 1),
+                                                         __ATOMIC_RELAXED, "agent");
         s_last = (t == (uint32_t)(nblocks - 1));
         if (s_last) s_min = 0xFFFFFFFFu;
     }
@@ -146,10 +149,7 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ p
         m2 = min_(m2, __hip_atomic_load(&part[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     atomicMin(&s_min, m2);
     __syncthreads();
-    if (tid == 0) {
-        hdr[1] = s_min;
-        __hip_atomic_store(&hdr[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (tid == 0) hdr[1] = s_min;
 }
 
 // Pass 2: the weights from the parked priorities (read and overwritten in

@@ -324,6 +324,26 @@ def test_sample_int_bit_exact(ps, k, strat):
     assert rel_err(w_g, w_o) <= 1e-6
 
 
+def test_is_weights_workspace_reuse(ps):
+    """One workspace across batch sizes on both paths (one kernel up to 8192
+    samples, two above), each call against the oracle's closed form; a block
+    counter left at a stray value is back in step after one call."""
+    n = 262144
+    p = si.generic_f32(n, 91, "exp")
+    Pd = dev(p)
+    ws = ps.Workspace(ps.is_weights_workspace_size(1 << 16))
+    rng = np.random.default_rng(4)
+    for step, k in enumerate([8192, 1000, 5000, 1 << 16, 1024, 8193, 3, 8192]):
+        if step == 6:
+            ws.buf.view(torch.int32)[0] = 5         # stray counter: this call is not checked
+            ps.is_weights(Pd, dev(rng.integers(0, n, k).astype(np.int32)), 0.6, 0.4, ws=ws)
+        idx = np.sort(rng.integers(0, n, k)).astype(np.int32)
+        w_g = host(ps.is_weights(Pd, dev(idx), 0.6, 0.4, ws=ws))
+        w_o = oracle.is_weights(p, 0.6, 1.0, idx, 0.4)
+        assert rel_err(w_g, w_o) <= 1e-6, (step, k)
+        assert w_g.max() == 1.0
+
+
 def test_per_mid_cfg_32_rounds(ps):
     """PER mid: B=262144, 32 updates of (CDF rebuild, 8192 stratified draws,
     IS weights, rewrite of the drawn priorities).  The oracle runs its own
