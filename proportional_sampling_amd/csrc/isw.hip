@@ -10,11 +10,11 @@
 // largest weight comes out as exactly 1.
 //
 // Small batches (k <= 8192) run in one kernel: blocks of 1024 samples gather
-// their priorities on different CUs at once (parked in the output array),
-// and the last block to finish forms the minimum and every weight.  Larger
-// ones use two kernels: per-block minima with a last-block reduction, then
+// their priorities on different CUs at once and exchange their minima.
+// Larger ones use two kernels: per-block minima with a last-block
+// reduction (the gathered priorities are parked in the output array), then
 // the weights from the parked values -- the priority array is gathered
-// once either way.
+// once.
 #include "psamp_device.h"
 #include "psamp_host.h"
 
@@ -25,6 +25,7 @@ constexpr int kIswPerThread = 4;
 constexpr int kIswBlock = kIswThreads * kIswPerThread;   // samples per block
 constexpr int64_t kIswSingleMax = 8192;            // one kernel up to this many samples
 constexpr int kIswHdrWords = 64;                        // 256-byte header (uint32)
+constexpr int kIswSpinLimit = 1 << 21;                  // bounded waits (about a second)
 
 template <class P>
 __device__ __forceinline__ uint32_t prio_key(P x);
@@ -44,65 +45,76 @@ __device__ __forceinline__ int64_t clamp_idx(int32_t i, int64_t n) {
     return i < 0 ? 0 : (i >= n ? n - 1 : (int64_t)i);
 }
 
-// k <= 8192: one sample per thread in blocks of 1024.  Each block gathers its
-// priorities (one round trip for the indices, one for the priorities),
-// parks their bits in out, folds its minimum into part[b] and counts itself
-// in on hdr[0] (a wrapping counter); the last block to arrive forms the
-// minimum over all blocks and writes every weight from the parked values.
+// k <= 8192: one sample per thread in blocks of 1024 (at most 8 blocks, so
+// all of them are resident at once).  Each block gathers its priorities
+// (one round trip for the indices, one for the priorities), publishes its
+// minimum in its slot, tagged with this call's number, and polls the other
+// blocks' slots until every one carries the tag; then each block writes its
+// own weights from the keys it holds in registers.  Block 0 advances the
+// call number once it has seen every slot -- by then every block has read
+// it.  No data but the minima crosses between blocks, so no fences.  Waits
+// are bounded (error bit 1 of the workspace header instead of a hang).
 // (One workgroup gathering all 8192 took 12 us: a single CU's request rate
-// bounds 8192 scattered gathers.)
+// bounds 8192 scattered loads; a last-block variant that formed every
+// weight in one workgroup, 10 us.)
+// Workspace header, as 64-bit words: [2] error bits (where
+// psamp_workspace_errors reads them), [4] the small path's call number,
+// [8, 16) its per-block slots; the two-kernel path uses the first two
+// 32-bit words and the words from byte 256 on.
+constexpr int kIswErrWord = 2;
+constexpr int kIswCallWord = 4;
+constexpr int kIswSlotWord0 = 8;
+
 template <class P>
 __global__ __launch_bounds__(kIswThreads) void k_isw_small(const P* __restrict__ prio, int64_t n,
                                                            const int32_t* __restrict__ idx,
                                                            int64_t k, double e,
-                                                           uint32_t* __restrict__ ws, int nblocks,
+                                                           uint64_t* __restrict__ ws, int nblocks,
                                                            float* __restrict__ out) {
     __shared__ MathLds M;
     __shared__ uint32_t s_min;
-    __shared__ int s_last;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const MathRegs mr = math_load(tid);
     if (tid == 0) s_min = 0xFFFFFFFFu;
     const int64_t i = (int64_t)blockIdx.x * kIswThreads + tid;
-    uint32_t* park = reinterpret_cast<uint32_t*>(out);
+    const uint32_t call = (uint32_t)load_agent(&ws[kIswCallWord]);
     uint32_t key = 0xFFFFFFFFu;
-    if (i < k) {
-        key = prio_key<P>(prio[clamp_idx(idx[i], n)]);
-        if (nblocks > 1) park[i] = key;
-    }
+    if (i < k) key = prio_key<P>(prio[clamp_idx(idx[i], n)]);
     math_store(&M, tid, mr);
     const uint32_t mn = wave_min_u32(key);
     __syncthreads();
-    if ((tid & 63) == 0) atomicMin(&s_min, mn);
+    if (lane == 0) atomicMin(&s_min, mn);
     __syncthreads();
-    if (nblocks == 1) {        // k <= 1024: the block's minimum is the minimum
-        const double pmin = prio_val<P>(s_min);
-        const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
-        if (i < k) out[i] = is_weight(pmin, lpmin, prio_val<P>(key), e, &M);
-        return;
+    if (nblocks > 1 && tid < kWave) {
+        const uint64_t tag = (uint64_t)(call + 1u) << 32;
+        if (tid == 0) store_agent(&ws[kIswSlotWord0 + blockIdx.x], tag | s_min);
+        // every slot of this call (lane b polls slot b)
+        const bool need = lane < nblocks;
+        const uint64_t* slot = &ws[kIswSlotWord0 + (need ? lane : 0)];
+        uint64_t w = load_agent(slot);
+        int limit = kIswSpinLimit;
+        asm volatile("" : "+s"(limit));
+        for (int polls = 0; __any(need && (w >> 32) != (tag >> 32)); ++polls) {
+            if (polls > limit) {
+                if (lane == 0)
+                    __hip_atomic_fetch_or(&ws[kIswErrWord], (uint64_t)1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            w = load_agent(slot);
+        }
+        const uint32_t g = wave_min_u32(need ? (uint32_t)w : 0xFFFFFFFFu);
+        if (lane == 0) {
+            s_min = min_(s_min, g);
+            if (blockIdx.x == 0) store_agent(&ws[kIswCallWord], (uint64_t)(call + 1u));
+        }
     }
-    uint32_t* hdr = ws;
-    uint32_t* part = ws + kIswHdrWords;
-    if (tid == 0) {
-        part[blockIdx.x] = s_min;
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        // counts 0 .. nblocks-1 and wraps back to 0 on the last block, so the
-        // counter is rearmed by the same atomic (and a stray value heals)
-        const uint32_t t = __builtin_amdgcn_atomic_inc32(&hdr[0], (uint32_t)(nblocks - 1),
-                                                         __ATOMIC_RELAXED, "agent");
-        s_last = (t == (uint32_t)(nblocks - 1));
-    }
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    // the minimum over all blocks (<= this block's, already in s_min)
-    if (tid < nblocks)
-        atomicMin(&s_min, __hip_atomic_load(&part[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
     __syncthreads();
     const double pmin = prio_val<P>(s_min);
     const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
-    for (int64_t j = tid; j < k; j += kIswThreads)
-        out[j] = is_weight(pmin, lpmin, prio_val<P>(park[j]), e, &M);
+    if (i < k) out[i] = is_weight(pmin, lpmin, prio_val<P>(key), e, &M);
 }
 
 // Pass 1: per-block minimum; the last block to finish reduces them into
@@ -182,7 +194,7 @@ static psamp_status launch_isw(const void* prio, int64_t n, const int32_t* idx, 
         const int nb = (int)ceil_div(k, kIswThreads);
         if (trace_enabled()) trace_launch("k_isw_small", nb, kIswThreads, k);
         hipLaunchKernelGGL(k_isw_small<P>, dim3(nb), dim3(kIswThreads), 0, st, (const P*)prio, n,
-                           idx, k, e, (uint32_t*)ws, nb, out);
+                           idx, k, e, (uint64_t*)ws, nb, out);
         return launch_status();
     }
     const int nb = (int)ceil_div(k, kIswBlock);
@@ -203,7 +215,7 @@ using namespace psamp;
 extern "C" size_t psamp_is_weights_workspace_size(int64_t k) {
     if (k < 0 || k > kMaxN) return 0;
     if (k == 0) return 0;
-    if (k <= kIswSingleMax) return (size_t)kIswHdrWords * 4 + (size_t)ceil_div(k, kIswThreads) * 4;
+    if (k <= kIswSingleMax) return (size_t)kIswHdrWords * 4;   // call number, error bits, 8 slots
     return (size_t)kIswHdrWords * 4 + (size_t)ceil_div(k, kIswBlock) * 4;
 }
 
