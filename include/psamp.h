@@ -146,10 +146,14 @@ psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_
  *   idx    : k indices from psamp_sample (clamped into [0, n) on use).
  *   out_w  : k float weights in (0, 1]; the largest is exactly 1.  Must not
  *            overlap prio (the gathered priorities are parked there).
- *   ws     : psamp_is_weights_workspace_size(k) bytes (256 B + 4 B per 1024
- *            samples up to 8192, per 4096 above; 0 for k = 0), zero-filled
- *            once after allocation; the calls keep it consistent.  One ws
- *            must not serve two calls that may run at the same time.
+ *   ws     : psamp_is_weights_workspace_size(k) bytes (256 B up to 8192
+ *            samples, plus 4 B per 4096 above; 0 for k = 0), zero-filled
+ *            once after allocation; the calls keep it consistent, whatever
+ *            sizes share it.  One ws must not serve two calls that may run
+ *            at the same time.  Up to 8192 samples the kernel's blocks (at
+ *            most 8) wait for one another's minima: a wait that does not end
+ *            within about a second sets bit 0 of the workspace errors
+ *            (psamp_workspace_errors) instead of hanging.
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (beta < 0 or not finite,
  * alpha <= 0), E_WORKSPACE, E_LAUNCH.
  * ---------------------------------------------------------------------- */

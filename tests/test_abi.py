@@ -54,10 +54,10 @@ def test_workspace_sizes(L):
     assert L.psamp_build_cdf_workspace_size(64 * 1024) == 256 + 4096
     assert L.psamp_build_cdf_workspace_size(64 * 1024 + 1) == 256 + 2 * 4096
     assert L.psamp_build_cdf_workspace_size(1 << 24) == 256 + 64 * (1 << 14)
-    assert L.psamp_per_round_workspace_size(262144, 8192) == 256 + 64 * 256 + 512
+    assert L.psamp_per_round_workspace_size(262144, 8192) == 256 + 64 * 256 + 256
     assert L.psamp_per_round_workspace_size(1 << 20, 1 << 20) == 256 + 64 * 1024 + 256 + 4 * 256
-    assert L.psamp_is_weights_workspace_size(8192) == 256 + 4 * 8
-    assert L.psamp_is_weights_workspace_size(1) == 256 + 4
+    assert L.psamp_is_weights_workspace_size(8192) == 256
+    assert L.psamp_is_weights_workspace_size(1) == 256
     assert L.psamp_is_weights_workspace_size(0) == 0
     assert L.psamp_is_weights_workspace_size(1 << 20) == 256 + 4 * 256
     assert L.psamp_scatter_workspace_size(262144, 8192) == 262144 * 4
@@ -221,7 +221,7 @@ def test_replay_validation(L):
     assert L.psamp_replay_sample(ref, FAKE, 1 << 20, 1, 0.4, FAKE, FAKE, None) == E_WS
     rb.cursor = 1000                                                    # corrupted state
     assert L.psamp_replay_update(ref, FAKE, FAKE, 4, None) == E_PARAM
-    assert L.psamp_replay_workspace_size(1000, 8192) == 256 + 4 * 8
+    assert L.psamp_replay_workspace_size(1000, 8192) == 256
     assert L.psamp_replay_workspace_size(1000, 1 << 20) > 0
 
 
