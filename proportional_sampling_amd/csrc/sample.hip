@@ -78,6 +78,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_int(
 // ranges are kept non-empty-or-empty by a running max, so every index is
 // still written with some value in [0, n).)
 constexpr int kStratThreads = 256;
+constexpr int kStratWin = 8;       // thresholds a thread tests directly
 
 // F(x) for fp thresholds t_i = ((i + U_i) / k) * T (double; for a
 // power-of-two k the division is a multiplication by 1/k, the same bits).
@@ -133,79 +134,148 @@ __device__ __forceinline__ int64_t strat_count(const Cnt& F, V x) {
     return lo;
 }
 
-template <class CdfT>
-__device__ __forceinline__ void load4(const CdfT* __restrict__ p, CdfT (&c)[4]);
-template <>
-__device__ __forceinline__ void load4<double>(const double* __restrict__ p, double (&c)[4]) {
-    const double2 a = reinterpret_cast<const double2*>(p)[0];
-    const double2 b = reinterpret_cast<const double2*>(p)[1];
-    c[0] = a.x; c[1] = a.y; c[2] = b.x; c[3] = b.y;
-}
-template <>
-__device__ __forceinline__ void load4<uint64_t>(const uint64_t* __restrict__ p, uint64_t (&c)[4]) {
-    const ulonglong2 a = reinterpret_cast<const ulonglong2*>(p)[0];
-    const ulonglong2 b = reinterpret_cast<const ulonglong2*>(p)[1];
-    c[0] = a.x; c[1] = a.y; c[2] = b.x; c[3] = b.y;
-}
-template <>
-__device__ __forceinline__ void load4<float>(const float* __restrict__ p, float (&c)[4]) {
-    const float4 a = *reinterpret_cast<const float4*>(p);
-    c[0] = a.x; c[1] = a.y; c[2] = a.z; c[3] = a.w;
-}
-
-// VEC: the CDF is 16-byte aligned and n % 4 == 0 (whole 4-element groups,
-// read as vectors).
-template <bool VEC, class CdfT, class V, class Cnt>
-__device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_t n, const Cnt& F,
-                                            int32_t* __restrict__ out) {
-    const int64_t e0 = ((int64_t)blockIdx.x * kStratThreads + threadIdx.x) * 4;
-    if (e0 >= n) return;
-    CdfT raw[4];
+// PER consecutive CDF values of a thread, as 16-byte vectors (VEC) or one
+// by one (clamped to the array).
+template <int PER, bool VEC, class CdfT, class V>
+__device__ __forceinline__ void load_elems(const CdfT* __restrict__ cdf, int64_t e0, int64_t n,
+                                           V (&x)[PER]) {
     if constexpr (VEC) {
-        load4<CdfT>(cdf + e0, raw);
+        if constexpr (sizeof(CdfT) == 8) {
+#pragma unroll
+            for (int h = 0; h < PER / 2; ++h) {
+                const ulonglong2 a = reinterpret_cast<const ulonglong2*>(cdf + e0)[h];
+                x[2 * h] = (V)__builtin_bit_cast(CdfT, a.x);
+                x[2 * h + 1] = (V)__builtin_bit_cast(CdfT, a.y);
+            }
+        } else {
+#pragma unroll
+            for (int h = 0; h < PER / 4; ++h) {
+                const float4 a = reinterpret_cast<const float4*>(cdf + e0)[h];
+                x[4 * h] = (V)a.x; x[4 * h + 1] = (V)a.y; x[4 * h + 2] = (V)a.z; x[4 * h + 3] = (V)a.w;
+            }
+        }
     } else {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) raw[j] = cdf[e0 + j < n ? e0 + j : n - 1];
+        for (int j = 0; j < PER; ++j) x[j] = (V)cdf[e0 + j < n ? e0 + j : n - 1];
     }
-    const int kk = (int)F.k;
-    int lo = e0 == 0 ? 0 : (int)strat_count(F, (V)cdf[e0 - 1]);
+}
+
+// VEC: the CDF is 16-byte aligned and n % PER == 0.  Each thread takes PER
+// consecutive elements (4 up to 2^20 elements, where more threads hide
+// more latency; 8 above, where fewer thresholds per element pay).  The thresholds that can fall among its values lie
+// in a short window [estimate(x_before) - 1, estimate(x_last) + 1]: the
+// thread forms them once (checking that the one below the window is at or
+// below its smallest value and the one above it beyond its largest), and
+// each element's count is the window's start plus the window thresholds at
+// or below its value -- a few thresholds per thread instead of a few per
+// element.  A window wider than kStratWin (many draws on these elements)
+// or a failed check falls back to strat_count per element.
+template <int PER, bool VEC, class CdfT, class V, class Cnt>
+__device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_t n, const Cnt& F,
+                                            int32_t* __restrict__ out) {
+    const int64_t e0 = ((int64_t)blockIdx.x * kStratThreads + threadIdx.x) * PER;
+    if (e0 >= n) return;
+    V x[PER];
+    load_elems<PER, VEC, CdfT, V>(cdf, e0, n, x);
+    const int nv = (int)min_<int64_t>(PER, n - e0);   // valid elements of this thread
+    const bool first = e0 == 0;
+    const V xp = first ? V(0) : (V)cdf[e0 - 1];
+    V xl = x[0];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int64_t e = e0 + j;
-        if (e < n) {
-            int hi = e == n - 1 ? kk : (int)strat_count(F, (V)raw[j]);
+    for (int j = 1; j < PER; ++j) xl = j < nv ? x[j] : xl;
+    const int64_t kk = F.k;
+    const int64_t ca = first ? 0 : F.estimate(xp);
+    const int64_t cb = F.estimate(xl);
+    const int64_t wlo = ca > 0 ? ca - 1 : 0;
+    const int64_t whi = cb + 1 < kk ? cb + 1 : kk - 1;
+    bool win = whi - wlo + 1 <= kStratWin;
+    V t[kStratWin];
+    if (win) {
+#pragma unroll
+        for (int w = 0; w < kStratWin; ++w) t[w] = wlo + w <= whi ? F.thr(wlo + w) : V(0);
+        if (!first && wlo > 0 && !(F.thr(wlo - 1) <= xp)) win = false;
+        if (whi + 1 < kk && !(F.thr(whi + 1) > xl)) win = false;
+    }
+    // (a value outside [x_before, x_last] -- only in a CDF that decreases
+    // somewhere -- is counted as the nearest end, so that neighbouring
+    // threads agree on the count at their shared boundary and every draw is
+    // written once more than zero times)
+    const int64_t span = whi - wlo;
+    auto count = [&](V v) -> int64_t {
+        if (!win) return strat_count(F, v);
+        v = v > xl ? xl : v;
+        if (!first) v = v < xp ? xp : v;
+        int64_t c = wlo;
+#pragma unroll
+        for (int w = 0; w < kStratWin; ++w) c += (w <= span && t[w] <= v) ? 1 : 0;
+        return c;
+    };
+    int64_t lo = first ? 0 : count(xp);
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+        if (j < nv) {
+            const int64_t e = e0 + j;
+            int64_t hi = e == n - 1 ? kk : count(x[j]);
             hi = hi > lo ? hi : lo;
-            for (int i = lo; i < hi; ++i) out[i] = (int32_t)e;
+            for (int64_t i = lo; i < hi; ++i) out[i] = (int32_t)e;
             lo = hi;
         }
     }
 }
 
-template <bool VEC, class CdfT>
+template <int PER, bool VEC, class CdfT>
 __global__ __launch_bounds__(kStratThreads) void k_sample_strat_fp(
     const CdfT* __restrict__ cdf, int64_t n, const CdfT* __restrict__ total,
     const float* __restrict__ U, int64_t k, int32_t* __restrict__ out) {
     const double T = (double)total[0];
     const StratCountFp F{U, k, T, (double)k / T, 1.0 / (double)k, (k & (k - 1)) == 0};
-    strat_place<VEC, CdfT, double>(cdf, n, F, out);
+    strat_place<PER, VEC, CdfT, double>(cdf, n, F, out);
 }
 
-template <bool VEC>
+template <int PER, bool VEC>
 __global__ __launch_bounds__(kStratThreads) void k_sample_strat_int(
     const uint64_t* __restrict__ cdf, int64_t n, const uint64_t* __restrict__ total,
     const uint32_t* __restrict__ r, int64_t k, int k_log2, int32_t* __restrict__ out) {
     const uint64_t T = total[0];
     const StratCountInt F{r, k, T, (double)k / (double)T, k_log2};
-    strat_place<VEC, uint64_t, uint64_t>(cdf, n, F, out);
+    strat_place<PER, VEC, uint64_t, uint64_t>(cdf, n, F, out);
 }
 
-// Stratified draws from the CDF's side when the CDF is small enough to be
-// read whole faster than k searches climb it (each search a chain of
-// log2 n dependent loads) and the draws are not too sparse in it.
-// (Measured: B = 262144 with 8192 draws 7.1 -> 5 us; at 2^24 with 2^20
-// draws the searches are bound by the bytes they touch and stay.)
+template <int PER>
+static psamp_status launch_strat(const void* cdf, psamp_dtype cdf_t, int64_t n, const void* total,
+                                 const void* u, int64_t k, int32_t* out_idx, hipStream_t st) {
+    const int64_t g = ceil_div(n, (int64_t)kStratThreads * PER);
+    const bool vec = n % PER == 0 && aligned(cdf, 16);
+    if (trace_enabled()) trace_launch("k_sample_strat", g, kStratThreads, n);
+#define PSAMP_STRAT_LAUNCH(V)                                                                     \
+    if (cdf_t == PSAMP_U64)                                                                      \
+        hipLaunchKernelGGL((k_sample_strat_int<PER, V>), dim3((unsigned)g), dim3(kStratThreads), 0, \
+                           st, (const uint64_t*)cdf, n, (const uint64_t*)total, (const uint32_t*)u,  \
+                           k, is_pow2(k) ? ilog2_exact(k) : -1, out_idx);                         \
+    else if (cdf_t == PSAMP_F64)                                                                 \
+        hipLaunchKernelGGL((k_sample_strat_fp<PER, V, double>), dim3((unsigned)g),                \
+                           dim3(kStratThreads), 0, st, (const double*)cdf, n,                     \
+                           (const double*)total, (const float*)u, k, out_idx);                    \
+    else                                                                                         \
+        hipLaunchKernelGGL((k_sample_strat_fp<PER, V, float>), dim3((unsigned)g),                 \
+                           dim3(kStratThreads), 0, st, (const float*)cdf, n, (const float*)total, \
+                           (const float*)u, k, out_idx);
+    if (vec) {
+        PSAMP_STRAT_LAUNCH(true)
+    } else {
+        PSAMP_STRAT_LAUNCH(false)
+    }
+#undef PSAMP_STRAT_LAUNCH
+    return launch_status();
+}
+
+// Stratified draws from the CDF's side when they are not too sparse in it
+// (each CDF line read once, against k searches of log2 n dependent loads,
+// the lower levels of which touch about three lines per draw).  Measured:
+// B = 262144 with 8192 draws 7.1 -> 4.9 us; 2^24 with 2^20 draws 55 -> 50 us
+// and 314 -> 145 MB of HBM traffic.  For sparse draws the searches read less.
 inline bool strat_from_cdf(int64_t n, int64_t k) {
-    return n <= ((int64_t)1 << 20) && 64 * k >= n;
+    return 64 * k >= n;
 }
 
 }  // namespace psamp
@@ -227,29 +297,8 @@ extern "C" psamp_status psamp_sample(const void* cdf, psamp_dtype cdf_t, int64_t
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
     if (stratified && strat_from_cdf(n, k)) {
-        const int64_t g = ceil_div(n, (int64_t)kStratThreads * 4);
-        const bool vec = n % 4 == 0 && aligned(cdf, 16);
-        if (trace_enabled()) trace_launch("k_sample_strat", g, kStratThreads, n);
-#define PSAMP_STRAT_LAUNCH(V)                                                                   \
-    if (in)                                                                                    \
-        hipLaunchKernelGGL(k_sample_strat_int<V>, dim3((unsigned)g), dim3(kStratThreads), 0, st, \
-                           (const uint64_t*)cdf, n, (const uint64_t*)total, (const uint32_t*)u, \
-                           k, is_pow2(k) ? ilog2_exact(k) : -1, out_idx);                       \
-    else if (cdf_t == PSAMP_F64)                                                               \
-        hipLaunchKernelGGL((k_sample_strat_fp<V, double>), dim3((unsigned)g), dim3(kStratThreads), \
-                           0, st, (const double*)cdf, n, (const double*)total, (const float*)u, \
-                           k, out_idx);                                                         \
-    else                                                                                       \
-        hipLaunchKernelGGL((k_sample_strat_fp<V, float>), dim3((unsigned)g), dim3(kStratThreads), \
-                           0, st, (const float*)cdf, n, (const float*)total, (const float*)u, k, \
-                           out_idx);
-        if (vec) {
-            PSAMP_STRAT_LAUNCH(true)
-        } else {
-            PSAMP_STRAT_LAUNCH(false)
-        }
-#undef PSAMP_STRAT_LAUNCH
-        return launch_status();
+        if (n <= ((int64_t)1 << 20)) return launch_strat<4>(cdf, cdf_t, n, total, u, k, out_idx, st);
+        return launch_strat<8>(cdf, cdf_t, n, total, u, k, out_idx, st);
     }
     const int64_t grid = ceil_div(k, kSampleThreads);
     if (trace_enabled()) trace_launch("k_sample", grid, kSampleThreads, k);
