@@ -427,6 +427,43 @@ def test_per_large_int_cfg(ps):
     assert rel_err(w_g, w_o) <= 1e-6
 
 
+@pytest.mark.timeout(400)
+def test_max_n_int(ps):
+    """The largest n the ABI takes, 2^31 - 1 (int32 indices; 262144 tiles in
+    4096 lookback groups, a ragged last tile, element-wise loads since n is
+    odd), integer mode so that every check is exact: the CDF and T bit for
+    bit; stratified draws through the binary search (k = 2^20 < n/64) and
+    from the CDF's side (k = 2^25 >= n/64), each equal to the oracle's
+    merge search over the oracle's thresholds; IS weights of the first."""
+    n = (1 << 31) - 1
+    say(f"max n int: n={n} generating")
+    q = si.sweep_u32(n)
+    C_o, T_o = oracle.build_cdf_int(q)
+    say("  oracle CDF done; GPU scan")
+    Q = dev(q)
+    cdf, tot = ps.build_cdf(Q)
+    C_g = host(cdf)
+    assert int(host(tot)[0]) == T_o
+    assert np.array_equal(C_g, C_o)
+    del C_g
+    say("  CDF bit-exact; searches")
+    rng = np.random.default_rng(31)
+    for k in (1 << 20, 1 << 25):
+        r = si.uniform_u32(rng, k)
+        t_o = oracle.thresholds_int(r, T_o, True)
+        idx_o = oracle.search_int(C_o, t_o)
+        idx = host(ps.sample(cdf, tot, dev(r), stratified=True))
+        say(f"  k={k}: {int(np.sum(idx != idx_o))} index mismatches")
+        assert np.array_equal(idx, idx_o)
+        if k == 1 << 20:
+            w_g = host(ps.is_weights(Q, dev(idx), 1.0, 0.5))
+            w_o = oracle.is_weights_int(q, T_o, idx_o, 0.5)
+            assert rel_err(w_g, w_o) <= 1e-6
+        del r, t_o, idx_o, idx
+    del cdf, tot, Q, C_o, q
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ fused update
 def _separate_round(ps, p, U, newp, alpha, beta):
     """The four separate calls, for comparison with the fused update."""

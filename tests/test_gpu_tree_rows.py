@@ -162,6 +162,45 @@ def test_per_large_tree_path(ps):
     assert np.array_equal(idx_t, idx_c)
 
 
+@pytest.mark.timeout(400)
+def test_tree_max_cap_int(ps):
+    """The largest tree the ABI takes: 2^30 leaves (2^31 uint64 nodes,
+    16 GiB) with n_valid = 2^30 - 3.  Root = the exact sum of the leaves;
+    stratified and iid descents equal to the oracle's integer CDF path (the
+    descent of an exact tree is the lower bound on the CDF); then 4096
+    updates of distinct leaves, the first and last valid ones among them,
+    and the same checks on the updated priorities."""
+    cap = 1 << 30
+    n = cap - 3
+    assert ps.segtree_cap_pow2(n) == cap
+    say(f"max tree int: cap={cap} n_valid={n}")
+    q = si.sweep_u32(n, seed=77)
+    tree = torch.zeros(2 * cap, dtype=torch.uint64, device="cuda")
+    ps.segtree_build(tree, dev(q))
+    rng = np.random.default_rng(30)
+    r = si.uniform_u32(rng, 1 << 16)
+
+    def check(what):
+        assert int(host(tree[1:2])[0]) == int(q.sum(dtype=np.uint64)), what
+        for strat in (True, False):
+            idx_t = host(ps.segtree_sample(tree, n, dev(r), stratified=strat))
+            _, _, _, idx_o = oracle.sample_int(q, r, strat)
+            say(f"  {what} strat={strat}: {int(np.sum(idx_t != idx_o))} mismatches")
+            assert np.array_equal(idx_t, idx_o), what
+
+    check("built")
+    m = 4096
+    upd = np.concatenate([[0, n - 1], 1 + rng.choice(n - 2, size=m - 2, replace=False)])
+    upd = upd.astype(np.int32)
+    v = rng.integers(1, 1 << 20, size=m, dtype=np.int64).astype(np.uint32)
+    v[:2] = [1 << 20, 1]
+    ps.segtree_update(tree, dev(upd), dev(v))
+    q[upd] = v
+    check("updated")
+    del tree
+    torch.cuda.empty_cache()
+
+
 # ------------------------------------------------------------ resampling
 def _row_check(lw, u_row, anc_g, what):
     anc_o = oracle.resample_rows(lw, u_row)
