@@ -287,17 +287,38 @@ def segtree_sample(tree: torch.Tensor, n_valid: int, u: torch.Tensor, *,
 # ------------------------------------------------------------ (4) rows
 def resample_rows(logw: torch.Tensor, u_row: torch.Tensor, *, out: torch.Tensor | None = None,
                   stream=None) -> torch.Tensor:
+    """int32 ancestors per row.  logw and out may be row-strided views (unit
+    column stride, row stride >= P): the row strides go to the call as
+    ld_in and ld_out."""
     if logw.dim() != 2:
         raise ValueError("logw must be rows x P")
     rows, P = logw.shape
     if out is None:
         out = torch.empty(rows, P, dtype=torch.int32, device=logw.device)
-    lw = _dev(logw, "logw", (torch.float32,))
+    if tuple(out.shape) != (rows, P):
+        raise ValueError(f"out must have shape {(rows, P)}, got {tuple(out.shape)}")
+    lw, ld_in = _rows_dev(logw, "logw", torch.float32)
     ur = _dev(u_row, "u_row", (torch.float32,))
-    o = _dev(out, "out", (torch.int32,))
+    o, ld_out = _rows_dev(out, "out", torch.int32)
     _check("psamp_resample_rows", lib().psamp_resample_rows(
-        lw, rows, P, P, ur, o, P, _stream(stream)))
+        lw, rows, P, ld_in, ur, o, ld_out, _stream(stream)))
     return out
+
+
+def _rows_dev(t: torch.Tensor, name: str, dtype) -> tuple[int, int]:
+    """Pointer and row stride (in elements) of a rows x P GPU matrix whose
+    rows are contiguous."""
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: dtype {t.dtype}, expected {dtype}")
+    rows, P = t.shape
+    ld = t.stride(0) if rows > 1 else P
+    if P > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name}: rows must be contiguous")
+    if ld < P:
+        raise ValueError(f"{name}: row stride {ld} < P = {P}")
+    return t.data_ptr(), ld
 
 
 class _ReplayStruct(C.Structure):

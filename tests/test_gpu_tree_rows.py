@@ -277,3 +277,43 @@ def test_resample_uniform_identity(ps):
     u = np.linspace(0.01, 0.99, 8).astype(np.float32)
     anc = host(ps.resample_rows(dev(lw), dev(u)))
     assert np.array_equal(anc, np.tile(np.arange(P, dtype=np.int32), (8, 1)))
+
+
+@pytest.mark.parametrize("rows,P,pad_in,pad_out", [(37, 1024, 64, 8), (37, 1024, 3, 1),
+                                                   (9, 1000, 3, 5), (5, 8192, 4, 4),
+                                                   (6, 4097, 1, 7)])
+def test_resample_strided_rows(ps, rows, P, pad_in, pad_out):
+    """Row-strided input and output (ld_in = P + pad_in, ld_out = P + pad_out;
+    a stride that is a multiple of 4 keeps the 16-byte path, others take the
+    element-wise one): the ancestors of every row as the oracle's, and the
+    padding of the output untouched."""
+    d = si.resample(seed=rows * P + pad_in, rows=rows, P=P)
+    big = np.full((rows, P + pad_in), np.float32(7.0))
+    big[:, :P] = d["lw"]
+    lw_t = dev(big)[:, :P]
+    out_big = torch.full((rows, P + pad_out), -7, dtype=torch.int32, device="cuda")
+    ps.resample_rows(lw_t, dev(d["u_row"]), out=out_big[:, :P])
+    o = host(out_big)
+    assert np.all(o[:, P:] == -7)
+    _row_check(d["lw"], d["u_row"], o[:, :P], f"strided {rows}x{P} +{pad_in}/+{pad_out}")
+
+
+@pytest.mark.timeout(400)
+def test_resample_rows_beyond_2p31_elements(ps):
+    """524291 rows x 4096 particles (2^31 + 12288 log-weights, 8 GiB in and
+    8 GiB out, so row offsets need 64 bits): the first and last 32 rows and
+    64 others as the oracle's; every row's ancestors non-decreasing and in
+    [0, P)."""
+    rows, P = (1 << 19) + 3, 4096
+    say(f"resample {rows}x{P}: generating")
+    d = si.resample(seed=2031, rows=rows, P=P)
+    anc = ps.resample_rows(dev(d["lw"]), dev(d["u_row"]))
+    rng = np.random.default_rng(5)
+    sel = np.concatenate([np.arange(32), np.arange(rows - 32, rows),
+                          rng.choice(rows - 64, size=64, replace=False) + 32])
+    a_sel = host(anc[torch.from_numpy(sel).cuda()])
+    _row_check(d["lw"][sel], d["u_row"][sel], a_sel, f"resample {rows}x{P} sampled rows")
+    assert bool((anc[:, 1:] >= anc[:, :-1]).all())
+    assert bool((anc >= 0).all()) and bool((anc < P).all())
+    del anc
+    torch.cuda.empty_cache()
