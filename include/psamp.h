@@ -355,10 +355,12 @@ psamp_status psamp_per_round(void* prio, int64_t n, double alpha, double beta,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
- * Diagnostics.  Copies the error bits a psamp_build_cdf workspace has
- * accumulated (bit 0: a bounded cross-workgroup wait timed out; bit 1: a
- * workgroup drew a ticket outside the call's grid) into *bits_host, with a
- * synchronous device-to-host copy on `stream`.  The only call that syncs.
+ * Diagnostics.  Copies the error bits a workspace of psamp_build_cdf,
+ * psamp_build_cdf_sample, psamp_per_round or psamp_is_weights has
+ * accumulated (bit 0: a bounded cross-workgroup wait timed out, so some
+ * outputs of that call are unspecified; the other bits are always 0) into
+ * *bits_host, with a synchronous device-to-host copy on `stream`.  The only
+ * call that syncs.  The bits stay set until the caller clears the word.
  * Errors: E_NULL, E_WORKSPACE, E_LAUNCH.
  * ---------------------------------------------------------------------- */
 psamp_status psamp_workspace_errors(const void* ws, size_t ws_bytes,
