@@ -147,12 +147,16 @@ psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_
  *   out_w  : k float weights in (0, 1]; the largest is exactly 1.  Must not
  *            overlap prio (the gathered priorities are parked there).
  *   ws     : psamp_is_weights_workspace_size(k) bytes (256 B up to 8192
- *            samples, plus 4 B per 4096 above; 0 for k = 0), zero-filled
- *            once after allocation; the calls keep it consistent, whatever
- *            sizes share it.  One ws must not serve two calls that may run
- *            at the same time.  Up to 8192 samples the kernel's blocks (at
- *            most 8) wait for one another's minima: a wait that does not end
- *            within about a second sets bit 0 of the workspace errors
+ *            samples; above, 8448 B plus 4 B per 4096 samples; 0 for
+ *            k = 0), zero-filled once after allocation; the calls keep it
+ *            consistent, whatever sizes share it.  One ws must not serve two
+ *            calls that may run at the same time.  One kernel whose blocks
+ *            wait for one another's minima serves up to 8192 samples (at
+ *            most 8 blocks of 1024) and, above, as long as its blocks of
+ *            4096 samples (at most 1024) can all be resident on the device
+ *            at once; larger batches take two kernels.  A wait that does not
+ *            end within about a second (blocks kept from running by other
+ *            work on the device) sets bit 0 of the workspace errors
  *            (psamp_workspace_errors) instead of hanging.
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (beta < 0 or not finite,
  * alpha <= 0), E_WORKSPACE, E_LAUNCH.

@@ -9,12 +9,12 @@
 // non-negative float bits), the power in double via log2 / exp2, and the
 // largest weight comes out as exactly 1.
 //
-// Small batches (k <= 8192) run in one kernel: blocks of 1024 samples gather
-// their priorities on different CUs at once and exchange their minima.
-// Larger ones use two kernels: per-block minima with a last-block
-// reduction (the gathered priorities are parked in the output array), then
-// the weights from the parked values -- the priority array is gathered
-// once.
+// One kernel while its blocks can all be resident at once: blocks of 1024
+// (k <= 8192) or 4096 samples gather their priorities on different CUs at
+// once and exchange their minima.  Larger batches use two kernels:
+// per-block minima with a last-block reduction (the gathered priorities are
+// parked in the output array), then the weights from the parked values --
+// the priority array is gathered once either way.
 #include "psamp_device.h"
 #include "psamp_host.h"
 
@@ -23,7 +23,7 @@ namespace psamp {
 constexpr int kIswThreads = 1024;
 constexpr int kIswPerThread = 4;
 constexpr int kIswBlock = kIswThreads * kIswPerThread;   // samples per block
-constexpr int64_t kIswSingleMax = 8192;            // one kernel up to this many samples
+constexpr int64_t kIswSingleMax = 8192;            // blocks of 1024 samples up to this many
 constexpr int kIswHdrWords = 64;                        // 256-byte header (uint32)
 constexpr int kIswSpinLimit = 1 << 21;                  // bounded waits (about a second)
 
@@ -45,57 +45,77 @@ __device__ __forceinline__ int64_t clamp_idx(int32_t i, int64_t n) {
     return i < 0 ? 0 : (i >= n ? n - 1 : (int64_t)i);
 }
 
-// k <= 8192: one sample per thread in blocks of 1024 (at most 8 blocks, so
-// all of them are resident at once).  Each block gathers its priorities
-// (one round trip for the indices, one for the priorities), publishes its
-// minimum in its slot, tagged with this call's number, and polls the other
-// blocks' slots until every one carries the tag; then each block writes its
-// own weights from the keys it holds in registers.  Block 0 advances the
-// call number once it has seen every slot -- by then every block has read
-// it.  No data but the minima crosses between blocks, so no fences.  Waits
-// are bounded (error bit 1 of the workspace header instead of a hang).
-// (One workgroup gathering all 8192 took 12 us: a single CU's request rate
-// bounds 8192 scattered loads; a last-block variant that formed every
-// weight in one workgroup, 10 us.)
-// Workspace header, as 64-bit words: [2] error bits (where
-// psamp_workspace_errors reads them), [4] the small path's call number,
-// [8, 16) its per-block slots; the two-kernel path uses the first two
-// 32-bit words and the words from byte 256 on.
+// The one-kernel path: PT samples per thread in blocks of 1024 threads,
+// nblocks <= 64 * PW blocks, all resident at once (the host checks).  Each
+// block gathers its priorities (one round trip for the indices, one for the
+// priorities), publishes its minimum in its slot, tagged with this call's
+// number, and polls the other blocks' slots until every one carries the
+// tag; then each block writes its own weights from the keys it holds in
+// registers.  Block 0 advances the call number once it has seen every slot
+// -- by then every block has read it.  No data but the minima crosses
+// between blocks, so no fences.  Waits are bounded (bit 0 of the
+// workspace's error word instead of a hang).
+// (k <= 8192: one workgroup gathering all 8192 took 12 us -- a single CU's
+// request rate bounds 8192 scattered loads; a last-block variant that
+// formed every weight in one workgroup, 10 us.  2^20 samples: the two
+// kernels took 26 us.)
+// Workspace, as 64-bit words: [2] error bits (where psamp_workspace_errors
+// reads them), [4] the call number, [8, 16) the slots of blocks of 1024
+// samples, [32, 32 + kIswExMax) those of blocks of 4096; the two-kernel path
+// uses the first two 32-bit words and the 32-bit words from kIswPartWord on.
 constexpr int kIswErrWord = 2;
 constexpr int kIswCallWord = 4;
-constexpr int kIswSlotWord0 = 8;
+constexpr int kIswSlotSmall = 8;
+constexpr int kIswSlotBig = 32;
+constexpr int kIswExMax = 1024;                              // blocks of the one-kernel path
+constexpr int kIswPartWord = kIswHdrWords + 2 * kIswExMax;   // 32-bit index
 
-template <class P>
-__global__ __launch_bounds__(kIswThreads) void k_isw_small(const P* __restrict__ prio, int64_t n,
-                                                           const int32_t* __restrict__ idx,
-                                                           int64_t k, double e,
-                                                           uint64_t* __restrict__ ws, int nblocks,
-                                                           float* __restrict__ out) {
+template <class P, int PT, int PW>
+__global__ __launch_bounds__(kIswThreads) void k_isw_exch(const P* __restrict__ prio, int64_t n,
+                                                          const int32_t* __restrict__ idx,
+                                                          int64_t k, double e,
+                                                          uint64_t* __restrict__ ws, int slot0,
+                                                          int nblocks, float* __restrict__ out) {
     __shared__ MathLds M;
     __shared__ uint32_t s_min;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const MathRegs mr = math_load(tid);
     if (tid == 0) s_min = 0xFFFFFFFFu;
-    const int64_t i = (int64_t)blockIdx.x * kIswThreads + tid;
+    const int64_t b0 = (int64_t)blockIdx.x * kIswThreads * PT;
     const uint32_t call = (uint32_t)load_agent(&ws[kIswCallWord]);
-    uint32_t key = 0xFFFFFFFFu;
-    if (i < k) key = prio_key<P>(prio[clamp_idx(idx[i], n)]);
+    uint32_t key[PT];
+    uint32_t mk = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int64_t i = b0 + j * kIswThreads + tid;
+        key[j] = i < k ? prio_key<P>(prio[clamp_idx(idx[i], n)]) : 0xFFFFFFFFu;
+        mk = min_(mk, key[j]);
+    }
     math_store(&M, tid, mr);
-    const uint32_t mn = wave_min_u32(key);
+    const uint32_t mn = wave_min_u32(mk);
     __syncthreads();
     if (lane == 0) atomicMin(&s_min, mn);
     __syncthreads();
     if (nblocks > 1 && tid < kWave) {
-        const uint64_t tag = (uint64_t)(call + 1u) << 32;
-        if (tid == 0) store_agent(&ws[kIswSlotWord0 + blockIdx.x], tag | s_min);
-        // every slot of this call (lane b polls slot b)
-        const bool need = lane < nblocks;
-        const uint64_t* slot = &ws[kIswSlotWord0 + (need ? lane : 0)];
-        uint64_t w = load_agent(slot);
+        const uint32_t tag = call + 1u;
+        if (tid == 0) store_agent(&ws[slot0 + blockIdx.x], ((uint64_t)tag << 32) | s_min);
+        // every slot of this call (lane l polls slots l, l + 64, ...)
+        bool need[PW];
+        uint64_t w[PW];
+#pragma unroll
+        for (int m = 0; m < PW; ++m) {
+            const int b = m * kWave + lane;
+            need[m] = b < nblocks;
+            w[m] = load_agent(&ws[slot0 + (need[m] ? b : 0)]);
+        }
         int limit = kIswSpinLimit;
         asm volatile("" : "+s"(limit));
-        for (int polls = 0; __any(need && (w >> 32) != (tag >> 32)); ++polls) {
+        for (int polls = 0;; ++polls) {
+            bool pend = false;
+#pragma unroll
+            for (int m = 0; m < PW; ++m) pend |= need[m] && (uint32_t)(w[m] >> 32) != tag;
+            if (!__any(pend)) break;
             if (polls > limit) {
                 if (lane == 0)
                     __hip_atomic_fetch_or(&ws[kIswErrWord], (uint64_t)1, __ATOMIC_RELAXED,
@@ -103,18 +123,28 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_small(const P* __restrict__
                 break;
             }
             __builtin_amdgcn_s_sleep(1);
-            w = load_agent(slot);
+#pragma unroll
+            for (int m = 0; m < PW; ++m)
+                if (need[m] && (uint32_t)(w[m] >> 32) != tag)
+                    w[m] = load_agent(&ws[slot0 + m * kWave + lane]);
         }
-        const uint32_t g = wave_min_u32(need ? (uint32_t)w : 0xFFFFFFFFu);
+        uint32_t g = 0xFFFFFFFFu;
+#pragma unroll
+        for (int m = 0; m < PW; ++m) g = min_(g, need[m] ? (uint32_t)w[m] : 0xFFFFFFFFu);
+        g = wave_min_u32(g);
         if (lane == 0) {
             s_min = min_(s_min, g);
-            if (blockIdx.x == 0) store_agent(&ws[kIswCallWord], (uint64_t)(call + 1u));
+            if (blockIdx.x == 0) store_agent(&ws[kIswCallWord], (uint64_t)tag);
         }
     }
     __syncthreads();
     const double pmin = prio_val<P>(s_min);
     const double lpmin = pmin > 0.0 ? log2_sig32(pmin, &M) : 0.0;
-    if (i < k) out[i] = is_weight(pmin, lpmin, prio_val<P>(key), e, &M);
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int64_t i = b0 + j * kIswThreads + tid;
+        if (i < k) out[i] = is_weight(pmin, lpmin, prio_val<P>(key[j]), e, &M);
+    }
 }
 
 // Pass 1: per-block minimum; the last block to finish reduces them into
@@ -144,7 +174,7 @@ __global__ __launch_bounds__(kIswThreads) void k_isw_min(const P* __restrict__ p
     atomicMin(&s_min, mn);
     __syncthreads();
     uint32_t* hdr = ws;
-    uint32_t* part = ws + kIswHdrWords;
+    uint32_t* part = ws + kIswPartWord;
     if (tid == 0) {
         part[blockIdx.x] = s_min;
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
@@ -192,18 +222,28 @@ static psamp_status launch_isw(const void* prio, int64_t n, const int32_t* idx, 
                                double e, float* out, void* ws, hipStream_t st) {
     if (k <= kIswSingleMax) {
         const int nb = (int)ceil_div(k, kIswThreads);
-        if (trace_enabled()) trace_launch("k_isw_small", nb, kIswThreads, k);
-        hipLaunchKernelGGL(k_isw_small<P>, dim3(nb), dim3(kIswThreads), 0, st, (const P*)prio, n,
-                           idx, k, e, (uint64_t*)ws, nb, out);
+        if (trace_enabled()) trace_launch("k_isw_exch<1>", nb, kIswThreads, k);
+        hipLaunchKernelGGL((k_isw_exch<P, 1, 1>), dim3(nb), dim3(kIswThreads), 0, st,
+                           (const P*)prio, n, idx, k, e, (uint64_t*)ws, kIswSlotSmall, nb, out);
         return launch_status();
     }
-    const int nb = (int)ceil_div(k, kIswBlock);
+    const int64_t nb = ceil_div(k, kIswBlock);
+    constexpr int kPW = kIswExMax / kWave;
+    if (nb <= kIswExMax &&
+        nb <= resident_grid(reinterpret_cast<const void*>(&k_isw_exch<P, kIswPerThread, kPW>),
+                            kIswThreads)) {
+        if (trace_enabled()) trace_launch("k_isw_exch<4>", nb, kIswThreads, k);
+        hipLaunchKernelGGL((k_isw_exch<P, kIswPerThread, kPW>), dim3((unsigned)nb),
+                           dim3(kIswThreads), 0, st, (const P*)prio, n, idx, k, e, (uint64_t*)ws,
+                           kIswSlotBig, (int)nb, out);
+        return launch_status();
+    }
     if (trace_enabled()) trace_launch("k_isw_min+apply", nb, kIswThreads, k);
-    hipLaunchKernelGGL(k_isw_min<P>, dim3(nb), dim3(kIswThreads), 0, st, (const P*)prio, n, idx, k,
-                       (uint32_t*)ws, nb, reinterpret_cast<uint32_t*>(out));
+    hipLaunchKernelGGL(k_isw_min<P>, dim3((unsigned)nb), dim3(kIswThreads), 0, st, (const P*)prio,
+                       n, idx, k, (uint32_t*)ws, (int)nb, reinterpret_cast<uint32_t*>(out));
     psamp_status s = launch_status();
     if (s != PSAMP_OK) return s;
-    hipLaunchKernelGGL(k_isw_apply<P>, dim3(nb), dim3(kIswThreads), 0, st, k, e,
+    hipLaunchKernelGGL(k_isw_apply<P>, dim3((unsigned)nb), dim3(kIswThreads), 0, st, k, e,
                        (const uint32_t*)ws, out);
     return launch_status();
 }
@@ -216,7 +256,7 @@ extern "C" size_t psamp_is_weights_workspace_size(int64_t k) {
     if (k < 0 || k > kMaxN) return 0;
     if (k == 0) return 0;
     if (k <= kIswSingleMax) return (size_t)kIswHdrWords * 4;   // call number, error bits, 8 slots
-    return (size_t)kIswHdrWords * 4 + (size_t)ceil_div(k, kIswBlock) * 4;
+    return (size_t)kIswPartWord * 4 + (size_t)ceil_div(k, kIswBlock) * 4;
 }
 
 extern "C" psamp_status psamp_is_weights(const void* prio, psamp_dtype prio_t, int64_t n,

@@ -307,11 +307,11 @@ static psamp_status launch_per_round(void* prio, int64_t n, double alpha, double
 
 using namespace psamp;
 
+// The scan's workspace: the fused kernel keeps its draw minima in the
+// header, and the three-kernel path forms the weights from the scan's slots.
 extern "C" size_t psamp_per_round_workspace_size(int64_t n, int64_t k) {
-    const size_t a = psamp_build_cdf_workspace_size(n);
-    const size_t b = psamp_is_weights_workspace_size(k);
-    if (a == 0) return 0;
-    return a + ((b + 255) / 256) * 256;
+    if (k < 0 || k > kMaxN) return 0;
+    return psamp_build_cdf_workspace_size(n);
 }
 
 extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, double beta,

@@ -54,12 +54,13 @@ def test_workspace_sizes(L):
     assert L.psamp_build_cdf_workspace_size(64 * 1024) == 256 + 4096
     assert L.psamp_build_cdf_workspace_size(64 * 1024 + 1) == 256 + 2 * 4096
     assert L.psamp_build_cdf_workspace_size(1 << 24) == 256 + 64 * (1 << 14)
-    assert L.psamp_per_round_workspace_size(262144, 8192) == 256 + 64 * 256 + 256
-    assert L.psamp_per_round_workspace_size(1 << 20, 1 << 20) == 256 + 64 * 1024 + 256 + 4 * 256
+    assert L.psamp_per_round_workspace_size(262144, 8192) == 256 + 64 * 256
+    assert L.psamp_per_round_workspace_size(1 << 20, 1 << 20) == 256 + 64 * 1024
     assert L.psamp_is_weights_workspace_size(8192) == 256
     assert L.psamp_is_weights_workspace_size(1) == 256
     assert L.psamp_is_weights_workspace_size(0) == 0
-    assert L.psamp_is_weights_workspace_size(1 << 20) == 256 + 4 * 256
+    assert L.psamp_is_weights_workspace_size(1 << 20) == 256 + 8 * 1024 + 4 * 256
+    assert L.psamp_is_weights_workspace_size(8193) == 256 + 8 * 1024 + 4 * 3
     assert L.psamp_scatter_workspace_size(262144, 8192) == 262144 * 4
     assert L.psamp_segtree_cap_pow2(500000) == 524288
     assert L.psamp_segtree_cap_pow2(100000) == 131072

@@ -325,23 +325,28 @@ def test_sample_int_bit_exact(ps, k, strat):
 
 
 def test_is_weights_workspace_reuse(ps):
-    """One workspace across batch sizes on both paths (one kernel up to 8192
-    samples, two above), each call against the oracle's closed form; a block
-    counter left at a stray value is back in step after one call."""
+    """One workspace across batch sizes on all three paths (blocks of 1024
+    samples up to 8192; blocks of 4096 exchanging minima while they can all
+    be resident; two kernels beyond 1024 such blocks), each call against the
+    oracle's closed form; a block counter of the two-kernel path left at a
+    stray value is back in step after one call."""
     n = 262144
     p = si.generic_f32(n, 91, "exp")
     Pd = dev(p)
-    ws = ps.Workspace(ps.is_weights_workspace_size(1 << 16))
+    big = (4 << 20) + 5
+    ws = ps.Workspace(ps.is_weights_workspace_size(big))
     rng = np.random.default_rng(4)
-    for step, k in enumerate([8192, 1000, 5000, 1 << 16, 1024, 8193, 3, 8192]):
-        if step == 6:
+    for step, k in enumerate([8192, 1000, 5000, 1 << 16, big, 1024, 8193, 3, 8192, 70001,
+                              big, 1 << 20, 4097]):
+        if step == 10:
             ws.buf.view(torch.int32)[0] = 5         # stray counter: this call is not checked
-            ps.is_weights(Pd, dev(rng.integers(0, n, k).astype(np.int32)), 0.6, 0.4, ws=ws)
+            ps.is_weights(Pd, dev(rng.integers(0, n, big).astype(np.int32)), 0.6, 0.4, ws=ws)
         idx = np.sort(rng.integers(0, n, k)).astype(np.int32)
         w_g = host(ps.is_weights(Pd, dev(idx), 0.6, 0.4, ws=ws))
         w_o = oracle.is_weights(p, 0.6, 1.0, idx, 0.4)
         assert rel_err(w_g, w_o) <= 1e-6, (step, k)
         assert w_g.max() == 1.0
+    assert ws.errors() == 0
 
 
 def test_per_mid_cfg_32_rounds(ps):
