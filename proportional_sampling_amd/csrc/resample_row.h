@@ -45,26 +45,52 @@ __device__ __forceinline__ double res_threshold(int k, float ub, float Pf, float
     return (double)(POW2 ? __fmul_rn(a, invP) : __fdiv_rn(a, Pf));
 }
 
-// #{k in [0, P) : t_k <= x}.  fl(k + u) is within 2^-11 of k + u (k < 2^13)
-// and the division or scaling adds one more rounding, so t_k P lies within
-// about 2^-11 of k + u: at most one k can be counted differently by the
-// estimate floor(x P - u) + 1, and one check on each side fixes it.
+// #{k in [0, P) : t_k <= x}.  fl(k + u) is within 2^-12 of k + u (k < 2^13)
+// and t_k P equals it for a power-of-two P (else the division adds at most
+// 2^-11 more), so t_k P lies within d = 2^-12 (2^-10) of k + u, and y =
+// x P - u in double within 2^-39 of its exact value.  When y is at least
+// eps = 2^-11 (2^-9) away from every integer, the count is floor(y) + 1
+// clamped to [0, P] with no threshold formed; otherwise at most one k can be
+// counted differently by that estimate, and one check on each side fixes
+// it.  (A wave takes the checks for some lane on a few per cent of the
+// counts.)
 template <bool POW2>
 __device__ __forceinline__ int res_count_le(double x, float ub, float Pf, float invP, int P) {
-    const double e = floor(x * (double)P - (double)ub);
+    constexpr double kEps = POW2 ? 0x1p-11 : 0x1p-9;
+    const double y = x * (double)P - (double)ub;
+    const double e = floor(y);
+    const double fr = y - e;                          // exact (Sterbenz)
     const int k = !(e >= 0.0) ? 0 : (e >= (double)P ? P : (int)e + 1);
+    const bool sure = (fr >= kEps && fr <= 1.0 - kEps) || e >= (double)P || e <= -2.0;
+    if (__builtin_expect(sure, 1)) return k;
     const bool over = k > 0 && res_threshold<POW2>(k - 1, ub, Pf, invP) > x;
     const bool under = k < P && res_threshold<POW2>(k, ub, Pf, invP) <= x;
     return k - (over ? 1 : 0) + (under ? 1 : 0);
 }
 
-// Workgroup scratch of the row resampler (R rows of 1024 particles).
+// exp(x) for x <= 0 (finite; a NaN passes through): exp2_tab without its
+// clamp and NaN select, the same bits -- for x below the range that the
+// clamp guards the integer conversion saturates and ldexp still gives 0.
+__device__ __forceinline__ double exp_nonpos(double x, const MathLds* M) {
+    const double y = x * kLog2e;
+    const double N = rint(y * 64.0);
+    const double f = fma(N, -1.0 / 64.0, y);
+    const int Ni = (int)N;
+    const double g = f * kLn2;
+    double q = fma(g, 1.0 / 120.0, 1.0 / 24.0);
+    q = fma(g, q, 1.0 / 6.0);
+    q = fma(g, q, 0.5);
+    q = fma(g, q, 1.0);
+    const double s = M->exp_tab[Ni & 63];
+    return ldexp(fma(s, g * q, s), Ni >> 6);
+}
+
 template <int R>
 struct ResLds {
     // first-offspring marks: O[k] = j + 1 if particle j's offspring start at k
     __attribute__((aligned(16))) uint16_t O[R * kResThreads * 4];
     uint32_t s_wm[4][R];
-    double s_last[4][R];
+    uint32_t s_lastk[4][R];
     double s_wtot[4][R];
     double s_wmax[4][R];
     float s_max[4];
@@ -105,7 +131,7 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const double e = (v[r][c] == ninf) ? 0.0 : exp_d((double)v[r][c] - m, M);
+            const double e = (v[r][c] == ninf) ? 0.0 : exp_nonpos((double)v[r][c] - m, M);
             q[r][c] = e;
             ssum = ssum + e;
         }
@@ -130,30 +156,38 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
 
     // ancestors: particle j takes k in [#{t <= M_{j-1}}, #{t <= M_j}); the
     // last particle also every k above.  O[k] = j + 1 at the first k of each
-    // non-empty range, 0 elsewhere.  prev[r]: M of the element before this
-    // thread's first element of row r.
-    double prev[R];
+    // non-empty range, 0 elsewhere.  kc: the counts at this thread's values;
+    // kp[r]: the count at the element before its first element of row r
+    // (the neighbour's last count, through DPP and, across waves and rows,
+    // LDS).
+    const float Pf = (float)Pi;
+    const float invP = 1.0f / Pf;              // exact when POW2
+    uint32_t kc[R][4];
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const int j = r * ROW + 4 * tid + c;
+            kc[r][c] = (uint32_t)((j >= Pi - 1) ? Pi : res_count_le<POW2>(q[r][c], ub, Pf, invP, Pi));
+        }
+    uint32_t kp[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        prev[r] = wave_shr1(q[r][3]);
-        if (lane == kWave - 1) L.s_last[wave][r] = q[r][3];
+        kp[r] = dpp32<kWaveShr1, 0xF, true>(kc[r][3]);
+        if (lane == kWave - 1) L.s_lastk[wave][r] = kc[r][3];
         *reinterpret_cast<uint2*>(&L.O[r * ROW + 4 * tid]) = make_uint2(0u, 0u);
     }
     __syncthreads();
 #pragma unroll
-    for (int r = 0; r < R; ++r)
-        if (lane == 0)
-            prev[r] = wave > 0 ? L.s_last[wave - 1][r] : (r > 0 ? L.s_last[3][r - 1] : 0.0);
-    const float Pf = (float)Pi;
-    const float invP = 1.0f / Pf;              // exact when POW2
-#pragma unroll
     for (int r = 0; r < R; ++r) {
+        if (lane == 0)
+            kp[r] = wave > 0 ? L.s_lastk[wave - 1][r] : (r > 0 ? L.s_lastk[3][r - 1] : 0u);
         const int j0 = r * ROW + 4 * tid;
-        int k0 = j0 == 0 ? 0 : res_count_le<POW2>(prev[r], ub, Pf, invP, Pi);
+        uint32_t k0 = j0 == 0 ? 0u : kp[r];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int j = j0 + c;
-            const int k1 = (j >= Pi - 1) ? Pi : res_count_le<POW2>(q[r][c], ub, Pf, invP, Pi);
+            const uint32_t k1 = kc[r][c];
             if (j < Pi && k1 > k0) L.O[k0] = (uint16_t)(j + 1);
             k0 = k1 > k0 ? k1 : k0;
         }
