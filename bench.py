@@ -97,6 +97,31 @@ class PerMid:
             ps.is_weights(self.p, self.idx, self.alpha, self.beta, out=self.w, ws=self.iws)
             ps.scatter_lww(self.p, self.idx, self.v[r], grouped=True)
 
+    def per_call_us(self, reps=200):
+        """Each of the four calls alone, back to back, on the chain's current
+        priorities (the CDF built from them first); the sample call's draws
+        per second is the sample-only rate."""
+        ps, torch = self.ps, self.torch
+        ps.build_cdf(self.p, self.alpha, cdf=self.cdf, total=self.tot, ws=self.ws)
+        ps.sample(self.cdf, self.tot, self.U[0], stratified=True, out=self.idx)
+        calls = {
+            "build_cdf": lambda: ps.build_cdf(self.p, self.alpha, cdf=self.cdf, total=self.tot,
+                                              ws=self.ws),
+            "sample": lambda: ps.sample(self.cdf, self.tot, self.U[0], stratified=True,
+                                        out=self.idx),
+            "is_weights": lambda: ps.is_weights(self.p, self.idx, self.alpha, self.beta,
+                                                out=self.w, ws=self.iws),
+            # rewrites the drawn priorities with the same values every time
+            "scatter_lww": lambda: ps.scatter_lww(self.p, self.idx, self.v[0], grouped=True),
+        }
+        # 32 calls per captured graph, so that host launches do not bound them
+        def graph_us(fn, per=32):
+            g = capture(torch, lambda: [fn() for _ in range(per)])
+            return loop_us(torch, g.replay, max(1, reps // per)) / per
+        out = {k: round(graph_us(fn), 3) for k, fn in calls.items()}
+        out["sample_only_indices_per_s"] = round(self.k / (out["sample"] * 1e-6), 1)
+        return out
+
     def algo_bytes(self, name):
         n, k = self.n, self.k
         return {
@@ -503,6 +528,7 @@ def main():
                              "indices_per_s": round(draws / eager_s, 1)},
              "separate_calls": {"ms_per_step": round(1e3 * sep_s / args.steps, 4),
                                 "indices_per_s": round(draws / sep_s, 1)}}
+    extra["separate_calls"]["per_call_us"] = work.per_call_us()
     if not args.no_extra:
         extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])
         extra["sumtree"] = sumtree_bench(ps, torch)
