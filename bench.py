@@ -114,11 +114,7 @@ class PerMid:
             # rewrites the drawn priorities with the same values every time
             "scatter_lww": lambda: ps.scatter_lww(self.p, self.idx, self.v[0], grouped=True),
         }
-        # 32 calls per captured graph, so that host launches do not bound them
-        def graph_us(fn, per=32):
-            g = capture(torch, lambda: [fn() for _ in range(per)])
-            return loop_us(torch, g.replay, max(1, reps // per)) / per
-        out = {k: round(graph_us(fn), 3) for k, fn in calls.items()}
+        out = {k: round(graph_us(torch, fn, reps), 3) for k, fn in calls.items()}
         out["sample_only_indices_per_s"] = round(self.k / (out["sample"] * 1e-6), 1)
         return out
 
@@ -179,6 +175,43 @@ def capture(torch, fn):
         fn()
     torch.cuda.synchronize()
     return g
+
+
+def graph_us(torch, fn, reps=200, per=32):
+    """Average time of one call of fn, from a HIP graph of `per` calls
+    replayed back to back (host launches do not bound short calls)."""
+    g = capture(torch, lambda: [fn() for _ in range(per)])
+    return loop_us(torch, g.replay, max(1, reps // per)) / per
+
+
+def small_bench(ps, torch):
+    """The scan at the two sizes the PR page times it (B = 8192 and 262144:
+    7.5 and 7.2 us there, on a GPU it does not name -- context, not a
+    target), and the PER-small update (B = 8192, 1024 stratified draws, IS
+    weights) as one fused call."""
+    import synthetic_inputs as si
+    out = {}
+    for n in (8192, 262144):
+        p = torch.from_numpy(si.generic_f32(n, n + 5, "exp")).cuda()
+        cdf = torch.empty(n, dtype=torch.float64, device="cuda")
+        tot = torch.empty(1, dtype=torch.float64, device="cuda")
+        ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+        out[f"build_cdf_{n}_us"] = round(graph_us(torch, lambda: ps.build_cdf(
+            p, 0.6, cdf=cdf, total=tot, ws=ws)), 3)
+    d = si.per_small()
+    P = torch.from_numpy(d["p"]).cuda()
+    U = torch.from_numpy(d["U"]).cuda()
+    n, k = P.numel(), U.numel()
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    w = torch.empty(k, dtype=torch.float32, device="cuda")
+    cdf = torch.empty(n, dtype=torch.float64, device="cuda")
+    tot = torch.empty(1, dtype=torch.float64, device="cuda")
+    rws = ps.Workspace(ps.per_round_workspace_size(n, k))
+    us = graph_us(torch, lambda: ps.per_round(P, U, d["alpha"], d["beta"], None, out_idx=idx,
+                                              out_w=w, cdf=cdf, total=tot, ws=rws))
+    out["per_small_update_us"] = round(us, 3)
+    out["per_small_indices_per_s"] = round(k / (us * 1e-6), 1)
+    return out
 
 
 def timed_steps(torch, fn, steps):
@@ -529,6 +562,7 @@ def main():
              "separate_calls": {"ms_per_step": round(1e3 * sep_s / args.steps, 4),
                                 "indices_per_s": round(draws / sep_s, 1)}}
     extra["separate_calls"]["per_call_us"] = work.per_call_us()
+    extra["small"] = small_bench(ps, torch)
     if not args.no_extra:
         extra["scan_sweep"] = scan_sweep(ps, torch, [1 << 22, 1 << 23, 1 << 24, 1 << 25, 1 << 26])
         extra["sumtree"] = sumtree_bench(ps, torch)
