@@ -37,6 +37,19 @@ namespace psamp {
 constexpr int kBuildThreads = 256;
 constexpr int kBuildLevels = 11;                 // levels per build pass
 constexpr int kUpdThreads = 1024;
+constexpr int kUpdWaves = kUpdThreads / kWave;
+static_assert(256 * kUpdWaves == 4 * kUpdThreads, "the radix prefix takes 4 counts per thread");
+
+// Inclusive sum over the 64 lanes (uint32; DPP rows, then across rows).
+__device__ __forceinline__ uint32_t wave_incl_u32(uint32_t x) {
+    x += dpp32<kRowShr1, 0xF, true>(x);
+    x += dpp32<kRowShr2, 0xF, true>(x);
+    x += dpp32<kRowShr4, 0xF, true>(x);
+    x += dpp32<kRowShr8, 0xF, true>(x);
+    x += dpp32<kRowBcast15, 0xA, false>(x);
+    x += dpp32<kRowBcast31, 0xC, false>(x);
+    return x;
+}
 constexpr int kMaxDepth = 30;                    // cap <= 2^30
 constexpr int kSampleTreeThreads = 256;
 constexpr int kSampleTreeThreadsBig = 1024;      // large batches: fewer copies of the top levels
@@ -99,6 +112,8 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
     V* __restrict__ tree, int64_t cap, int D, const int32_t* __restrict__ idx,
     const P* __restrict__ prio, int m, double alpha) {
     __shared__ uint64_t keys[kUpdThreads];
+    __shared__ uint32_t hist[256 * kUpdWaves];              // (digit, wave) counts, then offsets
+    __shared__ uint32_t hsum[kUpdWaves];
     __shared__ uint32_t wcount[kUpdThreads / kWave];
     __shared__ int32_t wl[kUpdThreads];                  // winner leaves, ascending
     __shared__ int32_t wj[kUpdThreads];                  // their batch positions
@@ -112,27 +127,55 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
     const int lane = tid & 63;
     if (sizeof(P) == 4 && sizeof(V) == 4) math_lds_fill(&M, tid, kUpdThreads);
 
-    // 1. keys = (leaf << 32) | batch position; out-of-range entries sort last.
+    // 1. keys = (leaf << 32) | batch position, sorted.  A stable LSD radix
+    // sort on the leaf (8-bit digits; an out-of-range entry takes the key
+    // cap, above every leaf, and keeps its all-ones word) leaves equal
+    // leaves in batch order, i.e. the array sorted by the whole key: per
+    // pass, ballots rank each key among the lanes of its wave with the same
+    // digit, and a digit-major prefix over the per-wave counts places it --
+    // five barriers a pass and ceil((D + 1) / 8) passes, against the 55
+    // compare-exchange steps of a bitonic network.
     uint64_t key = ~0ull;
     if (tid < m) {
         const int32_t l = idx[tid];
         if (l >= 0 && (int64_t)l < cap) key = ((uint64_t)(uint32_t)l << 32) | (uint32_t)tid;
     }
-    keys[tid] = key;
-    __syncthreads();
-    for (int size = 2; size <= kUpdThreads; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const int j = tid ^ stride;
-            if (j > tid) {
-                const uint64_t a = keys[tid];
-                const uint64_t b = keys[j];
-                const bool up = (tid & size) == 0;
-                if ((a > b) == up) {
-                    keys[tid] = b;
-                    keys[j] = a;
-                }
+    {
+        const uint64_t lane_lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+        const int passes = (D + 1 + 7) / 8;
+        for (int ps = 0; ps < passes; ++ps) {
+            const uint32_t lp = key == ~0ull ? (uint32_t)cap : (uint32_t)(key >> 32);
+            const uint32_t d = (lp >> (8 * ps)) & 255u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) hist[4 * tid + c] = 0u;
+            __syncthreads();
+            uint64_t peers = ~0ull;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint64_t bal = __ballot((d >> b) & 1u);
+                peers &= ((d >> b) & 1u) ? bal : ~bal;
+            }
+            const uint32_t rank = (uint32_t)__popcll(peers & lane_lt);
+            if (rank == 0) hist[d * kUpdWaves + wave] = (uint32_t)__popcll(peers);
+            __syncthreads();
+            uint32_t h[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) h[c] = hist[4 * tid + c];
+            const uint32_t loc = (h[0] + h[1]) + (h[2] + h[3]);
+            const uint32_t inc = wave_incl_u32(loc);
+            if (lane == kWave - 1) hsum[wave] = inc;
+            __syncthreads();
+            uint32_t ex = inc - loc;
+            for (int w2 = 0; w2 < wave; ++w2) ex += hsum[w2];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                hist[4 * tid + c] = ex;
+                ex += h[c];
             }
             __syncthreads();
+            keys[hist[d * kUpdWaves + wave] + rank] = key;
+            __syncthreads();
+            key = keys[tid];
         }
     }
 
