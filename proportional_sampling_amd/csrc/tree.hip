@@ -13,7 +13,8 @@
 // when two updates share an ancestor (a thread can read a stale sibling and
 // overwrite a correct parent) and on repeated indices.  Here one 1024-thread
 // workgroup handles a batch of up to 1024 updates deterministically:
-//   1. sort the (leaf, batch position) keys in LDS (bitonic);
+//   1. sort the (leaf, batch position) keys in LDS (stable radix sort on the
+//      leaf);
 //   2. keep the last entry of each run of equal leaves (largest batch
 //      position: last write wins);
 //   3. each winning leaf's thread prefetches the old values of all siblings
