@@ -110,7 +110,7 @@ psamp_status psamp_build_cdf(const void* prio, psamp_dtype prio_t, int64_t n,
  *                computed exactly, so integer mode is bit-exact.
  *   out_idx    : k int32 indices (non-decreasing in i when stratified).
  *   k          : 0 <= k <= 2^31 - 1 (0 is a no-op).
- * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (stratified not 0/1), E_LAUNCH.
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (stratified not 0/1), E_ALIGN, E_LAUNCH.
  * ---------------------------------------------------------------------- */
 psamp_status psamp_sample(const void* cdf, psamp_dtype cdf_t, int64_t n,
                           const void* total, const void* u, psamp_dtype u_t,
@@ -159,7 +159,7 @@ psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_
  *            work on the device) sets bit 0 of the workspace errors
  *            (psamp_workspace_errors) instead of hanging.
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (beta < 0 or not finite,
- * alpha <= 0), E_WORKSPACE, E_LAUNCH.
+ * alpha <= 0), E_WORKSPACE, E_ALIGN, E_LAUNCH.
  * ---------------------------------------------------------------------- */
 size_t psamp_is_weights_workspace_size(int64_t k);
 psamp_status psamp_is_weights(const void* prio, psamp_dtype prio_t, int64_t n,
@@ -181,7 +181,7 @@ psamp_status psamp_is_weights(const void* prio, psamp_dtype prio_t, int64_t n,
 int64_t psamp_segtree_cap_pow2(int64_t capacity);
 
 /* Build every node from n_valid priorities (0 < n_valid <= cap_pow2 <= 2^30).
- * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_LAUNCH. */
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_ALIGN, E_LAUNCH. */
 psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
                                  const void* prio, psamp_dtype prio_t, int64_t n_valid,
                                  double alpha, void* stream);
@@ -194,7 +194,7 @@ psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int64_t cap_pow
  * leaves.  idx_j must lie in [0, cap_pow2) (entries outside are ignored).
  * 1 <= m <= 1024 per call (larger batches: split them; order is kept).
  * ws: psamp_segtree_update_workspace_size(cap_pow2, m) bytes (0 today).
- * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_LAUNCH. */
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_ALIGN, E_LAUNCH. */
 size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m);
 psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
                                   const int32_t* idx, const void* prio,
@@ -206,7 +206,7 @@ psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int64_t cap_po
  * right; the result is clamped to n_valid - 1.  Thresholds: F32 tree --
  * iid t = U_i * root (float), stratified t = (float)(((i + U_i) / k) * root)
  * (double); U64 tree -- the integer formulas of psamp_sample with U32 r_i.
- * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_LAUNCH. */
+ * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_ALIGN, E_LAUNCH. */
 psamp_status psamp_segtree_sample(const void* tree, psamp_dtype tree_t, int64_t cap_pow2,
                                   int64_t n_valid, const void* u, psamp_dtype u_t,
                                   int64_t k, int stratified, int32_t* out_idx, void* stream);
@@ -278,7 +278,7 @@ const float* psamp_replay_total(const psamp_replay* rb);
  *   u_row  : rows floats in [0, 1).
  *   out_anc: rows x P int32, row stride ld_out elements (>= P).
  *   1 <= P <= 8192, 1 <= rows <= 2^31 - 1.
- * Errors: E_NULL, E_SIZE, E_LAUNCH.
+ * Errors: E_NULL, E_SIZE, E_ALIGN, E_LAUNCH.
  * ---------------------------------------------------------------------- */
 psamp_status psamp_resample_rows(const float* logw, int64_t rows, int64_t P,
                                  int64_t ld_in, const float* u_row, int32_t* out_anc,
@@ -324,7 +324,7 @@ psamp_status psamp_pf_step(const float* x, const float* logw, const float* obs,
  * ws: psamp_scatter_workspace_size(n, m) bytes (one uint32 per item, zeroed
  *   once; every call leaves it zeroed again), unless GROUPED.
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM (unknown flag), E_WORKSPACE,
- * E_LAUNCH.
+ * E_ALIGN, E_LAUNCH.
  * ---------------------------------------------------------------------- */
 #define PSAMP_SCATTER_GROUPED 1
 size_t psamp_scatter_workspace_size(int64_t n, int64_t m);
