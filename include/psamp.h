@@ -174,7 +174,9 @@ psamp_status psamp_is_weights(const void* prio, psamp_dtype prio_t, int64_t n,
  * children, recomputed as fl(left + right) ([SEGT] "Operations -- Update").
  * tree_t is PSAMP_F32 (leaves p^alpha rounded to float, sums in float, as
  * on the page) or PSAMP_U64 (leaves q from U32 priorities, exact sums).
- * Leaves n_valid .. cap_pow2-1 are 0.  Memory: 2 * cap_pow2 * sizeof(node).
+ * Leaves n_valid .. cap_pow2-1 are 0.  Memory: 2 * cap_pow2 * sizeof(node);
+ * the tree pointer must be 16-byte aligned (E_ALIGN otherwise), priorities
+ * and index arrays 4-byte aligned.
  * ---------------------------------------------------------------------- */
 /* Capacity rounded up to a power of two ([SEGT] "Tree Layout"); 0 if
  * capacity < 1 or the result would exceed 2^30. */

@@ -99,6 +99,8 @@ def test_sample_validation(L):
     assert f(FAKE, U64, 10, FAKE, FAKE, F32, 10, 1, FAKE, None) == E_DTYPE
     assert f(FAKE, F64, 10, FAKE, FAKE, F32, 0, 1, None, None) == OK      # k = 0: no-op
     assert f(FAKE, F64, 10, None, FAKE, F32, 10, 1, FAKE, None) == E_NULL
+    assert f(FAKE + 4, F64, 10, FAKE, FAKE, F32, 10, 1, FAKE, None) == E_ALIGN
+    assert f(FAKE, F64, 10, FAKE, FAKE, F32, 10, 1, FAKE + 2, None) == E_ALIGN
 
 
 def test_build_cdf_sample_validation(L):
@@ -130,6 +132,8 @@ def test_is_weights_validation(L):
     assert f(FAKE, F32, 10, 0.6, FAKE, 1 << 20, 0.4, FAKE, None, 0, None) == E_WS
     assert f(FAKE, F32, 10, 0.6, FAKE, 0, 0.4, None, None, 0, None) == OK
     assert f(None, F32, 10, 0.6, FAKE, 5, 0.4, FAKE, None, 0, None) == E_NULL
+    assert f(FAKE + 2, F32, 10, 0.6, FAKE, 5, 0.4, FAKE, FAKE, 256, None) == E_ALIGN
+    assert f(FAKE, F32, 10, 0.6, FAKE, 5, 0.4, FAKE, FAKE + 4, 256, None) == E_ALIGN
 
 
 def test_segtree_validation(L):
@@ -147,6 +151,9 @@ def test_segtree_validation(L):
     assert s(FAKE, F32, 1024, 0, FAKE, F32, 4, 0, FAKE, None) == E_SIZE
     assert s(FAKE, F32, 1024, 10, FAKE, U32, 4, 0, FAKE, None) == E_DTYPE
     assert s(FAKE, F32, 1024, 10, FAKE, F32, 4, 3, FAKE, None) == E_PARAM
+    assert s(FAKE + 8, F32, 1024, 10, FAKE, F32, 4, 0, FAKE, None) == E_ALIGN   # tree: 16 B
+    assert u(FAKE + 8, F32, 1024, FAKE, FAKE, F32, 4, 0.6, None, 0, None) == E_ALIGN
+    assert u(FAKE, F32, 1024, FAKE + 2, FAKE, F32, 4, 0.6, None, 0, None) == E_ALIGN
 
 
 def test_resample_and_scatter_validation(L):
@@ -155,11 +162,13 @@ def test_resample_and_scatter_validation(L):
     assert r(FAKE, 4, 8193, 8193, FAKE, FAKE, 8193, None) == E_SIZE
     assert r(FAKE, 0, 4096, 4096, FAKE, FAKE, 4096, None) == E_SIZE
     assert r(None, 4, 4096, 4096, FAKE, FAKE, 4096, None) == E_NULL
+    assert r(FAKE + 2, 4, 4096, 4096, FAKE, FAKE, 4096, None) == E_ALIGN
     sc = L.psamp_scatter_lww
     assert sc(FAKE, F64, 100, FAKE, FAKE, 10, 0, FAKE, 400, None) == E_DTYPE
     assert sc(FAKE, F32, 100, FAKE, FAKE, 10, 0, FAKE, 399, None) == E_WS
     assert sc(FAKE, F32, 100, FAKE, FAKE, 10, 2, FAKE, 400, None) == E_PARAM
     assert sc(FAKE, F32, 100, FAKE, FAKE, 0, 0, None, 0, None) == OK
+    assert sc(FAKE + 2, F32, 100, FAKE, FAKE, 10, 0, FAKE, 400, None) == E_ALIGN
     assert L.psamp_workspace_errors(None, 256, None, None) == E_NULL
     pr = L.psamp_per_round
     wsz = L.psamp_per_round_workspace_size(1000, 10)
