@@ -336,8 +336,10 @@ def test_is_weights_workspace_reuse(ps):
     big = (4 << 20) + 5
     ws = ps.Workspace(ps.is_weights_workspace_size(big))
     rng = np.random.default_rng(4)
+    # ((1 << 20) + 1: 257 blocks of 4096, more than one per CU can be
+    # resident on 256 CUs, so the occupancy check sends it to two kernels)
     for step, k in enumerate([8192, 1000, 5000, 1 << 16, big, 1024, 8193, 3, 8192, 70001,
-                              big, 1 << 20, 4097]):
+                              big, 1 << 20, 4097, (1 << 20) + 1, 1 << 20]):
         if step == 10:
             ws.buf.view(torch.int32)[0] = 5         # stray counter: this call is not checked
             ps.is_weights(Pd, dev(rng.integers(0, n, big).astype(np.int32)), 0.6, 0.4, ws=ws)
