@@ -386,7 +386,7 @@ def resample_bench(ps, torch, reps=50):
     u = torch.from_numpy(d["u_row"]).cuda()
     out = torch.empty_like(lw, dtype=torch.int32)
     fn = lambda: ps.resample_rows(lw, u, out=out)
-    warm = loop_us(torch, fn, reps)
+    warm = graph_us(torch, fn, 128)           # back to back, launched from a graph
     flush = CacheFlush(torch)
     us = cold_us(torch, fn, flush, max(5, reps // 4))
     del flush
@@ -413,7 +413,7 @@ def pf_bench(ps, torch, reps=50):
         fn = lambda: ps.pf_step(t["x"], t["lw"], t["obs"], t["A"], t["C"], t["eps"],
                                 d["sigma_p"], d["sigma_o"], t["u_row"], x_out=xo, logw_out=lo,
                                 anc_out=an)
-        warm = loop_us(torch, fn, reps)
+        warm = graph_us(torch, fn, 128)       # back to back, launched from a graph
         us = cold_us(torch, fn, flush, max(5, reps // 4))
         nbytes = rows * P * (3 * 4 * D + 12) + rows * 4 * (1 + d["obs"].shape[1])
         gbs = nbytes / (us * 1e-6) / 1e9
