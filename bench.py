@@ -321,11 +321,13 @@ def sumtree_bench(ps, torch, rounds=200):
         ps.segtree_update(tree, idx[r], v[r], d["alpha"])
         ps.segtree_sample(tree, nv, U[r], out=out)
 
-    res = {"round_us": round(loop_us(torch, one_round, rounds), 2),
-           "update_us": round(loop_us(torch, lambda: ps.segtree_update(tree, idx[0], v[0],
-                                                                        d["alpha"]), rounds), 2),
-           "sample_us": round(loop_us(torch, lambda: ps.segtree_sample(tree, nv, U[0], out=out),
-                                      rounds), 2)}
+    # each from a HIP graph of 32 calls (rounds r .. r + 31 for the round),
+    # so that Python launches do not bound these short calls
+    res = {"round_us": round(graph_us(torch, one_round, rounds), 2),
+           "update_us": round(graph_us(torch, lambda: ps.segtree_update(tree, idx[0], v[0],
+                                                                         d["alpha"]), rounds), 2),
+           "sample_us": round(graph_us(torch, lambda: ps.segtree_sample(tree, nv, U[0], out=out),
+                                       rounds), 2)}
     res["samples_per_s"] = round(1024 / (res["sample_us"] * 1e-6))
     log(f"sum tree: {res}")
     return res
