@@ -193,8 +193,13 @@ psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int64_t cap_pow
  * (as if the updates were applied one by one in batch order); every
  * ancestor of a changed leaf is recomputed exactly once, after both of its
  * children are final, so the tree stays bit-equal to a fresh build of its
- * leaves.  idx_j must lie in [0, cap_pow2) (entries outside are ignored).
- * 1 <= m <= 1024 per call (larger batches: split them; order is kept).
+ * leaves.  Entries with idx_j outside [0, cap_pow2) are ignored.  An
+ * entry in [n_valid, cap_pow2) -- n_valid being the count later passed to
+ * psamp_segtree_sample -- writes a padding leaf: its mass stays in every
+ * sum above it, and a descent that ends on it is clamped to n_valid - 1, so
+ * callers keep idx_j below n_valid.  0 <= m <= 2^31 - 1 (m = 0 is a no-op
+ * and may pass NULL pointers); the batch is processed in order, in chunks
+ * of 1024 entries, so later entries still win over earlier ones.
  * ws: psamp_segtree_update_workspace_size(cap_pow2, m) bytes (0 today).
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_ALIGN, E_LAUNCH. */
 size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m);

@@ -10,6 +10,7 @@ and fails loudly otherwise.
 from __future__ import annotations
 
 import ctypes as C
+import functools
 import os
 
 import torch
@@ -90,6 +91,22 @@ def _check(fn: str, code: int):
         raise PsampError(fn, code)
 
 
+def _on_stream(fn):
+    """Runs fn with `stream` (a torch stream, or a raw hipStream_t as an int)
+    made torch's current stream, so that every output and workspace fn
+    allocates is allocated, zero-filled and later reused in that stream's
+    order, the order the library's kernels run in."""
+    @functools.wraps(fn)
+    def run(*args, stream=None, **kw):
+        if stream is None:
+            return fn(*args, **kw)
+        if not isinstance(stream, torch.cuda.Stream):
+            stream = torch.cuda.ExternalStream(int(stream))
+        with torch.cuda.stream(stream):
+            return fn(*args, **kw)
+    return run
+
+
 def _stream(stream=None) -> int:
     """The hipStream_t to launch on: the given stream, else torch's current
     stream (read without building a Stream object: calls are launch-bound)."""
@@ -125,6 +142,7 @@ class Workspace:
     def ptr(self) -> int:
         return self.buf.data_ptr()
 
+    @_on_stream
     def errors(self, stream=None) -> int:
         out = C.c_uint64(0)
         _check("psamp_workspace_errors",
@@ -141,6 +159,7 @@ def build_cdf_workspace_size(n: int) -> int:
     return int(lib().psamp_build_cdf_workspace_size(int(n)))
 
 
+@_on_stream
 def build_cdf(prio: torch.Tensor, alpha: float = 1.0, *, cdf: torch.Tensor | None = None,
               total: torch.Tensor | None = None, cdf_dtype=None, ws: Workspace | None = None,
               stream=None):
@@ -164,6 +183,7 @@ def build_cdf(prio: torch.Tensor, alpha: float = 1.0, *, cdf: torch.Tensor | Non
     return cdf, total
 
 
+@_on_stream
 def sample(cdf: torch.Tensor, total: torch.Tensor, u: torch.Tensor, *, stratified: bool = True,
            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """int32 indices: first j with cdf[j] >= t_i, clamped to n-1."""
@@ -180,6 +200,7 @@ def sample(cdf: torch.Tensor, total: torch.Tensor, u: torch.Tensor, *, stratifie
     return out
 
 
+@_on_stream
 def build_cdf_sample(prio: torch.Tensor, u: torch.Tensor, alpha: float = 1.0, *,
                      cdf: torch.Tensor | None = None, total: torch.Tensor | None = None,
                      out: torch.Tensor | None = None, cdf_dtype=None, ws: Workspace | None = None,
@@ -210,6 +231,7 @@ def is_weights_workspace_size(k: int) -> int:
     return int(lib().psamp_is_weights_workspace_size(int(k)))
 
 
+@_on_stream
 def is_weights(prio: torch.Tensor, idx: torch.Tensor, alpha: float, beta: float, *,
                out: torch.Tensor | None = None, ws: Workspace | None = None,
                stream=None) -> torch.Tensor:
@@ -242,6 +264,7 @@ def segtree_empty(capacity: int, kind=torch.float32, device="cuda") -> torch.Ten
     return torch.zeros(2 * cap, dtype=kind, device=device)
 
 
+@_on_stream
 def segtree_build(tree: torch.Tensor, prio: torch.Tensor, alpha: float = 1.0,
                   n_valid: int | None = None, stream=None) -> torch.Tensor:
     cap = tree.numel() // 2
@@ -253,6 +276,7 @@ def segtree_build(tree: torch.Tensor, prio: torch.Tensor, alpha: float = 1.0,
     return tree
 
 
+@_on_stream
 def segtree_update(tree: torch.Tensor, idx: torch.Tensor, prio: torch.Tensor,
                    alpha: float = 1.0, stream=None) -> torch.Tensor:
     cap = tree.numel() // 2
@@ -268,6 +292,7 @@ def segtree_update(tree: torch.Tensor, idx: torch.Tensor, prio: torch.Tensor,
     return tree
 
 
+@_on_stream
 def segtree_sample(tree: torch.Tensor, n_valid: int, u: torch.Tensor, *,
                    stratified: bool = False, out: torch.Tensor | None = None,
                    stream=None) -> torch.Tensor:
@@ -285,6 +310,7 @@ def segtree_sample(tree: torch.Tensor, n_valid: int, u: torch.Tensor, *,
 
 
 # ------------------------------------------------------------ (4) rows
+@_on_stream
 def resample_rows(logw: torch.Tensor, u_row: torch.Tensor, *, out: torch.Tensor | None = None,
                   stream=None) -> torch.Tensor:
     """int32 ancestors per row.  logw and out may be row-strided views (unit
@@ -360,6 +386,7 @@ class ReplayPriorities:
     def cursor(self) -> int:
         return int(self._rb.cursor)
 
+    @_on_stream
     def insert(self, prio: torch.Tensor, *, out: torch.Tensor | None = None,
                stream=None) -> torch.Tensor:
         m = prio.numel()
@@ -370,6 +397,7 @@ class ReplayPriorities:
             _dev(out, "out", (torch.int32,)), _stream(stream)))
         return out
 
+    @_on_stream
     def update(self, slots: torch.Tensor, prio: torch.Tensor, stream=None):
         m = slots.numel()
         if prio.numel() != m:
@@ -378,6 +406,7 @@ class ReplayPriorities:
             C.byref(self._rb), _dev(slots, "slots", (torch.int32,)),
             _dev(prio, "prio", (torch.float32,)), m, _stream(stream)))
 
+    @_on_stream
     def sample(self, u: torch.Tensor, beta: float | None = 0.4, *, stratified: bool = True,
                out: torch.Tensor | None = None, out_w: torch.Tensor | None = None,
                stream=None):
@@ -402,6 +431,7 @@ class ReplayPriorities:
         return self.tree[1]
 
 
+@_on_stream
 def pf_step(x: torch.Tensor, logw: torch.Tensor, obs: torch.Tensor, A: torch.Tensor,
             C_obs: torch.Tensor, eps: torch.Tensor, sigma_p: float, sigma_o: float,
             u_row: torch.Tensor, *, x_out: torch.Tensor | None = None,
@@ -446,6 +476,7 @@ def scatter_workspace_size(n: int, m: int) -> int:
 SCATTER_GROUPED = 1
 
 
+@_on_stream
 def scatter_lww(prio: torch.Tensor, idx: torch.Tensor, vals: torch.Tensor,
                 ws: Workspace | None = None, *, grouped: bool = False,
                 stream=None) -> torch.Tensor:
@@ -471,6 +502,7 @@ def per_round_workspace_size(n: int, k: int) -> int:
     return int(lib().psamp_per_round_workspace_size(int(n), int(k)))
 
 
+@_on_stream
 def per_round(prio: torch.Tensor, u: torch.Tensor, alpha: float, beta: float,
               new_prio: torch.Tensor | None = None, *, out_idx: torch.Tensor | None = None,
               out_w: torch.Tensor | None = None, cdf: torch.Tensor | None = None,

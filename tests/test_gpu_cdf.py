@@ -28,6 +28,23 @@ def host(t):
     return t.cpu().numpy()
 
 
+def check_is_weights(w_g, p, alpha, T_o, idx_g, idx_o, beta, what, int_mode=False):
+    """IS weights against the oracle, always: on the GPU's index array (which
+    assert_indices has already matched to the oracle's own draws, up to
+    excused boundary ties), so that an excused index flip cannot move the
+    normaliser and skip the comparison; and, where the two index arrays are
+    the same, also against the oracle's own chain of draws."""
+    isw = oracle.is_weights_int if int_mode else oracle.is_weights
+    args = (p, T_o) if int_mode else (p, alpha, T_o)
+    w_v = isw(*args, np.asarray(idx_g, np.int32), beta)
+    e = rel_err(w_g, w_v)
+    say(f"  {what}: IS max rel err {e:.3e} (on the GPU's indices)")
+    assert e <= 1e-6, what
+    if np.array_equal(idx_g, idx_o):
+        assert rel_err(w_g, isw(*args, idx_o, beta)) <= 1e-6, what
+    assert w_g.max() == 1.0 and np.all(w_g > 0), what
+
+
 SIZES = [1, 2, 63, 64, 1023, 1024, 1025, 4095, 4096, 4097, 65536 + 3, 100003,
          (1 << 20), (1 << 20) + 1, (1 << 22) + 17]
 
@@ -207,12 +224,7 @@ def test_per_small_cfg(ps):
     assert rel_err(C_g, C_o) <= 1e-6
     assert_indices(idx_g, idx_o, t_o, C_o, T_o, "per_small")
     assert np.all(np.diff(idx_g) >= 0)
-    w_o = oracle.is_weights(d["p"], d["alpha"], T_o, idx_o, d["beta"])
-    if np.array_equal(idx_g, idx_o):
-        e = rel_err(w_g, w_o)
-        say(f"  IS max rel err {e:.3e}")
-        assert e <= 1e-6
-    assert w_g.max() == 1.0
+    check_is_weights(w_g, d["p"], d["alpha"], T_o, idx_g, idx_o, d["beta"], "per_small")
 
 
 @pytest.mark.parametrize("k,strat", [(1, True), (7, True), (1000, True), (1024, False),
@@ -228,10 +240,7 @@ def test_sample_and_weights_shapes(ps, k, strat):
     idx = host(ps.sample(cdf, tot, dev(U), stratified=strat))
     assert_indices(idx, idx_o, t_o, C_o, T_o, f"k={k}")
     w_g = host(ps.is_weights(Pd, dev(idx), 0.6, 0.4))
-    w_o = oracle.is_weights(p, 0.6, T_o, idx_o, 0.4)
-    if np.array_equal(idx, idx_o):
-        assert rel_err(w_g, w_o) <= 1e-6
-    assert w_g.max() == 1.0 and np.all(w_g > 0)
+    check_is_weights(w_g, p, 0.6, T_o, idx, idx_o, 0.4, f"k={k}")
 
 
 def test_sample_edges(ps):
@@ -285,8 +294,9 @@ def test_stratified_search_host_cdf(ps, n, k, dt, kind):
     U = si.uniform_f32(rng, k)
     U[0] = 0.0
     T = float(C[-1])
-    t = ((np.arange(k, dtype=np.float64) + U.astype(np.float64)) / k) * T
-    expect = _host_search(C.astype(np.float64), t)
+    t = oracle.thresholds(U, T, True)
+    expect = oracle.search_f32cdf(C, t) if dt == "f32" else oracle.search(C, t)
+    assert np.array_equal(expect, _host_search(C.astype(np.float64), t))
     cdf = dev(C)
     idx = host(ps.sample(cdf, cdf[-1:].clone(), dev(U), stratified=True))
     assert np.array_equal(idx, expect)
@@ -415,9 +425,7 @@ def test_per_large_cfg(ps):
     say(f"  max rel CDF err {e:.3e}; T gpu {T_g!r} oracle {T_o!r}")
     assert e <= 1e-6
     assert_indices(idx_g, idx_o, t_o, C_o, T_o, "per_large")
-    w_o = oracle.is_weights(d["p"], d["alpha"], T_o, idx_o, d["beta"])
-    if np.array_equal(idx_g, idx_o):
-        assert rel_err(w_g, w_o) <= 1e-6
+    check_is_weights(w_g, d["p"], d["alpha"], T_o, idx_g, idx_o, d["beta"], "per_large")
 
 
 def test_per_large_int_cfg(ps):
@@ -472,6 +480,28 @@ def test_max_n_int(ps):
 
 
 # ------------------------------------------------------------ fused update
+def check_round_vs_oracle(p, U, newp, alpha, beta, C_g, T_g, idx_g, w_g, p_g, what):
+    """One PER update (CDF, stratified draws, IS weights, rewrite) against
+    the oracle's own steps on the same inputs.  Returns the number of
+    excused index mismatches (boundary ties) and the oracle's rewritten
+    priorities (its own draws)."""
+    C_o, T_o, t_o, idx_o = oracle.sample(p, alpha, U, True)
+    e = rel_err(C_g, C_o)
+    assert e <= 1e-12, f"{what}: CDF rel err {e:.3e}"
+    assert abs(float(T_g) - T_o) <= 1e-12 * T_o, what
+    exc = assert_indices(idx_g, idx_o, t_o, C_o, T_o, what)
+    check_is_weights(w_g, p, alpha, T_o, idx_g, idx_o, beta, what)
+    p_next = p
+    if newp is not None:
+        # rewritten priorities: the oracle's last-write-wins scatter of the
+        # new values at the draws (at the GPU's draws when an excused tie
+        # moved one: the rest of the rewrite must still be exact)
+        p_next = oracle.scatter_lww(p, idx_o, newp)
+        p_chk = p_next if exc == 0 else oracle.scatter_lww(p, idx_g, newp)
+        assert np.array_equal(p_g, p_chk), f"{what}: rewritten priorities"
+    return exc, p_next
+
+
 def _separate_round(ps, p, U, newp, alpha, beta):
     """The four separate calls, for comparison with the fused update."""
     Pd = dev(p)
@@ -505,6 +535,9 @@ def test_per_round_equals_separate_calls(ps, n, k):
     assert np.array_equal(host(Pd), p_s)
     # the CDF is exactly monotone and ends at T
     assert np.all(np.diff(C_s) >= 0) and C_s[-1] == T_s[0]
+    # and the fused update meets the oracle directly
+    check_round_vs_oracle(p, U, newp, 0.6, 0.4, C_s, T_s[0], idx_s, w_s, p_s,
+                          f"per_round n={n} k={k}")
 
 
 def test_per_round_chain_vs_oracle(ps):
@@ -611,6 +644,18 @@ def test_build_cdf_sample_equals_separate(ps, n, k, mode):
         assert torch.equal(cdf, c_s), f"rep {rep}: cdf"
         assert torch.equal(tot, t_s), f"rep {rep}: total"
         assert torch.equal(idx, i_s), f"rep {rep}: indices"
+        # the fused call against the oracle directly
+        what = f"build_cdf_sample {mode} n={n} k={k} rep {rep}"
+        if mode == "fp":
+            C_o, T_o, t_o, idx_o = oracle.sample(p, alpha, u, True)
+            assert rel_err(host(cdf), C_o) <= 1e-12, what
+            assert abs(float(host(tot)[0]) - T_o) <= 1e-12 * T_o, what
+            assert_indices(host(idx), idx_o, t_o, C_o, T_o, what)
+        else:
+            C_o, T_o, t_o, idx_o = oracle.sample_int(p, u, True)
+            assert np.array_equal(host(cdf), C_o), what
+            assert int(host(tot)[0]) == T_o, what
+            assert np.array_equal(host(idx), idx_o), what
     assert ws.errors() == 0
 
 
@@ -624,6 +669,13 @@ def test_build_cdf_sample_per_large(ps):
     c_s, t_s = ps.build_cdf(P, d["alpha"])
     assert torch.equal(cdf, c_s) and torch.equal(tot, t_s)
     assert torch.equal(idx, ps.sample(c_s, t_s, Ud, stratified=True))
+    say("PER large fused fp: oracle ...")
+    C_o, T_o, t_o, idx_o = oracle.sample(d["p"], d["alpha"], d["U"], True)
+    e = rel_err(host(cdf), C_o)
+    say(f"  max rel CDF err {e:.3e}")
+    assert e <= 1e-12
+    assert abs(float(host(tot)[0]) - T_o) <= 1e-12 * T_o
+    assert_indices(host(idx), idx_o, t_o, C_o, T_o, "per_large fused fp")
     di = si.per_large_int()
     Q, R = dev(di["q"]), dev(di["r"])
     idx_i, _, _ = ps.build_cdf_sample(Q, R)
@@ -678,4 +730,26 @@ def test_per_round_large_chain(ps):
         assert np.array_equal(host(idx), idx_s), f"update {r}: indices"
         assert np.array_equal(host(w), w_s), f"update {r}: weights"
         assert np.array_equal(host(Pd), p_ref), f"update {r}: rewritten priorities"
+    assert ws.errors() == 0
+
+
+def test_per_round_large_chain_vs_oracle(ps):
+    """Beyond a resident grid (2^23 + 1 priorities: 1025 tiles, three
+    kernels per update), 2^18 stratified draws, four chained updates on one
+    workspace, against the oracle's own chain: CDF within 1e-12, indices
+    under the boundary rule (none observed; the chains would fork on one),
+    IS weights within 1e-6, rewritten priorities bit for bit."""
+    n, k = (1 << 23) + 1, 1 << 18
+    p_o = si.generic_f32(n, 23, "lognormal")
+    Pd = dev(p_o)
+    ws = ps.Workspace(ps.per_round_workspace_size(n, k))
+    for r in range(4):
+        U = si.uniform_f32(np.random.default_rng(300 + r), k)
+        newp = si.generic_f32(k, 400 + r, "exp")
+        idx, w, cdf, tot = ps.per_round(Pd, dev(U), 0.7, 0.5, dev(newp), ws=ws)
+        what = f"per_round large chain update {r}"
+        say(what)
+        exc, p_o = check_round_vs_oracle(p_o, U, newp, 0.7, 0.5, host(cdf), host(tot)[0],
+                                         host(idx), host(w), host(Pd), what)
+        assert exc == 0, "chains would fork; the oracle never takes GPU data"
     assert ws.errors() == 0

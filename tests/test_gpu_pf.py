@@ -88,13 +88,13 @@ def test_pf_step_pages_shape(ps):
     check(d, xo, lo, anc, "pf 16x1024")
 
 
-def test_pf_step_large_sampled(ps):
-    """1024 filters x 4096 particles, D = 4, O = 2 (the timed shape): 24
-    filters checked against the oracle, every filter for the properties."""
+def test_pf_step_large(ps):
+    """1024 filters x 4096 particles, D = 4, O = 2 (the timed shape): every
+    filter checked against the oracle, and the properties that hold for any
+    filter."""
     d = si.pf_step()
     xo, lo, anc = run_gpu(ps, d)
-    rows = np.r_[0:8, 500:508, 1016:1024]
-    check(d, xo, lo, anc, "pf 1024x4096 sampled", rows=rows)
+    check(d, xo, lo, anc, "pf 1024x4096")
     assert np.all(np.diff(anc, axis=1) >= 0)
     assert np.all(lo == np.float32(-np.log(4096)))
     # each output row is made of the filter's own predictions: the gathered

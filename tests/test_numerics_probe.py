@@ -31,3 +31,44 @@ def test_float32_sums_break_the_index_budget(shape):
     idx32 = _fp32_pipeline(p, alpha, U)
     frac = float(np.mean(idx32 != idx64))
     assert frac > lo, f"{shape}: float32 pipeline differs on {frac:.2e} of draws"
+
+
+def _fp32_weights_fp64_scan(p, alpha, U):
+    """Weights rounded to float32 (correctly: the oracle's double pow, then
+    one rounding), then the oracle's own fp64 scan, thresholds and search."""
+    w32 = oracle.weights(p, alpha).astype(np.float32).astype(np.float64)
+    C, T = oracle.cdf_f64(w32)
+    return oracle.search(C, oracle.thresholds(U, T, True))
+
+
+def _fp64_weights_blocked_scan(p, alpha, U, tile=8192):
+    """fp64 weights summed in another association: per-tile sequential sums,
+    then the tile offsets (as any parallel scan must)."""
+    w = oracle.weights(p, alpha)
+    n = w.size
+    pad = (-n) % tile
+    local = np.cumsum(np.r_[w, np.zeros(pad)].reshape(-1, tile), axis=1)
+    offs = np.r_[0.0, np.cumsum(local[:, -1])[:-1]]
+    C = (local + offs[:, None]).reshape(-1)[:n]
+    return oracle.search(C, oracle.thresholds(U, float(C[-1]), True))
+
+
+def test_float32_weights_use_up_the_index_budget_at_per_large():
+    """fp32-rounded weights, even with an exact-enough fp64 scan, flip about
+    1e-4 of the 2^20 draws over 2^24 LogNormal(0,2) priorities (the rounding
+    error of each weight, ~2^-25 relative, random-walks through the CDF): on
+    the workload's own seed 7.3e-5, and over the 1e-4 budget on other seeds
+    of the same distribution (1.55e-4 on seed 2001).  fp64 weights with a
+    tile-blocked fp64 scan (another association, as any parallel scan's)
+    flip 4 draws (3.8e-6, ties moved by the few-ulp change of T), twenty
+    times fewer.  This is why p^alpha is evaluated in double."""
+    d = si.per_large()
+    _, _, _, idx64 = oracle.sample(d["p"], d["alpha"], d["U"], True)
+    f32 = float(np.mean(_fp32_weights_fp64_scan(d["p"], d["alpha"], d["U"]) != idx64))
+    assert f32 > 5e-5, f"fp32 weights flip {f32:.2e}: no longer half the budget"
+    f64 = float(np.mean(_fp64_weights_blocked_scan(d["p"], d["alpha"], d["U"]) != idx64))
+    assert f64 < 1e-5 and f32 > 10 * f64, (f32, f64)
+    d = si.per_large(seed=2001)
+    _, _, _, idx64 = oracle.sample(d["p"], d["alpha"], d["U"], True)
+    f32 = float(np.mean(_fp32_weights_fp64_scan(d["p"], d["alpha"], d["U"]) != idx64))
+    assert f32 > 1e-4, f"seed 2001: fp32 weights flip {f32:.2e}, within the budget"

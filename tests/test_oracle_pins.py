@@ -142,6 +142,29 @@ def test_search_ties_and_clamp(orc):
     assert list(orc.search(Cc, t)) == [0, 0, 2, 2, 3, 3, 0]
 
 
+def test_search_f32cdf_matches_numpy_and_brute_force(orc):
+    """The search over a float32 CDF with double thresholds: equal to numpy's
+    left searchsorted on the CDF widened to double (exact, every float is a
+    double), clamped; and, on a tiny CDF with ties and rounding collisions,
+    to a brute-force scan for the first entry >= t."""
+    rng = np.random.default_rng(44)
+    w = rng.exponential(1.0, 40000)
+    w[rng.random(w.size) < 0.3] = 0.0
+    Cf = np.cumsum(w).astype(np.float32)
+    U = si.uniform_f32(rng, 5000)
+    for strat in (True, False):
+        t = orc.thresholds(U, float(Cf[-1]), strat)
+        ref = np.searchsorted(Cf.astype(np.float64), t, side="left").clip(0, Cf.size - 1)
+        assert np.array_equal(orc.search_f32cdf(Cf, t), ref)
+    Cs = np.array([0.5, 0.5, 1.0, np.float32(1.0) + np.float32(2**-23), 3.0], np.float32)
+    t = np.array([-1.0, 0.0, 0.5, 0.5 + 1e-12, 1.0, 1.0 + 1e-9, 1.0 + 2**-23, 2.9, 3.0, 3.5])
+    brute = []
+    for x in t:
+        hits = [j for j in range(Cs.size) if float(Cs[j]) >= x]
+        brute.append(hits[0] if hits else Cs.size - 1)
+    assert list(orc.search_f32cdf(Cs, t)) == brute == [0, 0, 0, 2, 2, 3, 3, 4, 4, 4]
+
+
 def test_search_int_brute_force_counts(orc):
     rng = np.random.default_rng(41)
     for n in (1, 2, 3, 5, 8):
