@@ -329,8 +329,10 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
                   (new_prio && !aligned(new_prio, 4))))
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
-    const size_t scan_ws = psamp_build_cdf_workspace_size(n);
-    const uint64_t max_slots = ws_tile_capacity(scan_ws);
+    // The clearing of the other parity runs up to the largest tile count any
+    // call on this workspace has used, which can exceed this call's: the
+    // bound is the workspace's own capacity, not the one this n needs.
+    const uint64_t max_slots = ws_tile_capacity(ws_bytes);
     const int vec_ok = aligned(cdf, 16);   // 16-byte stores of whole tiles
     if (k > 0) {
         // The scan's own tiling (so the CDF is the same bits as psamp_build_cdf's);
@@ -358,6 +360,7 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
     // weights), the same results as the four separate calls.
     if (k > 0)
         return launch_per_update((float*)prio, n, alpha, beta, u, k, new_prio, out_idx, out_w,
-                                 cdf, total, ws, scan_ws, st);
-    return psamp_build_cdf(prio, PSAMP_F32, n, alpha, cdf, PSAMP_F64, total, ws, scan_ws, stream);
+                                 cdf, total, ws, ws_bytes, st);
+    return psamp_build_cdf(prio, PSAMP_F32, n, alpha, cdf, PSAMP_F64, total, ws, ws_bytes, stream);
 }
+

@@ -753,3 +753,29 @@ def test_per_round_large_chain_vs_oracle(ps):
                                          host(idx), host(w), host(Pd), what)
         assert exc == 0, "chains would fork; the oracle never takes GPU data"
     assert ws.errors() == 0
+
+
+def test_per_round_one_workspace_shrinking_then_growing(ps):
+    """One workspace for fused updates whose tile counts shrink and then grow
+    again (1025 tiles on the three-kernel path, 256 and 8 on the one-kernel
+    path, then 2048): every update's status words must be clean, i.e. each
+    call clears the other parity up to the largest tile count the workspace
+    has seen, not only up to its own.  A regression test: the clearing was
+    bounded by the capacity the current n needs, which left stale tile sums
+    of an earlier, larger update for a later one to read."""
+    sizes = [((1 << 23) + 1, 1 << 16), (262144, 8192), (8192, 1024), (1 << 24, 1 << 18),
+             (300000, 5000), ((1 << 23) + 1, 1 << 16)]
+    ws = ps.Workspace(ps.per_round_workspace_size(1 << 24, 1 << 18))
+    for call, (n, k) in enumerate(sizes):
+        say(f"shared workspace call {call}: n={n} k={k}")
+        p = si.generic_f32(n, 600 + call, "lognormal")
+        U = dev(si.uniform_f32(np.random.default_rng(700 + call), k))
+        newp = dev(si.generic_f32(k, 800 + call, "exp"))
+        P_ref, P_sh = dev(p), dev(p)
+        ref = ps.per_round(P_ref, U, 0.7, 0.5, newp,
+                           ws=ps.Workspace(ps.per_round_workspace_size(n, k)))
+        got = ps.per_round(P_sh, U, 0.7, 0.5, newp, ws=ws)
+        for name, r, g in zip(("indices", "weights", "cdf", "total"), ref, got):
+            assert torch.equal(r, g), f"call {call}: {name}"
+        assert torch.equal(P_ref, P_sh), f"call {call}: rewritten priorities"
+    assert ws.errors() == 0
