@@ -366,6 +366,31 @@ psamp_status psamp_per_round(void* prio, int64_t n, double alpha, double beta,
                              void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * psamp_per_round without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments (less ws, ws_bytes), same
+ * kernels and the same results bit for bit as psamp_per_round; the
+ * workspace is a library-owned device array of 256 B + 4 KiB per 65536
+ * priorities up to PSAMP_NOALLOC_MAX_N (4 MiB + 256 B), one per GPU, kept
+ * until the process ends.  No call allocates or frees anything.
+ *   n : 1 <= n <= PSAMP_NOALLOC_MAX_N (E_SIZE above).
+ * The array is shared by every call on one GPU and keeps the last call's
+ * state (it stays consistent, as a caller's workspace does): two calls that
+ * may overlap on one GPU -- on different streams, or from different host
+ * threads -- race and give unspecified results.  A bounded wait that gives
+ * up sets a bit in that array, which no call reports.  The first call on
+ * each device finds the array's address and, unless its stream is being
+ * captured, clears it with a kernel on that stream.
+ * Errors: those of psamp_per_round (E_WORKSPACE never), E_LAUNCH if the
+ * array's address cannot be found.
+ * ---------------------------------------------------------------------- */
+#define PSAMP_NOALLOC_MAX_N (1 << 26)
+psamp_status psamp_per_round_noalloc(void* prio, int64_t n, double alpha, double beta,
+                                     const float* u, int64_t k, const float* new_prio,
+                                     int32_t* out_idx, float* out_w, double* cdf, double* total,
+                                     void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.  Copies the error bits a workspace of psamp_build_cdf,
  * psamp_build_cdf_sample, psamp_per_round or psamp_is_weights has
  * accumulated (bit 0: a bounded cross-workgroup wait timed out, so some

@@ -63,6 +63,7 @@ SIGNATURES = {
     "psamp_scatter_lww": (_int, [_p, _int, _i64, _p, _p, _i64, _int, _p, _sz, _p]),
     "psamp_per_round_workspace_size": (_sz, [_i64, _i64]),
     "psamp_per_round": (_int, [_p, _i64, _dbl, _dbl, _p, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
+    "psamp_per_round_noalloc": (_int, [_p, _i64, _dbl, _dbl, _p, _i64, _p, _p, _p, _p, _p, _p]),
     "psamp_workspace_errors": (_int, [_p, _sz, C.POINTER(C.c_uint64), _p]),
 }
 
@@ -529,3 +530,31 @@ def per_round(prio: torch.Tensor, u: torch.Tensor, alpha: float, beta: float,
         _dev(out_w, "out_w", (torch.float32,)), _dev(cdf, "cdf", (torch.float64,)),
         _dev(total, "total", (torch.float64,)), ws.ptr, ws.nbytes, _stream(stream)))
     return out_idx, out_w, cdf, total
+
+
+NOALLOC_MAX_N = 1 << 26      # PSAMP_NOALLOC_MAX_N
+
+
+@_on_stream
+def per_round_noalloc(prio: torch.Tensor, u: torch.Tensor, alpha: float, beta: float,
+                      new_prio: torch.Tensor | None = None, *, out_idx: torch.Tensor,
+                      out_w: torch.Tensor, cdf: torch.Tensor, total: torch.Tensor,
+                      stream=None):
+    """per_round with the library's own scratch instead of a workspace: the
+    caller passes every output, so nothing is allocated.  Calls that overlap
+    on one GPU race.  Returns (out_idx, out_w, cdf, total)."""
+    n, k = prio.numel(), u.numel()
+    npp = None
+    if new_prio is not None:
+        if new_prio.numel() != k:
+            raise ValueError("new_prio must have one value per draw")
+        npp = _dev(new_prio, "new_prio", (torch.float32,))
+    if out_idx.numel() != k or out_w.numel() != k or cdf.numel() != n or total.numel() != 1:
+        raise ValueError("outputs: k indices, k weights, n CDF values, 1 total")
+    _check("psamp_per_round_noalloc", lib().psamp_per_round_noalloc(
+        _dev(prio, "prio", (torch.float32,)), n, float(alpha), float(beta),
+        _dev(u, "u", (torch.float32,)), k, npp, _dev(out_idx, "out_idx", (torch.int32,)),
+        _dev(out_w, "out_w", (torch.float32,)), _dev(cdf, "cdf", (torch.float64,)),
+        _dev(total, "total", (torch.float64,)), _stream(stream)))
+    return out_idx, out_w, cdf, total
+

@@ -25,6 +25,8 @@
 // The grid is one workgroup per tile and must be resident at once (two
 // grid-wide waits); the host checks the occupancy and otherwise runs the
 // separate kernels, which give the same bits.
+#include <mutex>
+
 #include "psamp_host.h"
 #include "scan_tile.h"
 
@@ -364,3 +366,81 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
     return psamp_build_cdf(prio, PSAMP_F32, n, alpha, cdf, PSAMP_F64, total, ws, ws_bytes, stream);
 }
 
+// ---------------------------------------------------------------------------
+// psamp_per_round_noalloc: psamp_per_round for callers that cannot allocate
+// device memory.  Its workspace is `scratch`, a file-scope device array, one
+// copy on every GPU the library runs on, held until the process ends.  Host
+// code never passes the array's name to a kernel or a copy (on the host it
+// is only a stand-in for the symbol): it takes the array's device address on
+// each device from hipGetSymbolAddress, once, and uses that.
+// ---------------------------------------------------------------------------
+namespace psamp {
+
+constexpr int64_t kNoAllocMaxN = PSAMP_NOALLOC_MAX_N;
+constexpr size_t kNoAllocBytes = ws_bytes_for_tiles((kNoAllocMaxN + kMinTile - 1) / kMinTile);
+static_assert(kNoAllocBytes % 8 == 0, "scratch is an array of 64-bit words");
+
+static __device__ __align__(256) uint64_t scratch[kNoAllocBytes / 8];
+
+__global__ void k_zero_words(uint64_t* __restrict__ p, int64_t words) {
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+         i += (int64_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
+constexpr int kNoAllocMaxDevices = 64;
+
+// The device address of this device's scratch, found once per device.  On
+// that first call the array is also cleared by a kernel on the caller's
+// stream (it starts zeroed as a zero-initialised static; the kernel only
+// makes that explicit) -- unless the stream is being captured, where the
+// static zero state is the one the first call finds.
+static psamp_status noalloc_scratch(hipStream_t st, uint64_t** out) {
+    static std::mutex mu;
+    static uint64_t* ptr[kNoAllocMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kNoAllocMaxDevices) {
+        (void)hipGetLastError();
+        return PSAMP_E_LAUNCH;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return PSAMP_E_LAUNCH;
+        }
+        hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(st, &cap) != hipSuccess) {
+            (void)hipGetLastError();
+            return PSAMP_E_LAUNCH;
+        }
+        if (cap == hipStreamCaptureStatusNone) {
+            hipLaunchKernelGGL(k_zero_words, dim3(256), dim3(256), 0, st, (uint64_t*)p,
+                               (int64_t)(kNoAllocBytes / 8));
+            if (launch_status() != PSAMP_OK) return PSAMP_E_LAUNCH;
+        }
+        ptr[dev] = (uint64_t*)p;
+    }
+    *out = ptr[dev];
+    return PSAMP_OK;
+}
+
+}  // namespace psamp
+
+extern "C" psamp_status psamp_per_round_noalloc(void* prio, int64_t n, double alpha, double beta,
+                                                const float* u, int64_t k,
+                                                const float* new_prio, int32_t* out_idx,
+                                                float* out_w, double* cdf, double* total,
+                                                void* stream) {
+    if (n > kNoAllocMaxN) return PSAMP_E_SIZE;
+    // the checks of psamp_per_round that need no workspace, before set-up
+    if (!prio || !cdf || !total) return PSAMP_E_NULL;
+    if (n < 1 || k < 0 || k > kMaxN) return PSAMP_E_SIZE;
+    if (!(finite_d(alpha) && alpha > 0.0) || !(finite_d(beta) && beta >= 0.0)) return PSAMP_E_PARAM;
+    uint64_t* ws = nullptr;
+    const psamp_status e = noalloc_scratch(as_stream(stream), &ws);
+    if (e != PSAMP_OK) return e;
+    return psamp_per_round(prio, n, alpha, beta, u, k, new_prio, out_idx, out_w, cdf, total, ws,
+                           kNoAllocBytes, stream);
+}
