@@ -48,13 +48,14 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=8.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying a HIP graph")
     ap.add_argument("--only", default="",
-                    help="profiling helper: scan:<n> | copy:<MiB> | pf | per_large")
+                    help="profiling helper: per_mid | scan:<n> | ceiling:<n> | copy:<MiB> | "
+                         "pf | per_large")
     return ap.parse_args()
 
 
@@ -119,14 +120,23 @@ class PerMid:
         return out
 
     def algo_bytes(self, name):
+        """Algorithmic bytes per launch, by the per-unit table of the scope
+        contract: scan 12 B per element (f32 in, f64 out); stratified sample
+        + IS 12 B per draw (U in, index and weight out) plus the touched CDF
+        lines min(8 n, 64 k) and the gathered priority lines min(4 n, 64 k).
+        The fused update is the scan plus the sample + IS row (its rewrite of
+        the drawn priorities, 8 B per draw, is in no row of that table and is
+        left out); `per_round_own` is the fused kernel's own count, which
+        reads no CDF line back and gathers no priority line twice."""
         n, k = self.n, self.k
         return {
             "build_cdf": 12 * n,                                   # f32 in, f64 out
             "sample": 8 * k + min(8 * n, 64 * k),                  # U in, idx out, CDF lines
             "is_weights": 8 * k + min(4 * n, 64 * k),              # idx in, w out, p lines
             "scatter_lww": 8 * k + 4 * k,                          # idx, vals in; prio out
-            # fused: p in, CDF out, U in, idx + w out, new p in, p rewrites
-            "per_round": 12 * n + 4 * k + 8 * k + 4 * k + 4 * k,
+            "per_round": 12 * n + 12 * k + min(8 * n, 64 * k) + min(4 * n, 64 * k),
+            # fused, its own bytes: p in, CDF out, U in, idx + w out, new p in, p rewrites
+            "per_round_own": 12 * n + 4 * k + 8 * k + 4 * k + 4 * k,
         }[name]
 
 
@@ -249,11 +259,34 @@ def flush_cache(torch, flush):
     flush()
 
 
-def scan_sweep(ps, torch, sizes, reps=8):
-    """Median launch time of psamp_build_cdf per size, cache flushed."""
+def scan_sweep(ps, torch, sizes, reps=8, copy=True):
+    """Median launch time of psamp_build_cdf per size, cache flushed, next to
+    the copy ceiling: psamp_ceiling_copy (the scan's bytes in its access
+    pattern, no arithmetic, no exchange) in the scan's tile geometry (8 rows)
+    and in the smaller one (4 rows), timed the same way."""
     out = []
     flush = CacheFlush(torch)
     for n in sizes:
+        ceil = {}
+        if copy:
+            src = torch.rand(n, device="cuda")
+            dst = torch.empty(n, dtype=torch.float64, device="cuda")
+            for rows, nt in ((8, True), (2, False)):
+                ps.ceiling_copy(src, dst, rows, nt)
+                ts = []
+                for _ in range(reps):
+                    flush_cache(torch, flush)
+                    e0 = torch.cuda.Event(enable_timing=True)
+                    e1 = torch.cuda.Event(enable_timing=True)
+                    e0.record()
+                    ps.ceiling_copy(src, dst, rows, nt)
+                    e1.record()
+                    torch.cuda.synchronize()
+                    ts.append(e0.elapsed_time(e1) * 1e3)
+                ceil[rows] = statistics.median(ts)
+            log(f"copy ceiling n=2^{n.bit_length() - 1}: {ceil[8]:.1f} us (scan's tile: 8 rows, "
+                f"non-temporal), {ceil[2]:.1f} us (best copy: 2 rows, plain stores)")
+            del src, dst
         g = torch.Generator(device="cuda").manual_seed(n)
         p = torch.exp(2.0 * torch.randn(n, device="cuda", generator=g)).float()
         q = torch.randint(1, (1 << 20) + 1, (n,), device="cuda", generator=g,
@@ -276,8 +309,15 @@ def scan_sweep(ps, torch, sizes, reps=8):
                 ts.append(e0.elapsed_time(e1) * 1e3)
             us = statistics.median(ts)
             gbs = 12.0 * n / (us * 1e-6) / 1e9
-            out.append({"n": n, "mode": mode, "us": round(us, 2), "GB/s": round(gbs, 1),
-                        "frac_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            row = {"n": n, "mode": mode, "us": round(us, 2), "GB/s": round(gbs, 1),
+                   "frac_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            if ceil:
+                row["copy_ceiling_us"] = {"scan_tile_nt": round(ceil[8], 2),
+                                          "best_rows2_plain": round(ceil[2], 2)}
+                row["copy_ceiling_frac_peak"] = round(12.0 * n / (min(ceil.values()) * 1e-6)
+                                                      / 1e9 / HBM_PEAK_GBS, 4)
+                row["scan_frac_of_best_copy"] = round(min(ceil.values()) / us, 3)
+            out.append(row)
             log(f"scan {mode} n=2^{n.bit_length() - 1}: {us:.1f} us {gbs:.0f} GB/s")
             del cdf, ws
         del p, q
@@ -461,7 +501,82 @@ def per_large_bench(ps, torch, reps=10):
 
 
 # ----------------------------------------------------------------- CPU side
-def cpu_baseline(seconds):
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _median_s(fn, runs):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return statistics.median(ts)
+
+
+def cpu_functions(gpu_us):
+    """The oracle's steps one by one at their workloads (median of 3 runs; one
+    run for the 2^24-leaf pointer tree), each next to the GPU's time of the
+    same step (from this run's measurements, when taken) and the ratio."""
+    import oracle
+    import synthetic_inputs as si
+    rows = {}
+
+    def put(name, secs, what, gpu_key):
+        us = secs * 1e6
+        g = gpu_us.get(gpu_key)
+        rows[name] = {"oracle_us": round(us, 1), "gpu_us": g, "workload": what,
+                      "oracle_over_gpu": round(us / g, 1) if g else None}
+
+    d = si.per_mid()
+    p, U, a, b = d["p0"], d["U"][0], d["alpha"], d["beta"]
+    C, T = oracle.build_cdf(p, a)
+    t = oracle.thresholds(U, T, True)
+    idx = oracle.search(C, t)
+    put("scan", _median_s(lambda: oracle.build_cdf(p, a), 3), "PER mid: 262144 priorities",
+        "build_cdf_per_mid")
+    put("search", _median_s(lambda: oracle.search(C, oracle.thresholds(U, T, True)), 3),
+        "PER mid: 8192 stratified draws", "sample_per_mid")
+    put("is_weights", _median_s(lambda: oracle.is_weights(p, a, T, idx, b), 3),
+        "PER mid: 8192 draws", "is_weights_per_mid")
+    d = si.per_large()
+    p, U, a, b = d["p"], d["U"], d["alpha"], d["beta"]
+    C, T = oracle.build_cdf(p, a)
+    t = oracle.thresholds(U, T, True)
+    idx = oracle.search(C, t)
+    put("scan_large", _median_s(lambda: oracle.build_cdf(p, a), 3), "PER large: 2^24 priorities",
+        "build_cdf_per_large")
+    put("search_large", _median_s(lambda: oracle.search(C, oracle.thresholds(U, T, True)), 3),
+        "PER large: 2^20 stratified draws", "sample_per_large")
+    put("is_weights_large", _median_s(lambda: oracle.is_weights(p, a, T, idx, b), 3),
+        "PER large: 2^20 draws", "is_weights_per_large")
+    del C, t, idx
+    big = oracle.Tree("f32", 1 << 24)
+    put("tree_build_large", _median_s(lambda: big.build(p, p.size, a), 1),
+        "PER large: 2^24-leaf tree build", "tree_build_per_large")
+    put("tree_sample_large", _median_s(lambda: big.sample(U, p.size, stratified=True), 1),
+        "PER large: 2^20 stratified descents", "tree_sample_per_large")
+    del big
+    d = si.sumtree(rounds=3)
+    tr = oracle.Tree("f32", 1 << 19).build(d["p0"], 500000, d["alpha"])
+    it = iter(range(3))
+    put("tree_update", _median_s(lambda: tr.update(d["idx"][next(it)], d["v"][0], d["alpha"]), 3),
+        "sum tree: 1024 updates on 2^19 leaves", "tree_update_sumtree")
+    put("tree_sample", _median_s(lambda: tr.sample(d["U"][0], 500000), 3),
+        "sum tree: 1024 iid descents", "tree_sample_sumtree")
+    d = si.resample()
+    put("resample_rows", _median_s(lambda: oracle.resample_rows(d["lw"], d["u_row"]), 3),
+        "particle resampling: 1024 rows x 4096", "resample_rows")
+    return rows
+
+
+def cpu_baseline(seconds, gpu_us):
     import oracle
     import synthetic_inputs as si
     d = si.per_mid()
@@ -480,9 +595,14 @@ def cpu_baseline(seconds):
     k, rounds = d["U"].shape[1], d["U"].shape[0]
     val = steps * rounds * k / el
     log(f"cpu oracle: {steps} steps in {el:.1f} s -> {val:.0f} indices/s")
+    t1 = time.perf_counter()
+    funcs = cpu_functions(gpu_us)
+    log(f"cpu oracle functions ({time.perf_counter() - t1:.1f} s): {json.dumps(funcs)}")
     return {"value": round(val, 1), "unit": "sampled indices/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} full steps (32 updates of B=262144 / 8192 draws each) of the "
-                      f"same seeded workload, {el:.1f} s, single thread"}
+                      f"same seeded workload, {el:.1f} s, single thread",
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count(),
+            "functions": funcs}
 
 
 # ----------------------------------------------------------------- main
@@ -509,6 +629,18 @@ def main():
     if args.only == "per_large":
         log(json.dumps(per_large_bench(ps, torch)))
         return
+    if args.only.startswith("ceiling:"):
+        n = int(args.only.split(":")[1])
+        src = torch.rand(n, device="cuda")
+        dst = torch.empty(n, dtype=torch.float64, device="cuda")
+        flush = CacheFlush(torch)
+        for rows, nt in ((8, True), (2, False)):
+            for _ in range(10):
+                flush()
+                ps.ceiling_copy(src, dst, rows, nt)
+        torch.cuda.synchronize()
+        log(f"ceiling copy n={n}: 10 calls per geometry, each after a cache flush")
+        return
     if args.only.startswith("copy:"):
         mib = int(args.only.split(":")[1])
         a = torch.ones(mib * 1024 * 1024 // 4, dtype=torch.float32, device="cuda")
@@ -520,6 +652,15 @@ def main():
         return
 
     work = PerMid(ps, torch)
+    if args.only == "per_mid":
+        # profiling helper: only the timed region of the headline (the step
+        # replayed from its HIP graph), nothing else
+        for _ in range(args.warmup):
+            work.step_fused()
+        g = capture(torch, work.step_fused)
+        gpu_s, _ = timed_steps(torch, g.replay, args.steps)
+        log(f"PER mid graph: {1e3 * gpu_s / args.steps:.4f} ms/step over {args.steps} steps")
+        return
     log(f"PER mid: warmup {args.warmup} steps")
     for _ in range(args.warmup):
         work.step_fused()
@@ -550,11 +691,14 @@ def main():
     avg_us = 1e6 * gpu_s / launches
     dom = "per_round"
     ab = work.algo_bytes(dom)
+    ab_own = work.algo_bytes("per_round_own")
     achieved = ab / (avg_us * 1e-6) / 1e9
     traffic = profiled_traffic("per_round_per_mid.md")
     roofline = {"bound": "hbm", "kernel": KERNEL_NAMES[dom], "achieved": round(achieved, 2),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                 "traffic": traffic, "algo_bytes_per_launch": ab,
+                "own_bytes_per_launch": ab_own,
+                "own_frac": round(ab_own / (avg_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 5),
                 "avg_launch_us": round(avg_us, 3), "launches_timed": launches}
     log(f"k_per_round: {avg_us:.2f} us/launch, {achieved:.0f} GB/s algorithmic, traffic {traffic}")
 
@@ -575,9 +719,21 @@ def main():
 
     cpu = None
     if not args.no_cpu:
-        cpu = cpu_baseline(args.cpu_seconds)
+        pc = extra["separate_calls"]["per_call_us"]
+        gpu_us = {"build_cdf_per_mid": pc["build_cdf"], "sample_per_mid": pc["sample"],
+                  "is_weights_per_mid": pc["is_weights"]}
+        if "per_large" in extra:
+            pl = extra["per_large"]
+            gpu_us.update({"build_cdf_per_large": pl["build_cdf"],
+                           "sample_per_large": pl["sample"],
+                           "is_weights_per_large": pl["is_weights"],
+                           "tree_build_per_large": pl["tree_build"],
+                           "tree_sample_per_large": pl["tree_sample"],
+                           "tree_update_sumtree": extra["sumtree"]["update_us"],
+                           "tree_sample_sumtree": extra["sumtree"]["sample_us"],
+                           "resample_rows": extra["resample_rows"]["us"]})
+        cpu = cpu_baseline(args.cpu_seconds, gpu_us)
         extra["gpu_over_cpu"] = round(value / cpu["value"], 1)
-        extra["host_cpus"] = os.cpu_count()
 
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "sampled indices/s",

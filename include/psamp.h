@@ -391,6 +391,56 @@ psamp_status psamp_per_round_noalloc(void* prio, int64_t n, double alpha, double
                                      void* stream);
 
 /* ------------------------------------------------------------------------
+ * Measurement aid: the bandwidth ceiling of the CDF scan on this device.
+ * out[i] = (double)in[i] for i < n -- the scan's bytes (4 read, 8 written
+ * per element) in its access pattern, without its arithmetic or its
+ * exchange between workgroups.  rows: 8 (the scan's tile of 8192 elements
+ * per workgroup), 4 or 2 (smaller workgroups, more of them per CU); nt: 1
+ * for non-temporal stores (as the scan's large tiles use), 0 for plain
+ * ones.  n a multiple of 4, 4 <= n <= 2^31 - 1; in and out 16-byte aligned.
+ * Errors: E_NULL, E_SIZE, E_PARAM, E_ALIGN, E_LAUNCH.
+ * ---------------------------------------------------------------------- */
+psamp_status psamp_ceiling_copy(const float* in, double* out, int64_t n, int rows, int nt,
+                                 void* stream);
+
+/* ------------------------------------------------------------------------
+ * Device-side precondition checks.  The preconditions above that need a
+ * sync to check (priorities finite and >= 0 with a positive total,
+ * threshold fractions in [0, 1), indices in range, log-weights not NaN or
+ * +inf) are checked on the device when checking is on: every entry point
+ * then enqueues small check kernels on its stream next to its own, and a
+ * violation sets a bit in a per-device word.  The checks change no output
+ * and no status code.  Checking starts on when PSAMP_CHECK=1 is in the
+ * environment at the library's first use.
+ *   psamp_check_enable(1 / 0) turns it on / off and returns the previous
+ *   state; psamp_check_enable(-1) only returns the state.
+ *   psamp_check_errors copies the word to *bits_host, syncing `stream`
+ *   (enqueue it on the stream of the calls it should cover); clear = 1 also
+ *   zeroes the word.  Errors: E_NULL, E_LAUNCH.
+ * Bits (which entry points check what):
+ *   PSAMP_CHECK_PRIORITY   a priority (or new priority) NaN, infinite or < 0
+ *                          (float priorities of build_cdf, build_cdf_sample,
+ *                          per_round, segtree_build/update, scatter_lww,
+ *                          replay insert/update)
+ *   PSAMP_CHECK_ZERO_TOTAL the total of the weights is not > 0 (build_cdf,
+ *                          build_cdf_sample, per_round, sample, after
+ *                          segtree_build)
+ *   PSAMP_CHECK_FRACTION   a float threshold fraction U_i or u_row outside
+ *                          [0, 1) (sample, build_cdf_sample, per_round,
+ *                          segtree_sample, replay sample, resample_rows,
+ *                          pf_step)
+ *   PSAMP_CHECK_INDEX      an index outside [0, n) (is_weights)
+ *   PSAMP_CHECK_LOGWEIGHT  a log-weight NaN or +inf (resample_rows, pf_step)
+ * ---------------------------------------------------------------------- */
+#define PSAMP_CHECK_PRIORITY 2u
+#define PSAMP_CHECK_ZERO_TOTAL 4u
+#define PSAMP_CHECK_FRACTION 8u
+#define PSAMP_CHECK_INDEX 16u
+#define PSAMP_CHECK_LOGWEIGHT 32u
+int psamp_check_enable(int on);
+psamp_status psamp_check_errors(uint64_t* bits_host, int clear, void* stream);
+
+/* ------------------------------------------------------------------------
  * Diagnostics.  Copies the error bits a workspace of psamp_build_cdf,
  * psamp_build_cdf_sample, psamp_per_round or psamp_is_weights has
  * accumulated (bit 0: a bounded cross-workgroup wait timed out, so some

@@ -64,6 +64,9 @@ SIGNATURES = {
     "psamp_per_round_workspace_size": (_sz, [_i64, _i64]),
     "psamp_per_round": (_int, [_p, _i64, _dbl, _dbl, _p, _i64, _p, _p, _p, _p, _p, _p, _sz, _p]),
     "psamp_per_round_noalloc": (_int, [_p, _i64, _dbl, _dbl, _p, _i64, _p, _p, _p, _p, _p, _p]),
+    "psamp_ceiling_copy": (_int, [_p, _p, _i64, _int, _int, _p]),
+    "psamp_check_enable": (_int, [_int]),
+    "psamp_check_errors": (_int, [C.POINTER(C.c_uint64), _int, _p]),
     "psamp_workspace_errors": (_int, [_p, _sz, C.POINTER(C.c_uint64), _p]),
 }
 
@@ -557,4 +560,36 @@ def per_round_noalloc(prio: torch.Tensor, u: torch.Tensor, alpha: float, beta: f
         _dev(out_w, "out_w", (torch.float32,)), _dev(cdf, "cdf", (torch.float64,)),
         _dev(total, "total", (torch.float64,)), _stream(stream)))
     return out_idx, out_w, cdf, total
+
+
+@_on_stream
+def ceiling_copy(src: torch.Tensor, out: torch.Tensor, rows: int = 2, nt: bool = False,
+                 stream=None):
+    """out = src as float64 with the scan's bytes and access pattern (a
+    measurement aid: the bandwidth ceiling of build_cdf)."""
+    if src.numel() != out.numel():
+        raise ValueError("src and out must have the same length")
+    _check("psamp_ceiling_copy", lib().psamp_ceiling_copy(
+        _dev(src, "src", (torch.float32,)), _dev(out, "out", (torch.float64,)), src.numel(),
+        int(rows), int(bool(nt)), _stream(stream)))
+    return out
+
+
+# Device-side precondition checks (PSAMP_CHECK=1 or check_enable(True)).
+CHECK_PRIORITY, CHECK_ZERO_TOTAL, CHECK_FRACTION, CHECK_INDEX, CHECK_LOGWEIGHT = 2, 4, 8, 16, 32
+
+
+def check_enable(on: bool | None = True) -> bool:
+    """Turns the device-side checks on or off (None: leave as is); returns
+    the previous state."""
+    return bool(lib().psamp_check_enable(-1 if on is None else int(bool(on))))
+
+
+@_on_stream
+def check_errors(clear: bool = True, stream=None) -> int:
+    """The check bits set on this device so far (syncs the stream)."""
+    out = C.c_uint64(0)
+    _check("psamp_check_errors", lib().psamp_check_errors(C.byref(out), int(bool(clear)),
+                                                            _stream(stream)))
+    return int(out.value)
 

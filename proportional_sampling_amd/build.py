@@ -16,7 +16,7 @@ OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libpsamp.so")
 SOURCES = ["api.hip", "scan.hip", "sample.hip", "isw.hip", "tree.hip", "resample.hip",
            "scatter.hip", "per_round.hip", "pf.hip",
-           "replay.hip"]
+           "replay.hip", "ceiling.hip", "check.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

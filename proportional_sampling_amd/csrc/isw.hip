@@ -273,6 +273,7 @@ extern "C" psamp_status psamp_is_weights(const void* prio, psamp_dtype prio_t, i
     if (!aligned(prio, 4) || !aligned(idx, 4) || !aligned(out_w, 4) || (need && !aligned(ws, 8)))
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
+    if (check_on()) check_i32(idx, k, n, st);
     if (prio_t == PSAMP_F32) return launch_isw<float>(prio, n, idx, k, alpha * beta, out_w, ws, st);
     return launch_isw<uint32_t>(prio, n, idx, k, beta, out_w, ws, st);
 }

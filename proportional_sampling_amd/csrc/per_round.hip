@@ -316,10 +316,26 @@ extern "C" size_t psamp_per_round_workspace_size(int64_t n, int64_t k) {
     return psamp_build_cdf_workspace_size(n);
 }
 
+static psamp_status per_round_impl(void* prio, int64_t n, double alpha, double beta,
+                                   const float* u, int64_t k, const float* new_prio,
+                                   int32_t* out_idx, float* out_w, double* cdf, double* total,
+                                   void* ws, size_t ws_bytes, void* stream);
+
 extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, double beta,
                                         const float* u, int64_t k, const float* new_prio,
                                         int32_t* out_idx, float* out_w, double* cdf,
                                         double* total, void* ws, size_t ws_bytes, void* stream) {
+    const bool chk = check_on();
+    const psamp_status e = per_round_impl(prio, n, alpha, beta, u, k, new_prio, out_idx, out_w,
+                                          cdf, total, ws, ws_bytes, stream);
+    if (chk && e == PSAMP_OK) check_total(total, PSAMP_F64, as_stream(stream));
+    return e;
+}
+
+static psamp_status per_round_impl(void* prio, int64_t n, double alpha, double beta,
+                                   const float* u, int64_t k, const float* new_prio,
+                                   int32_t* out_idx, float* out_w, double* cdf, double* total,
+                                   void* ws, size_t ws_bytes, void* stream) {
     if (!prio || !cdf || !total) return PSAMP_E_NULL;
     if (n < 1 || n > kMaxN || k < 0 || k > kMaxN) return PSAMP_E_SIZE;
     if (!(finite_d(alpha) && alpha > 0.0) || !(finite_d(beta) && beta >= 0.0)) return PSAMP_E_PARAM;
@@ -331,6 +347,12 @@ extern "C" psamp_status psamp_per_round(void* prio, int64_t n, double alpha, dou
                   (new_prio && !aligned(new_prio, 4))))
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
+    if (check_on()) {
+        // (checked before the update rewrites the drawn priorities)
+        check_prio((const float*)prio, n, st);
+        if (k > 0) check_unit(u, k, st);
+        if (k > 0 && new_prio) check_prio(new_prio, k, st);
+    }
     // The clearing of the other parity runs up to the largest tile count any
     // call on this workspace has used, which can exceed this call's: the
     // bound is the workspace's own capacity, not the one this n needs.

@@ -290,6 +290,10 @@ extern "C" psamp_status psamp_pf_step(const float* x, const float* logw, const f
     const int lw_vec = aligned(logw, 16) && P % 4 == 0;
     const bool pow2 = (P & (P - 1)) == 0;
     hipStream_t st = as_stream(stream);
+    if (check_on()) {
+        check_f32(logw, rows, P, P, kChkLogw, PSAMP_CHECK_LOGWEIGHT, st);
+        check_unit(u_row, rows, st);
+    }
     const int64_t R = ceil_div(P, kResThreads * 4);
     if (trace_enabled()) trace_launch("k_pf_step", rows, kResThreads, P);
     bool ok;

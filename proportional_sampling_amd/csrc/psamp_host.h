@@ -48,6 +48,21 @@ psamp_status launch_per_update(float* prio, int64_t n, double alpha, double beta
                                double* cdf, double* total, void* ws, size_t ws_bytes,
                                hipStream_t st);
 
+// Optional device-side precondition checks (check.hip).  check_on() is
+// cheap; the check_* launchers enqueue a check kernel on `st`.
+enum : int { kChkPrio = 0, kChkUnit = 1, kChkLogw = 2 };
+bool check_on();
+void check_f32(const float* a, int64_t rows, int64_t P, int64_t ld, int mode, uint64_t bit,
+               hipStream_t st);
+inline void check_prio(const float* p, int64_t n, hipStream_t st) {
+    check_f32(p, 1, n, n, kChkPrio, PSAMP_CHECK_PRIORITY, st);
+}
+inline void check_unit(const float* u, int64_t n, hipStream_t st) {
+    check_f32(u, 1, n, n, kChkUnit, PSAMP_CHECK_FRACTION, st);
+}
+void check_i32(const int32_t* idx, int64_t m, int64_t hi, hipStream_t st);
+void check_total(const void* t, int kind, hipStream_t st);
+
 // Optional launch trace: PSAMP_TRACE=1 prints one line per launch.
 bool trace_enabled();
 void trace_launch(const char* kernel, int64_t grid, int block, int64_t n);

@@ -86,6 +86,10 @@ extern "C" psamp_status psamp_resample_rows(const float* logw, int64_t rows, int
     const int vec_ok = aligned(logw, 16) && aligned(out_anc, 16) && ld_in % 4 == 0 &&
                        ld_out % 4 == 0;
     hipStream_t st = as_stream(stream);
+    if (check_on()) {
+        check_f32(logw, rows, P, ld_in, kChkLogw, PSAMP_CHECK_LOGWEIGHT, st);
+        check_unit(u_row, rows, st);
+    }
     const int64_t R = ceil_div(P, kResThreads * 4);
     if (R <= 1) launch_rows<1>(logw, rows, P, ld_in, u_row, out_anc, ld_out, vec_ok, st);
     else if (R <= 2) launch_rows<2>(logw, rows, P, ld_in, u_row, out_anc, ld_out, vec_ok, st);

@@ -296,6 +296,10 @@ extern "C" psamp_status psamp_sample(const void* cdf, psamp_dtype cdf_t, int64_t
     if (!aligned(cdf, csz) || !aligned(total, csz) || !aligned(u, 4) || !aligned(out_idx, 4))
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
+    if (check_on()) {
+        if (fp) check_unit((const float*)u, k, st);
+        check_total(total, cdf_t, st);
+    }
     if (stratified && strat_from_cdf(n, k)) {
         if (n <= ((int64_t)1 << 20)) return launch_strat<4>(cdf, cdf_t, n, total, u, k, out_idx, st);
         return launch_strat<8>(cdf, cdf_t, n, total, u, k, out_idx, st);

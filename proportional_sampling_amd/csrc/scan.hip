@@ -640,10 +640,15 @@ extern "C" psamp_status psamp_build_cdf(const void* prio, psamp_dtype prio_t, in
     if (!aligned(prio, 4) || !aligned(cdf, osz) || !aligned(total, osz) || !aligned(ws, 8))
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
-    if (in) return launch_build_cdf<uint32_t, uint64_t>(prio, n, 0.0, cdf, total, ws, ws_bytes, st);
-    if (cdf_t == PSAMP_F64)
-        return launch_build_cdf<float, double>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
-    return launch_build_cdf<float, float>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
+    const bool chk = check_on();
+    if (chk && fp) check_prio((const float*)prio, n, st);
+    psamp_status e;
+    if (in) e = launch_build_cdf<uint32_t, uint64_t>(prio, n, 0.0, cdf, total, ws, ws_bytes, st);
+    else if (cdf_t == PSAMP_F64)
+        e = launch_build_cdf<float, double>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
+    else e = launch_build_cdf<float, float>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
+    if (chk && e == PSAMP_OK) check_total(total, cdf_t, st);
+    return e;
 }
 
 extern "C" psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_t n,
@@ -677,16 +682,26 @@ extern "C" psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype pri
     const uint64_t max_slots = ws_tile_capacity(ws_bytes);
     const int vec_ok = aligned(cdf, 16);
     const SampleArgs sa{u, k, is_pow2(k) ? ilog2_exact(k) : -1, out_idx};
+    const bool chk = check_on();
+    if (chk && fp) {
+        check_prio((const float*)prio, n, st);
+        check_unit((const float*)u, k, st);
+    }
+    psamp_status e;
     if (in) {
         if (scan_rows_for(n) == 1)
-            return launch_scan_sample<4, uint32_t>(prio, n, 0.0, cdf, total, ws, max_slots, vec_ok,
-                                                   sa, st);
-        return launch_scan_sample<32, uint32_t>(prio, n, 0.0, cdf, total, ws, max_slots, vec_ok,
+            e = launch_scan_sample<4, uint32_t>(prio, n, 0.0, cdf, total, ws, max_slots, vec_ok,
                                                 sa, st);
-    }
-    if (scan_rows_for(n) == 1)
-        return launch_scan_sample<4, float>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, sa,
-                                            st);
-    return launch_scan_sample<32, float>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, sa,
+        else
+            e = launch_scan_sample<32, uint32_t>(prio, n, 0.0, cdf, total, ws, max_slots, vec_ok,
+                                                 sa, st);
+    } else if (scan_rows_for(n) == 1) {
+        e = launch_scan_sample<4, float>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, sa,
                                          st);
+    } else {
+        e = launch_scan_sample<32, float>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, sa,
+                                          st);
+    }
+    if (chk && e == PSAMP_OK) check_total(total, cdf_t, st);
+    return e;
 }

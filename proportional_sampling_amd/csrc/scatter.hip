@@ -80,6 +80,7 @@ extern "C" psamp_status psamp_scatter_lww(void* prio, psamp_dtype prio_t, int64_
     if (!aligned(prio, 4) || !aligned(idx, 4) || !aligned(vals, 4) || (!grouped && !aligned(ws, 4)))
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
+    if (check_on() && prio_t == PSAMP_F32) check_prio((const float*)vals, m, st);
     const int64_t grid = ceil_div(m, kScatThreads);
     if (grouped) {
         if (trace_enabled()) trace_launch("k_scatter_grouped", grid, kScatThreads, m);

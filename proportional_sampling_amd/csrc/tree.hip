@@ -395,8 +395,16 @@ extern "C" psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int6
     if (tree_t == PSAMP_F32 && !(finite_d(alpha) && alpha > 0.0)) return PSAMP_E_PARAM;
     if (!aligned(tree, 16) || !aligned(prio, 4)) return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
-    if (tree_t == PSAMP_F32) return launch_build<float, float>(tree, cap_pow2, prio, n_valid, alpha, st);
-    return launch_build<uint64_t, uint32_t>(tree, cap_pow2, prio, n_valid, 0.0, st);
+    const bool chk = check_on();
+    if (chk && tree_t == PSAMP_F32) check_prio((const float*)prio, n_valid, st);
+    const psamp_status e =
+        tree_t == PSAMP_F32 ? launch_build<float, float>(tree, cap_pow2, prio, n_valid, alpha, st)
+                            : launch_build<uint64_t, uint32_t>(tree, cap_pow2, prio, n_valid, 0.0, st);
+    if (chk && e == PSAMP_OK)
+        check_total(tree_t == PSAMP_F32 ? (const void*)((const float*)tree + 1)
+                                        : (const void*)((const uint64_t*)tree + 1),
+                     tree_t, st);
+    return e;
 }
 
 extern "C" size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m) {
@@ -419,6 +427,7 @@ extern "C" psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int
     if (!tree || !idx || !prio) return PSAMP_E_NULL;
     if (!aligned(tree, 16) || !aligned(prio, 4) || !aligned(idx, 4)) return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
+    if (check_on() && tree_t == PSAMP_F32) check_prio((const float*)prio, m, st);
     const int D = ilog2_exact(cap_pow2);
     // Batches larger than one workgroup go in order, chunk by chunk: later
     // chunks overwrite earlier ones, which keeps last-write-wins.
@@ -454,6 +463,7 @@ extern "C" psamp_status psamp_segtree_sample(const void* tree, psamp_dtype tree_
     if (!tree || !u || !out_idx) return PSAMP_E_NULL;
     if (!aligned(tree, 16) || !aligned(u, 4) || !aligned(out_idx, 4)) return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
+    if (check_on() && f) check_unit((const float*)u, k, st);
     const int D = ilog2_exact(cap_pow2);
     const int k_log2 = is_pow2(k) ? ilog2_exact(k) : -1;
     // Every workgroup copies the top levels (up to 32 KiB) into LDS: large

@@ -779,3 +779,13 @@ def test_per_round_one_workspace_shrinking_then_growing(ps):
             assert torch.equal(r, g), f"call {call}: {name}"
         assert torch.equal(P_ref, P_sh), f"call {call}: rewritten priorities"
     assert ws.errors() == 0
+
+
+@pytest.mark.parametrize("n,rows,nt", [(4, 8, True), (1 << 20, 8, True), ((1 << 22) + 12, 4, False),
+                                       (8200, 8, False), (4100, 2, False), ((1 << 20) + 4, 2, True)])
+def test_ceiling_copy(ps, n, rows, nt):
+    """The measurement aid copies every float to a double, tail included."""
+    src = torch.rand(n, device="cuda")
+    dst = torch.full((n,), -1.0, dtype=torch.float64, device="cuda")
+    ps.ceiling_copy(src, dst, rows, nt)
+    assert torch.equal(dst, src.double())
