@@ -17,18 +17,27 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "psamp_oracle.cpp")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# PSAMP_ORACLE_LIB names another build (the sanitized build of the CPU
+# sanitizer test); by default the in-tree liboracle.so.
+_LIB = os.environ.get("PSAMP_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 
 CXXFLAGS = ["-std=c++17", "-O2", "-ffp-contract=off", "-fno-fast-math",
             "-Wall", "-Wextra", "-shared", "-fPIC"]
 
 
-def build() -> str:
-    """Compile liboracle.so (always recompiles)."""
-    tmp = _LIB + ".tmp"
-    subprocess.check_call(["g++", *CXXFLAGS, "-o", tmp, _SRC])
-    os.replace(tmp, _LIB)
-    return _LIB
+SANITIZE = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+            "-fno-omit-frame-pointer", "-g"]
+
+
+def build(out: str | None = None, sanitize: bool = False) -> str:
+    """Compile liboracle.so (always recompiles); sanitize: with ASan + UBSan,
+    for the CPU sanitizer test (load it with the sanitizer runtime
+    preloaded)."""
+    lib = out or _LIB
+    tmp = lib + ".tmp"
+    subprocess.check_call(["g++", *CXXFLAGS, *(SANITIZE if sanitize else []), "-o", tmp, _SRC])
+    os.replace(tmp, lib)
+    return lib
 
 
 _lib = None

@@ -16,7 +16,9 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpsamp.so")
+# PSAMP_LIB names another build of the library (the host-sanitized build of
+# the CPU sanitizer test); by default the in-tree libpsamp.so.
+LIB_PATH = os.environ.get("PSAMP_LIB") or os.path.join(_HERE, "libpsamp.so")
 
 F32, F64, U32, U64, I32 = 0, 1, 2, 3, 4
 _DT = {torch.float32: F32, torch.float64: F64, torch.uint32: U32, torch.uint64: U64,

@@ -31,9 +31,16 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer for the CPU test of
+# the argument validation (the device code is built as usual).
+SANITIZE_HOST = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer",
+                 "-Xarch_host", "-g"]
+
+
+def _compile(src: str, objdir: str = OBJ, extra=()) -> str:
+    obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     msg = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in l)
@@ -44,20 +51,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    """Compile every kernel source for gfx950 and link libpsamp.so."""
-    os.makedirs(OBJ, exist_ok=True)
+def build(verbose: bool = True, sanitize_host: bool = False, out: str | None = None) -> str:
+    """Compile every kernel source for gfx950 and link libpsamp.so (or, with
+    sanitize_host, a copy whose host code carries ASan + UBSan, at `out`)."""
+    lib = out or LIB
+    objdir = OBJ if not sanitize_host else os.path.join(os.path.dirname(lib), "_obj_sanitize")
+    os.makedirs(objdir, exist_ok=True)
+    extra = SANITIZE_HOST if sanitize_host else []
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda s_: _compile(s_, objdir, extra), SOURCES))
+    tmp = lib + ".tmp"
+    # (a sanitized build leaves the sanitizer runtime's symbols to the
+    # runtime the process preloads)
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout + r.stderr)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 def clean() -> None:

@@ -2,6 +2,7 @@
 // launch tracing (PSAMP_TRACE=1) and the workspace error query.
 #include <stdio.h>
 #include <stdlib.h>
+#include <string.h>
 
 #include <mutex>
 
@@ -59,7 +60,12 @@ void trace_launch(const char* kernel, int64_t grid, int block, int64_t n) {
 using namespace psamp;
 
 extern "C" const char* psamp_status_string(psamp_status s) {
-    switch (s) {
+    // A C caller may pass any int: its bits are read as an int, since loading
+    // a value outside the enumerators' range as the enum type is undefined
+    // in C++.
+    int v = 0;
+    memcpy(&v, &s, sizeof(v) < sizeof(s) ? sizeof(v) : sizeof(s));
+    switch (v) {
         case PSAMP_OK: return "ok";
         case PSAMP_E_NULL: return "null pointer";
         case PSAMP_E_SIZE: return "size out of range";
@@ -69,6 +75,7 @@ extern "C" const char* psamp_status_string(psamp_status s) {
         case PSAMP_E_ALIGN: return "misaligned pointer";
         case PSAMP_E_LAUNCH: return "kernel launch failed";
         case PSAMP_E_UNSUPPORTED: return "unsupported";
+        default: break;
     }
     return "unknown status";
 }

@@ -240,3 +240,31 @@ def test_binding_fails_loudly_without_gpu_tensors():
     import proportional_sampling_amd as ps
     with pytest.raises(ValueError):
         ps.build_cdf(torch.ones(10, dtype=torch.float32), 0.6, ws=None)
+
+
+def test_noalloc_ceiling_and_check_host_paths(L):
+    """The paths of the later entry points that never reach the device:
+    the no-allocation update refuses sizes beyond its scratch (and bad
+    arguments) before any set-up; the copy-ceiling aid validates its
+    geometry; the check switch toggles and reports its state."""
+    na = L.psamp_per_round_noalloc
+    assert na(FAKE, (1 << 26) + 1, 0.6, 0.4, FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, None) == E_SIZE
+    assert na(FAKE, 0, 0.6, 0.4, FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, None) == E_SIZE
+    assert na(None, 100, 0.6, 0.4, FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, None) == E_NULL
+    assert na(FAKE, 100, 0.0, 0.4, FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, None) == E_PARAM
+    assert na(FAKE, 100, 0.6, float("nan"), FAKE, 8, None, FAKE, FAKE, FAKE, FAKE, None) == E_PARAM
+    cc = L.psamp_ceiling_copy
+    assert cc(None, FAKE, 1024, 8, 1, None) == E_NULL
+    assert cc(FAKE, FAKE, 1022, 8, 1, None) == E_SIZE
+    assert cc(FAKE, FAKE, 1024, 3, 1, None) == E_PARAM
+    assert cc(FAKE, FAKE, 1024, 2, 2, None) == E_PARAM
+    assert cc(FAKE + 4, FAKE, 1024, 2, 0, None) == E_ALIGN
+    prev = L.psamp_check_enable(-1)
+    try:
+        L.psamp_check_enable(1)
+        assert L.psamp_check_enable(-1) == 1
+        assert L.psamp_check_enable(0) == 1
+        assert L.psamp_check_enable(-1) == 0
+    finally:
+        L.psamp_check_enable(prev)
+    assert L.psamp_check_errors(None, 1, None) == E_NULL
