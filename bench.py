@@ -353,19 +353,21 @@ def sumtree_bench(ps, torch, rounds=200):
     v = torch.from_numpy(d["v"]).cuda()
     U = torch.from_numpy(d["U"]).cuda()
     out = torch.empty(d["U"].shape[1], dtype=torch.int32, device="cuda")
+    uws = ps.Workspace(ps.segtree_update_workspace_size(cap, 1024))
     it = {"r": 0}
 
     def one_round():
         r = it["r"] % rounds
         it["r"] += 1
-        ps.segtree_update(tree, idx[r], v[r], d["alpha"])
+        ps.segtree_update(tree, idx[r], v[r], d["alpha"], ws=uws)
         ps.segtree_sample(tree, nv, U[r], out=out)
 
     # each from a HIP graph of 32 calls (rounds r .. r + 31 for the round),
     # so that Python launches do not bound these short calls
     res = {"round_us": round(graph_us(torch, one_round, rounds), 2),
            "update_us": round(graph_us(torch, lambda: ps.segtree_update(tree, idx[0], v[0],
-                                                                         d["alpha"]), rounds), 2),
+                                                                         d["alpha"], ws=uws),
+                                       rounds), 2),
            "sample_us": round(graph_us(torch, lambda: ps.segtree_sample(tree, nv, U[0], out=out),
                                        rounds), 2)}
     res["samples_per_s"] = round(1024 / (res["sample_us"] * 1e-6))

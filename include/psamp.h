@@ -199,8 +199,13 @@ psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int64_t cap_pow
  * sum above it, and a descent that ends on it is clamped to n_valid - 1, so
  * callers keep idx_j below n_valid.  0 <= m <= 2^31 - 1 (m = 0 is a no-op
  * and may pass NULL pointers); the batch is processed in order, in chunks
- * of 1024 entries, so later entries still win over earlier ones.
- * ws: psamp_segtree_update_workspace_size(cap_pow2, m) bytes (0 today).
+ * of 1024 entries, so later entries still win over earlier ones.  Each
+ * chunk runs as 64 workgroups, one per subtree below the top 6 levels, and
+ * the workgroup that finishes last recomputes those levels; it finds out it
+ * is last through a counter in ws.
+ * ws: psamp_segtree_update_workspace_size(cap_pow2, m) bytes (256), 4-byte
+ *   aligned, zero-filled once after allocation (every call leaves it zero
+ *   again); one ws must not serve two updates that may run at the same time.
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_ALIGN, E_LAUNCH. */
 size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m);
 psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
@@ -229,7 +234,8 @@ psamp_status psamp_segtree_sample(const void* tree, psamp_dtype tree_t, int64_t 
  * memory, zero-filled by the caller before psamp_replay_init.  The struct is
  * host memory owned by the caller; insert advances cursor and size when it
  * enqueues.  ws: psamp_replay_workspace_size(capacity, largest batch) bytes
- * of device memory, zero-filled once (may be NULL when that size is 0).
+ * of device memory, zero-filled once: the tree update's workspace, then the
+ * IS weights'.
  * Calls are stream-ordered like the rest of the library; two streams must
  * not use one psamp_replay at the same time.
  * ---------------------------------------------------------------------- */

@@ -283,8 +283,15 @@ def segtree_build(tree: torch.Tensor, prio: torch.Tensor, alpha: float = 1.0,
 
 
 @_on_stream
+def segtree_update_workspace_size(cap_pow2: int, m: int) -> int:
+    return int(lib().psamp_segtree_update_workspace_size(int(cap_pow2), int(m)))
+
+
 def segtree_update(tree: torch.Tensor, idx: torch.Tensor, prio: torch.Tensor,
-                   alpha: float = 1.0, stream=None) -> torch.Tensor:
+                   alpha: float = 1.0, *, ws: Workspace | None = None,
+                   stream=None) -> torch.Tensor:
+    """Batched leaf update, last write wins; ws (zeroed once) may be reused
+    by every update on this stream."""
     cap = tree.numel() // 2
     m = idx.numel()
     if prio.numel() != m:
@@ -292,8 +299,10 @@ def segtree_update(tree: torch.Tensor, idx: torch.Tensor, prio: torch.Tensor,
     t = _dev(tree, "tree", (torch.float32, torch.uint64))
     i = _dev(idx, "idx", (torch.int32,))
     p = _dev(prio, "prio", (torch.float32, torch.uint32))
+    if ws is None:
+        ws = Workspace(segtree_update_workspace_size(cap, m), tree.device)
     _check("psamp_segtree_update", lib().psamp_segtree_update(
-        t, _DT[tree.dtype], cap, i, p, _DT[prio.dtype], m, float(alpha), None, 0,
+        t, _DT[tree.dtype], cap, i, p, _DT[prio.dtype], m, float(alpha), ws.ptr, ws.nbytes,
         _stream(stream)))
     return tree
 

@@ -35,13 +35,14 @@ static psamp_status check_rb(const psamp_replay* rb) {
 
 using namespace psamp;
 
+// The workspace: the tree update's (its counter) first, then the IS
+// weights' -- two regions, since both keep state from call to call.
+static size_t upd_ws_bytes() { return psamp_segtree_update_workspace_size(1, 1); }
+
 extern "C" size_t psamp_replay_workspace_size(int64_t capacity, int64_t max_batch) {
     const int64_t cp = psamp_segtree_cap_pow2(capacity);
     if (cp == 0 || max_batch < 0) return 0;
-    const size_t a = psamp_segtree_update_workspace_size(cp, max_batch < kTreeBatch ? max_batch
-                                                                                  : kTreeBatch);
-    const size_t b = psamp_is_weights_workspace_size(max_batch);
-    return a > b ? a : b;
+    return upd_ws_bytes() + psamp_is_weights_workspace_size(max_batch);
 }
 
 extern "C" psamp_status psamp_replay_init(psamp_replay* rb, int64_t capacity, double alpha,
@@ -70,9 +71,7 @@ extern "C" psamp_status psamp_replay_insert(psamp_replay* rb, const float* prio,
     if (m < 0 || m > kMaxN) return PSAMP_E_SIZE;
     if (!aligned(prio, 4) || !aligned(out_slots, 4)) return PSAMP_E_ALIGN;
     if (m == 0) return PSAMP_OK;
-    if (psamp_segtree_update_workspace_size(rb->cap_pow2, m < kTreeBatch ? m : kTreeBatch) >
-        rb->ws_bytes)
-        return PSAMP_E_WORKSPACE;
+    if (upd_ws_bytes() > rb->ws_bytes) return PSAMP_E_WORKSPACE;
     hipStream_t st = as_stream(stream);
     hipLaunchKernelGGL(k_ring_slots, dim3((unsigned)ceil_div(m, 256)), dim3(256), 0, st,
                        out_slots, m, rb->cursor, rb->capacity);
@@ -116,13 +115,15 @@ extern "C" psamp_status psamp_replay_sample(const psamp_replay* rb, const float*
     if (stratified != 0 && stratified != 1) return PSAMP_E_PARAM;
     if (out_w && (!(beta >= 0.0) || !finite_d(beta))) return PSAMP_E_PARAM;
     if (k == 0) return PSAMP_OK;
-    if (out_w && psamp_is_weights_workspace_size(k) > rb->ws_bytes) return PSAMP_E_WORKSPACE;
+    if (out_w && upd_ws_bytes() + psamp_is_weights_workspace_size(k) > rb->ws_bytes)
+        return PSAMP_E_WORKSPACE;
     s = psamp_segtree_sample(rb->tree, PSAMP_F32, rb->cap_pow2, rb->size, u, PSAMP_F32, k,
                              stratified, out_slots, stream);
     if (s != PSAMP_OK || !out_w) return s;
     // the leaves already hold p^alpha: IS = (L_min / L_i)^beta
     return psamp_is_weights(rb->tree + rb->cap_pow2, PSAMP_F32, rb->size, 1.0, out_slots, k,
-                            beta, out_w, rb->ws, rb->ws_bytes, stream);
+                            beta, out_w, (char*)rb->ws + upd_ws_bytes(),
+                            rb->ws_bytes - upd_ws_bytes(), stream);
 }
 
 extern "C" const float* psamp_replay_total(const psamp_replay* rb) {

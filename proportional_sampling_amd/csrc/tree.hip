@@ -11,20 +11,27 @@
 // Update ([SEGT] "Operations -- Update": write the leaf, recompute each
 // ancestor as left + right).  The page's one-thread-per-update kernel races
 // when two updates share an ancestor (a thread can read a stale sibling and
-// overwrite a correct parent) and on repeated indices.  Here one 1024-thread
-// workgroup handles a batch of up to 1024 updates deterministically:
-//   1. sort the (leaf, batch position) keys in LDS (stable radix sort on the
-//      leaf);
-//   2. keep the last entry of each run of equal leaves (largest batch
+// overwrite a correct parent) and on repeated indices.  Here a batch of up
+// to 1024 updates is split by subtree: 64 workgroups, one per subtree below
+// the top 6 levels, each deterministically
+//   1. keeps the entries whose leaf lies in its subtree (about 16 of 1024);
+//   2. sorts their (leaf, batch position) keys;
+//   3. keeps the last entry of each run of equal leaves (largest batch
 //      position: last write wins);
-//   3. each winning leaf's thread prefetches the old values of all siblings
-//      on its root path at once (one round of loads, no per-level latency);
-//   4. level by level, the first winner under each dirty node (its "owner")
-//      forms fl(left + right) from its own value, a clean sibling from its
-//      registers, or the dirty sibling's value from LDS; each owner also
-//      carries the index of the next owner, so it finds that sibling in O(1).
-// Every dirty node is written exactly once, after both children are final,
-// as fl(left + right): the tree stays bit-equal to a fresh build.
+//   4. fetches the old values of the siblings on each winner's path up to
+//      the subtree root (all at once, no per-level latency);
+//   5. level by level, lets the first winner under each dirty node (its
+//      "owner") form fl(left + right) from its own value, a clean sibling,
+//      or the dirty sibling's value held by the next owner (found through a
+//      carried index, so in O(1)).
+// With up to 64 entries (the usual case) one wave does 2-5: a direct ranking
+// in registers, the levels with cross-lane reads; above, the whole
+// workgroup: a stable radix sort in LDS and the levels through LDS.  The
+// workgroup that finishes last (an atomic counter in the caller's
+// workspace, which that workgroup resets) recomputes the 63 nodes above the
+// subtree roots.  Every dirty node is written once per call, after both of
+// its children are final, as fl(left + right) (the top levels are formed
+// again in full): the tree stays bit-equal to a fresh build.
 //
 // Sample ([SEGT] "Operations -- Sample"): descend from the root, left if
 // t <= left sum (or the right sum is 0), else subtract and go right.  The
@@ -52,6 +59,9 @@ __device__ __forceinline__ uint32_t wave_incl_u32(uint32_t x) {
     return x;
 }
 constexpr int kMaxDepth = 30;                    // cap <= 2^30
+constexpr int kUpdTopLevels = 6;                 // update: 2^6 subtree workgroups
+constexpr size_t kUpdWsBytes = 256;              // update: its counter (zeroed once)
+static_assert((1 << kUpdTopLevels) <= kWave, "the top levels are formed by one wave");
 constexpr int kSampleTreeThreads = 256;
 constexpr int kSampleTreeThreadsBig = 1024;      // large batches: fewer copies of the top levels
 constexpr int kSampleTreeDpt = 2;                // draws per thread in large batches
@@ -108,101 +118,41 @@ __global__ __launch_bounds__(kBuildThreads) void k_tree_build_pass(
     }
 }
 
+// Agent-scope (cross-XCD) loads and stores of one node, float or uint64.
+__device__ __forceinline__ void node_store_agent(float* p, float v) {
+    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void node_store_agent(uint64_t* p, uint64_t v) { store_agent(p, v); }
+__device__ __forceinline__ float node_load_agent(const float* p) {
+    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p),
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ uint64_t node_load_agent(const uint64_t* p) { return load_agent(p); }
+
+// A barrier of one wave: its lanes run in lockstep and its LDS accesses
+// complete in order; the wavefront-scope fences keep the compiler from
+// moving memory accesses across.
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Steps 4 and 5 of the update when a subtree has many winners (up to 1024;
+// wl, wj: leaves ascending and their batch positions), thread tid < u
+// taking winner tid: each prefetches the old values of all siblings on its
+// path up to the subtree root; then level by level the first winner under
+// each dirty node (its owner) forms fl(left + right) from its own value, a
+// clean sibling from its registers, or the dirty sibling's value from LDS
+// (the next owner's, found through the carried index).  The subtree's root
+// is stored at agent scope: the workgroup that finishes last reads it.
 template <class V, class P>
-__global__ __launch_bounds__(kUpdThreads) void k_tree_update(
-    V* __restrict__ tree, int64_t cap, int D, const int32_t* __restrict__ idx,
-    const P* __restrict__ prio, int m, double alpha) {
-    __shared__ uint64_t keys[kUpdThreads];
-    __shared__ uint32_t hist[256 * kUpdWaves];              // (digit, wave) counts, then offsets
-    __shared__ uint32_t hsum[kUpdWaves];
-    __shared__ uint32_t wcount[kUpdThreads / kWave];
-    __shared__ int32_t wl[kUpdThreads];                  // winner leaves, ascending
-    __shared__ int32_t wj[kUpdThreads];                  // their batch positions
-    __shared__ V vbuf[2][kUpdThreads];
-    __shared__ int32_t ebuf[2][kUpdThreads];
-    __shared__ uint32_t s_u;
-    __shared__ MathLds M;
-
+__device__ __forceinline__ void propagate(V* __restrict__ tree, int64_t cap, int Ds, int T, int u,
+                                          const int32_t* wl, const int32_t* wj, const P* pbuf,
+                                          V (*vbuf)[kUpdThreads], int32_t (*ebuf)[kUpdThreads],
+                                          double alpha, const MathLds* M) {
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
-    const int lane = tid & 63;
-    if (sizeof(P) == 4 && sizeof(V) == 4) math_lds_fill(&M, tid, kUpdThreads);
-
-    // 1. keys = (leaf << 32) | batch position, sorted.  A stable LSD radix
-    // sort on the leaf (8-bit digits; an out-of-range entry takes the key
-    // cap, above every leaf, and keeps its all-ones word) leaves equal
-    // leaves in batch order, i.e. the array sorted by the whole key: per
-    // pass, ballots rank each key among the lanes of its wave with the same
-    // digit, and a digit-major prefix over the per-wave counts places it --
-    // five barriers a pass and ceil((D + 1) / 8) passes, against the 55
-    // compare-exchange steps of a bitonic network.
-    uint64_t key = ~0ull;
-    if (tid < m) {
-        const int32_t l = idx[tid];
-        if (l >= 0 && (int64_t)l < cap) key = ((uint64_t)(uint32_t)l << 32) | (uint32_t)tid;
-    }
-    {
-        const uint64_t lane_lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-        const int passes = (D + 1 + 7) / 8;
-        for (int ps = 0; ps < passes; ++ps) {
-            const uint32_t lp = key == ~0ull ? (uint32_t)cap : (uint32_t)(key >> 32);
-            const uint32_t d = (lp >> (8 * ps)) & 255u;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) hist[4 * tid + c] = 0u;
-            __syncthreads();
-            uint64_t peers = ~0ull;
-#pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const uint64_t bal = __ballot((d >> b) & 1u);
-                peers &= ((d >> b) & 1u) ? bal : ~bal;
-            }
-            const uint32_t rank = (uint32_t)__popcll(peers & lane_lt);
-            if (rank == 0) hist[d * kUpdWaves + wave] = (uint32_t)__popcll(peers);
-            __syncthreads();
-            uint32_t h[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) h[c] = hist[4 * tid + c];
-            const uint32_t loc = (h[0] + h[1]) + (h[2] + h[3]);
-            const uint32_t inc = wave_incl_u32(loc);
-            if (lane == kWave - 1) hsum[wave] = inc;
-            __syncthreads();
-            uint32_t ex = inc - loc;
-            for (int w2 = 0; w2 < wave; ++w2) ex += hsum[w2];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                hist[4 * tid + c] = ex;
-                ex += h[c];
-            }
-            __syncthreads();
-            keys[hist[d * kUpdWaves + wave] + rank] = key;
-            __syncthreads();
-            key = keys[tid];
-        }
-    }
-
-    // 2. winners: the last key of each run of equal leaves.
-    const uint64_t my = keys[tid];
-    const uint64_t nx = tid + 1 < kUpdThreads ? keys[tid + 1] : ~0ull;
-    const bool win = my != ~0ull && (nx >> 32) != (my >> 32);
-    const uint64_t bal = __ballot(win);
-    if (lane == 0) wcount[wave] = (uint32_t)__popcll(bal);
-    __syncthreads();
-    uint32_t pos = (uint32_t)__popcll(bal & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-    uint32_t tot = 0;
-    for (int w2 = 0; w2 < kUpdThreads / kWave; ++w2) {
-        const uint32_t c = wcount[w2];
-        if (w2 < wave) pos += c;
-        tot += c;
-    }
-    if (win) {
-        wl[pos] = (int32_t)(my >> 32);
-        wj[pos] = (int32_t)(uint32_t)my;
-    }
-    if (tid == 0) s_u = tot;
-    __syncthreads();
-    const int u = (int)s_u;
-
-    // 3. per-winner state and the prefetch of all path siblings.
     const bool act = tid < u;
     int64_t L = 0, Lp = -1;
     V val = V(0);
@@ -211,29 +161,28 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
     if (act) {
         L = wl[tid];
         Lp = tid > 0 ? (int64_t)wl[tid - 1] : -1;
-        val = leaf_value(prio[wj[tid]], alpha, &M);
+        val = leaf_value(pbuf[wj[tid]], alpha, M);
 #pragma unroll
         for (int d = 0; d < kMaxDepth; ++d)
-            if (d < D) sib[d] = tree[((cap + L) >> d) ^ 1];
-        tree[cap + L] = val;
+            if (d < Ds) sib[d] = tree[((cap + L) >> d) ^ 1];
+        if (Ds == 0 && T > 0) node_store_agent(tree + cap + L, val);
+        else tree[cap + L] = val;
         vbuf[0][tid] = val;
         ebuf[0][tid] = end;
     }
     __syncthreads();
-
-    // 4. levels 1..D (unrolled so that sib[] stays in registers).
 #pragma unroll
     for (int d = 1; d <= kMaxDepth; ++d) {
-        if (d <= D) {
+        if (d <= Ds) {
             const int bi = (d - 1) & 1;
             const int bo = d & 1;
             const bool own = act && (tid == 0 || ((cap + Lp) >> d) != ((cap + L) >> d));
             if (own) {
-                const int64_t c = (cap + L) >> (d - 1);
-                const int64_t N = c >> 1;
+                const int64_t cn = (cap + L) >> (d - 1);
+                const int64_t N = cn >> 1;
                 V left, right;
                 int32_t ne = end;
-                if ((c & 1) == 0) {
+                if ((cn & 1) == 0) {
                     left = val;
                     const int32_t j = end;
                     if (j < u && ((cap + (int64_t)wl[j]) >> d) == N) {
@@ -248,13 +197,284 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
                 }
                 val = left + right;
                 end = ne;
-                tree[N] = val;
+                if (d == Ds && T > 0) node_store_agent(tree + N, val);
+                else tree[N] = val;
                 vbuf[bo][tid] = val;
                 ebuf[bo][tid] = end;
             }
             __syncthreads();
         }
     }
+}
+
+// One batch of up to 1024 updates.  Workgroup s of S = 2^T owns the subtree
+// below node S + s (the leaves whose top T of D bits are s): it keeps the
+// batch entries that fall there, resolves last-write-wins and recomputes
+// every dirty node of its subtree up to that node; the workgroup that
+// finishes last (a counter in the workspace, reset by that workgroup) then
+// recomputes the T levels above, from the S subtree roots.  No workgroup
+// waits for another, so the grid need not be resident at once.
+template <class V, class P>
+__global__ __launch_bounds__(kUpdThreads) void k_tree_update(
+    V* __restrict__ tree, int64_t cap, int D, int T, const int32_t* __restrict__ idx,
+    const P* __restrict__ prio, int m, double alpha, uint32_t* __restrict__ counter) {
+    __shared__ uint64_t keys[kUpdThreads];
+    __shared__ P pbuf[kUpdThreads];                      // the batch's values, by position
+    __shared__ uint32_t hist[256 * kUpdWaves];           // (digit, wave) counts, then offsets
+    __shared__ uint32_t hsum[kUpdWaves];
+    __shared__ uint32_t wcount[kUpdWaves];
+    __shared__ int32_t wl[kUpdThreads];                  // winner leaves, ascending
+    __shared__ int32_t wj[kUpdThreads];                  // their batch positions
+    __shared__ V vbuf[2][kUpdThreads];
+    __shared__ int32_t ebuf[2][kUpdThreads];
+    __shared__ uint32_t s_u, s_last;
+    __shared__ uint64_t s_sk[kWave];                     // few entries: keys in order,
+    __shared__ int32_t s_sp[kWave];                      //   their compact positions,
+    __shared__ V s_lv[kWave];                            //   leaf values by position
+    __shared__ MathLds M;
+
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6;
+    const int lane = tid & 63;
+    const uint64_t lane_lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+    const int S = 1 << T;
+    const int Ds = D - T;                                // levels inside a subtree
+    const int sub = (int)blockIdx.x;
+    if (sizeof(P) == 4 && sizeof(V) == 4) math_lds_fill(&M, tid, kUpdThreads);
+
+    // 1. this subtree's entries, keyed (leaf << 32) | batch position (an entry
+    // outside [0, cap) belongs to no subtree); the batch's values by position
+    uint64_t key = ~0ull;
+    P pv = P(0);
+    if (tid < m) {
+        const int32_t l = idx[tid];
+        pv = prio[tid];
+        pbuf[tid] = pv;
+        if (l >= 0 && (int64_t)l < cap && ((int64_t)l >> Ds) == sub)
+            key = ((uint64_t)(uint32_t)l << 32) | (uint32_t)tid;
+    }
+    const uint64_t sel = __ballot(key != ~0ull);
+    if (lane == 0) wcount[wave] = (uint32_t)__popcll(sel);
+    __syncthreads();
+    uint32_t pos = (uint32_t)__popcll(sel & lane_lt), c = 0;
+    for (int w2 = 0; w2 < kUpdWaves; ++w2) {
+        const uint32_t cw = wcount[w2];
+        if (w2 < wave) pos += cw;
+        c += cw;
+    }
+    if (c == 0) goto done;                               // (uniform: c is the same everywhere)
+
+    if (c <= (uint32_t)kWave) {
+        // 2-5, few entries (the usual case, about m / S): one wave does it.
+        // Each entry's thread loads its path siblings and forms its leaf
+        // value right away (the loads travel while wave 0 ranks the keys)
+        // and parks them in LDS by compact position; wave 0 ranks the keys
+        // by direct comparison, keeps the last entry of each leaf, and runs
+        // the levels in registers, each owner taking the dirty sibling's
+        // value from the next owner's lane.
+        V* sibl = &vbuf[0][0];                           // [d * kWave + pos]
+        V psib[kMaxDepth];
+        V lval = V(0);
+        if (key != ~0ull) {
+            const int64_t L = (int64_t)(key >> 32);
+            keys[pos] = key;
+#pragma unroll
+            for (int d = 0; d < kMaxDepth; ++d)
+                if (d < Ds) psib[d] = tree[((cap + L) >> d) ^ 1];
+            lval = leaf_value(pv, alpha, &M);
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // keys are distinct (batch positions differ): rank = #smaller
+            const uint64_t k_i = (uint32_t)lane < c ? keys[lane] : ~0ull;
+            uint32_t rank = 0;
+            for (int j = 0; j < (int)c; ++j) rank += readlane(k_i, j) < k_i ? 1u : 0u;
+            if ((uint32_t)lane < c) {
+                s_sk[rank] = k_i;
+                s_sp[rank] = lane;
+            }
+        }
+        if (key != ~0ull) {
+#pragma unroll
+            for (int d = 0; d < kMaxDepth; ++d)
+                if (d < Ds) sibl[d * kWave + pos] = psib[d];
+            s_lv[pos] = lval;
+        }
+        __syncthreads();
+        if (wave == 0) {
+            // winners: the last key of each run of equal leaves, moved to
+            // lanes 0..u-1 in leaf order
+            const uint64_t sk = (uint32_t)lane < c ? s_sk[lane] : ~0ull;
+            const int sp = (uint32_t)lane < c ? s_sp[lane] : 0;
+            const uint64_t nk = __shfl_down(sk, 1);
+            const bool win = (uint32_t)lane < c &&
+                             ((uint32_t)lane + 1 >= c || (nk >> 32) != (sk >> 32));
+            const uint64_t wb = __ballot(win);
+            const int u = (int)__popcll(wb);
+            if (win) {
+                const int wr = (int)__popcll(wb & lane_lt);
+                wl[wr] = (int32_t)(sk >> 32);
+                wj[wr] = sp;
+            }
+            wave_sync();
+            const bool act = lane < u;
+            const int p = act ? wj[lane] : 0;
+            const int64_t L = act ? (int64_t)wl[lane] : 0;
+            V val = act ? s_lv[p] : V(0);
+            const V leafv = val;
+            // (every lane shuffles: a lane reading from an inactive lane
+            // gets 0, so the shuffle must not sit under a branch)
+            const int Li = (int)L;                       // leaves < 2^30
+            const int Lprev = __shfl(Li, lane > 0 ? lane - 1 : 0);
+            const int Lp = lane > 0 ? Lprev : -1;
+            int end = lane + 1;
+            uint32_t owned = 0;
+            // A compact loop (the clean siblings come from LDS, the level
+            // values go to LDS, next to them: slot d - 1 of sibl is read
+            // before it is written): unrolled over 30 levels the code spread
+            // over many more instruction-cache lines, and a global store in
+            // the loop would make each level wait for the previous store.
+#pragma unroll 1
+            for (int d = 1; d <= Ds; ++d) {
+                // the next owner's leaf, value and next owner (every lane
+                // reads, before any lane updates its own)
+                const int j = end < kWave ? end : kWave - 1;
+                const int Lj = __shfl(Li, j);
+                const V vj = __shfl(val, j);
+                const int ej = __shfl(end, j);
+                const V sb = sibl[(d - 1) * kWave + p];
+                const bool own = act && (lane == 0 || (Lp >> d) != (Li >> d));
+                if (own) {
+                    V left, right;
+                    int ne = end;
+                    if (((Li >> (d - 1)) & 1) == 0) {
+                        left = val;
+                        if (end < u && (Lj >> d) == (Li >> d)) {
+                            right = vj;
+                            ne = ej;
+                        } else {
+                            right = sb;
+                        }
+                    } else {
+                        left = sb;
+                        right = val;
+                    }
+                    val = left + right;
+                    end = ne;
+                    owned |= 1u << d;
+                }
+                wave_sync();                       // every lane read slot d - 1
+                if (act) sibl[(d - 1) * kWave + lane] = val;
+            }
+            if (act) {
+                if (Ds == 0 && T > 0) node_store_agent(tree + cap + L, leafv);
+                else tree[cap + L] = leafv;
+#pragma unroll 1
+                for (int d = 1; d <= Ds; ++d) {
+                    if ((owned >> d) & 1u) {
+                        const int64_t N = (cap + L) >> d;
+                        const V x = sibl[(d - 1) * kWave + lane];
+                        if (d == Ds && T > 0) node_store_agent(tree + N, x);
+                        else tree[N] = x;
+                    }
+                }
+            }
+        }
+        goto done;
+    }
+
+    // 2. many entries: sorted by key, so that equal leaves are adjacent in
+    // batch order -- a stable LSD radix sort on the leaf over the whole
+    // workgroup (8-bit digits; per pass, ballots rank each key among the
+    // lanes of its wave with the same digit, and a digit-major prefix over
+    // the per-wave counts places it).
+    {
+        const int passes = (D + 1 + 7) / 8;
+        for (int ps = 0; ps < passes; ++ps) {
+            const uint32_t lp = key == ~0ull ? (uint32_t)cap : (uint32_t)(key >> 32);
+            const uint32_t d = (lp >> (8 * ps)) & 255u;
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) hist[4 * tid + cc] = 0u;
+            __syncthreads();
+            uint64_t peers = ~0ull;
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const uint64_t bal = __ballot((d >> b) & 1u);
+                peers &= ((d >> b) & 1u) ? bal : ~bal;
+            }
+            const uint32_t rank = (uint32_t)__popcll(peers & lane_lt);
+            if (rank == 0) hist[d * kUpdWaves + wave] = (uint32_t)__popcll(peers);
+            __syncthreads();
+            uint32_t h[4];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) h[cc] = hist[4 * tid + cc];
+            const uint32_t loc = (h[0] + h[1]) + (h[2] + h[3]);
+            const uint32_t inc = wave_incl_u32(loc);
+            if (lane == kWave - 1) hsum[wave] = inc;
+            __syncthreads();
+            uint32_t ex = inc - loc;
+            for (int w2 = 0; w2 < wave; ++w2) ex += hsum[w2];
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {
+                hist[4 * tid + cc] = ex;
+                ex += h[cc];
+            }
+            __syncthreads();
+            keys[hist[d * kUpdWaves + wave] + rank] = key;
+            __syncthreads();
+            key = keys[tid];
+        }
+    }
+    {
+        // 3. winners: the last key of each run of equal leaves (largest batch
+        // position: last write wins)
+        const uint64_t my = (uint32_t)tid < c ? keys[tid] : ~0ull;
+        const uint64_t nx = (uint32_t)tid + 1 < c ? keys[tid + 1] : ~0ull;
+        const bool win = my != ~0ull && (nx >> 32) != (my >> 32);
+        const uint64_t bal = __ballot(win);
+        if (lane == 0) wcount[wave] = (uint32_t)__popcll(bal);
+        __syncthreads();
+        uint32_t wp = (uint32_t)__popcll(bal & lane_lt);
+        uint32_t tot = 0;
+        for (int w2 = 0; w2 < kUpdWaves; ++w2) {
+            const uint32_t cw = wcount[w2];
+            if (w2 < wave) wp += cw;
+            tot += cw;
+        }
+        if (win) {
+            wl[wp] = (int32_t)(my >> 32);
+            wj[wp] = (int32_t)(uint32_t)my;
+        }
+        if (tid == 0) s_u = tot;
+        __syncthreads();
+    }
+    // 4, 5: the whole workgroup (the winners may be up to 1024)
+    propagate<V, P>(tree, cap, Ds, T, (int)s_u, wl, wj, pbuf, vbuf, ebuf, alpha, &M);
+
+done:
+    if (T == 0) return;
+    // 6. the last workgroup to get here recomputes the top T levels (every
+    // node there, from the S subtree roots: the same fl(left + right) a
+    // fresh build forms)
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        s_last = old == (uint32_t)S - 1 ? 1u : 0u;
+        if (s_last)
+            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    if (!s_last) return;
+    if (wave != 0) return;                               // S <= 64: one wave
+    V* top = vbuf[0];                                    // top[j]: node j, j in [1, 2S)
+    if (tid < S) top[S + tid] = node_load_agent(tree + S + tid);
+    wave_sync();
+    for (int h = S >> 1; h >= 1; h >>= 1) {
+        if (tid < h) top[h + tid] = top[2 * (h + tid)] + top[2 * (h + tid) + 1];
+        wave_sync();
+    }
+    if (tid >= 1 && tid < S) tree[tid] = top[tid];
 }
 
 // The threshold of draw i (see psamp_segtree_sample).
@@ -407,41 +627,44 @@ extern "C" psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int6
     return e;
 }
 
+// The update's workspace: the counter that finds the last subtree workgroup.
 extern "C" size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m) {
     (void)cap_pow2;
     (void)m;
-    return 0;
+    return kUpdWsBytes;
 }
 
 extern "C" psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int64_t cap_pow2,
                                              const int32_t* idx, const void* prio,
                                              psamp_dtype prio_t, int64_t m, double alpha, void* ws,
                                              size_t ws_bytes, void* stream) {
-    (void)ws;
-    (void)ws_bytes;
     if (!is_pow2(cap_pow2) || cap_pow2 > (int64_t(1) << kMaxDepth) || m < 0 || m > kMaxN)
         return PSAMP_E_SIZE;
     if (tree_types(tree_t, prio_t) != PSAMP_OK) return PSAMP_E_DTYPE;
     if (tree_t == PSAMP_F32 && !(finite_d(alpha) && alpha > 0.0)) return PSAMP_E_PARAM;
     if (m == 0) return PSAMP_OK;
     if (!tree || !idx || !prio) return PSAMP_E_NULL;
-    if (!aligned(tree, 16) || !aligned(prio, 4) || !aligned(idx, 4)) return PSAMP_E_ALIGN;
+    if (!ws || ws_bytes < kUpdWsBytes) return PSAMP_E_WORKSPACE;
+    if (!aligned(tree, 16) || !aligned(prio, 4) || !aligned(idx, 4) || !aligned(ws, 4))
+        return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
     if (check_on() && tree_t == PSAMP_F32) check_prio((const float*)prio, m, st);
     const int D = ilog2_exact(cap_pow2);
+    // S = 2^T subtree workgroups (each subtree keeps at least one level)
+    const int T = D - 1 < kUpdTopLevels ? (D > 1 ? D - 1 : 0) : kUpdTopLevels;
     // Batches larger than one workgroup go in order, chunk by chunk: later
     // chunks overwrite earlier ones, which keeps last-write-wins.
     for (int64_t off = 0; off < m; off += kUpdThreads) {
         const int mm = (int)min_<int64_t>(kUpdThreads, m - off);
-        if (trace_enabled()) trace_launch("k_tree_update", 1, kUpdThreads, mm);
+        if (trace_enabled()) trace_launch("k_tree_update", int64_t(1) << T, kUpdThreads, mm);
         if (tree_t == PSAMP_F32)
-            hipLaunchKernelGGL((k_tree_update<float, float>), dim3(1), dim3(kUpdThreads), 0, st,
-                               (float*)tree, cap_pow2, D, idx + off, (const float*)prio + off, mm,
-                               alpha);
+            hipLaunchKernelGGL((k_tree_update<float, float>), dim3(1u << T), dim3(kUpdThreads), 0,
+                               st, (float*)tree, cap_pow2, D, T, idx + off,
+                               (const float*)prio + off, mm, alpha, (uint32_t*)ws);
         else
-            hipLaunchKernelGGL((k_tree_update<uint64_t, uint32_t>), dim3(1), dim3(kUpdThreads), 0,
-                               st, (uint64_t*)tree, cap_pow2, D, idx + off,
-                               (const uint32_t*)prio + off, mm, 0.0);
+            hipLaunchKernelGGL((k_tree_update<uint64_t, uint32_t>), dim3(1u << T),
+                               dim3(kUpdThreads), 0, st, (uint64_t*)tree, cap_pow2, D, T,
+                               idx + off, (const uint32_t*)prio + off, mm, 0.0, (uint32_t*)ws);
         psamp_status e = launch_status();
         if (e != PSAMP_OK) return e;
     }

@@ -317,3 +317,53 @@ def test_resample_rows_beyond_2p31_elements(ps):
     assert bool((anc >= 0).all()) and bool((anc < P).all())
     del anc
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("cap", [1, 2, 4, 8, 64, 128, 256, 4096])
+def test_tree_update_small_trees(ps, cap):
+    """Trees with fewer levels than the update's split (1 to 64 subtree
+    workgroups): random batches with repeats, f32 against the pointer tree
+    bit for bit, u64 exactly; one update workspace for all calls."""
+    rng = np.random.default_rng(cap)
+    p0 = si.generic_f32(cap, cap + 1, "uniform")
+    tree = torch.zeros(2 * cap, dtype=torch.float32, device="cuda")
+    ps.segtree_build(tree, dev(p0), 0.6)
+    ot = oracle.Tree("f32", cap).build(p0, cap, 0.6)
+    q0 = si.sweep_u32(cap)
+    treeq = torch.zeros(2 * cap, dtype=torch.uint64, device="cuda")
+    ps.segtree_build(treeq, dev(q0))
+    otq = oracle.Tree("u64", cap).build(q0, cap)
+    ws = ps.Workspace(ps.segtree_update_workspace_size(cap, 1024))
+    for m in (1, 3, 100, 1024, 3000):
+        idx = rng.integers(0, cap, m).astype(np.int32)
+        v = si.generic_f32(m, m + cap, "uniform")
+        ps.segtree_update(tree, dev(idx), dev(v), 0.6, ws=ws)
+        ot.update(idx, v, 0.6)
+        check_f32_tree(host(tree), ot, cap, f"cap {cap} m {m}")
+        q = si.sweep_u32(m)
+        ps.segtree_update(treeq, dev(idx), dev(q), ws=ws)
+        otq.update(idx, q)
+        assert np.array_equal(host(treeq)[1:], otq.flat()[1:]), (cap, m)
+    assert int(host(ws.buf).astype(np.int64).sum()) == 0     # the counter is back at 0
+
+
+@pytest.mark.parametrize("per_sub", [63, 64, 65, 200])
+def test_tree_update_crowded_subtree(ps, per_sub):
+    """A subtree that receives per_sub entries of the batch (ranked in one
+    wave up to 64, radix-sorted above), with repeats, next to sparsely
+    updated subtrees."""
+    cap = 1 << 19
+    rng = np.random.default_rng(per_sub)
+    p0 = si.generic_f32(cap, 5, "uniform")
+    tree = torch.zeros(2 * cap, dtype=torch.float32, device="cuda")
+    ps.segtree_build(tree, dev(p0), 0.6)
+    ot = oracle.Tree("f32", cap).build(p0, cap, 0.6)
+    sub = cap // 64
+    crowd = rng.integers(5 * sub, 5 * sub + per_sub // 2 + 1, per_sub)   # repeats too
+    rest = rng.integers(0, cap, 1024 - per_sub)
+    idx = np.concatenate([crowd, rest]).astype(np.int32)
+    rng.shuffle(idx)
+    v = si.generic_f32(1024, per_sub + 7, "uniform")
+    ps.segtree_update(tree, dev(idx), dev(v), 0.6)
+    ot.update(idx, v, 0.6)
+    check_f32_tree(host(tree), ot, cap, f"crowded {per_sub}")
