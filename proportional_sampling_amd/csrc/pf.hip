@@ -80,7 +80,6 @@ __global__ __launch_bounds__(kResThreads) void k_pf_step(
     static_assert(RW * D <= kPfMaxLds, "pred does not fit the LDS budget");
     __shared__ __attribute__((aligned(16))) float predS[D * RW];
     __shared__ ResLds<R> L;
-    __shared__ MathLds M;
 
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
@@ -89,7 +88,7 @@ __global__ __launch_bounds__(kResThreads) void k_pf_step(
     const float* eb = eps + b * P * D;
     const float* lb = lw + b * P;
     const float* ob = obs + (int64_t)b * O;
-    const MathRegs mr = math_load(tid);
+    const double et = exp_row_tab_load(tid);     // (the exp table, with the first loads)
     const float ub = u_row[b];
     const float ninf = __int_as_float(0xFF800000);
 
@@ -128,7 +127,7 @@ __global__ __launch_bounds__(kResThreads) void k_pf_step(
     for (int d = 0; d < D; ++d)
 #pragma unroll
         for (int k = 0; k < D; ++k) Am[d][k] = A[d * D + k];
-    math_store(&M, tid, mr);
+    L.etab[tid] = et;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -179,7 +178,7 @@ __global__ __launch_bounds__(kResThreads) void k_pf_step(
     }
 
     uint32_t a[R][4];
-    res_ancestors<R, POW2>(v, Pi, ub, &M, L, a);
+    res_ancestors<R, POW2>(v, Pi, ub, L, a);
 
     // every read of L.O happened before the last barrier of res_ancestors:
     // reuse it to hand the ancestors to the gather layout

@@ -12,12 +12,11 @@ __global__ __launch_bounds__(kResThreads) void k_resample_rows(
     int32_t* __restrict__ anc, int64_t ld_out, int vec_ok) {
     constexpr int ROW = kResThreads * 4;
     __shared__ ResLds<R> L;
-    __shared__ MathLds M;
 
     const int tid = threadIdx.x;
     const int64_t b = blockIdx.x;
     const float* x = lw + b * ld_in;
-    const MathRegs mr = math_load(tid);
+    const double et = exp_row_tab_load(tid);     // (the exp table, with the first loads)
     const float ub = u_row[b];
 
     const float ninf = __int_as_float(0xFF800000);
@@ -39,11 +38,11 @@ __global__ __launch_bounds__(kResThreads) void k_resample_rows(
                 v[r][c] = j < P ? t : ninf;
             }
     }
-    math_store(&M, tid, mr);
+    L.etab[tid] = et;
 
     const int Pi = (int)P;
     uint32_t a[R][4];
-    res_ancestors<R, POW2>(v, Pi, ub, &M, L, a);
+    res_ancestors<R, POW2>(v, Pi, ub, L, a);
 
     int32_t* out = anc + b * ld_out;
 #pragma unroll

@@ -57,32 +57,38 @@ __device__ __forceinline__ double res_threshold(int k, float ub, float Pf, float
 template <bool POW2>
 __device__ __forceinline__ int res_count_le(double x, float ub, float Pf, float invP, int P) {
     constexpr double kEps = POW2 ? 0x1p-11 : 0x1p-9;
-    const double y = x * (double)P - (double)ub;
+    const double y = fma(x, (double)P, -(double)ub);  // one rounding
     const double e = floor(y);
     const double fr = y - e;                          // exact (Sterbenz)
-    const int k = !(e >= 0.0) ? 0 : (e >= (double)P ? P : (int)e + 1);
-    const bool sure = (fr >= kEps && fr <= 1.0 - kEps) || e >= (double)P || e <= -2.0;
-    if (__builtin_expect(sure, 1)) return k;
+    // floor(y) + 1 clamped to [0, P] (the conversion saturates; NaN gives 0)
+    const int k = max_(min_((int)e, P - 1) + 1, 0);
+    // fr in [eps, 1 - eps] (fr - 0.5 is exact: fr is a multiple of 2^-40)
+    if (__builtin_expect(fabs(fr - 0.5) <= 0.5 - kEps, 1)) return k;
     const bool over = k > 0 && res_threshold<POW2>(k - 1, ub, Pf, invP) > x;
     const bool under = k < P && res_threshold<POW2>(k, ub, Pf, invP) <= x;
     return k - (over ? 1 : 0) + (under ? 1 : 0);
 }
 
-// exp(x) for x <= 0 (finite; a NaN passes through): exp2_tab without its
-// clamp and NaN select, the same bits -- for x below the range that the
-// clamp guards the integer conversion saturates and ldexp still gives 0.
-__device__ __forceinline__ double exp_nonpos(double x, const MathLds* M) {
-    const double y = x * kLog2e;
-    const double N = rint(y * 64.0);
-    const double f = fma(N, -1.0 / 64.0, y);
+// exp(x) for x <= 0 in double, to about 1e-13 relative (the weights need
+// about 1e-9 for the ancestors to follow an exact-arithmetic reading):
+// x = N ln2/256 + g with |g| <= ln2/512, exp(x) = 2^(N/256) e^g, 2^(j/256)
+// from a 256-entry table (correctly rounded), e^g from its cubic Taylor
+// polynomial (truncation below 1.4e-13 relative); ln2/256 rounded to double
+// adds at most |N| 2^-61 to g.  x below the double range gives 0 (the
+// conversion saturates and ldexp underflows); a NaN passes through.
+__device__ __forceinline__ double exp_row(double x, const double* __restrict__ tab) {
+    const double N = rint(x * 0x1.71547652b82fep+8);          // 256 / ln 2
+    const double g = fma(N, -0x1.62e42fefa39efp-9, x);        // ln 2 / 256
     const int Ni = (int)N;
-    const double g = f * kLn2;
-    double q = fma(g, 1.0 / 120.0, 1.0 / 24.0);
-    q = fma(g, q, 1.0 / 6.0);
-    q = fma(g, q, 0.5);
-    q = fma(g, q, 1.0);
-    const double s = M->exp_tab[Ni & 63];
-    return ldexp(fma(s, g * q, s), Ni >> 6);
+    const double b = fma(g, fma(g, 1.0 / 6.0, 0.5), 1.0);
+    const double s = tab[Ni & 255];
+    return ldexp(fma(s, g * b, s), Ni >> 8);
+}
+
+// The table of exp_row, one entry per thread of a 256-thread block: each
+// thread loads its entry with its first loads and stores it to LDS later.
+__device__ __forceinline__ double exp_row_tab_load(int tid) {
+    return __longlong_as_double((long long)kExp2Tab256[tid & 255]);
 }
 
 template <int R>
@@ -92,20 +98,19 @@ struct ResLds {
     uint32_t s_wm[4][R];
     uint32_t s_lastk[4][R];
     double s_wtot[4][R];
-    double s_wmax[4][R];
     float s_max[4];
     double s_sum[4];
+    double etab[256];          // the table of exp_row (the caller stores it)
 };
 
 // The ancestors of one row.  v: this thread's log-weights r*1024 + 4t + c
 // (-inf past the end of the row).  On return anc[r][c] is the ancestor of
-// offspring k = r*1024 + 4t + c (k < P).  M must be written and visible
-// after the first barrier (the caller stores it before calling).
+// offspring k = r*1024 + 4t + c (k < P).  L.etab must be written (thread t
+// entry t, exp_row_tab_load) and is read after the first barrier.
 // POW2: P is a power of two (see res_threshold).
 template <int R, bool POW2>
 __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, float ub,
-                                              const MathLds* M, ResLds<R>& L,
-                                              uint32_t (&anc)[R][4]) {
+                                              ResLds<R>& L, uint32_t (&anc)[R][4]) {
     constexpr int ROW = kResThreads * 4;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
@@ -131,7 +136,7 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const double e = (v[r][c] == ninf) ? 0.0 : exp_nonpos((double)v[r][c] - m, M);
+            const double e = (v[r][c] == ninf) ? 0.0 : exp_row((double)v[r][c] - m, L.etab);
             q[r][c] = e;
             ssum = ssum + e;
         }
@@ -141,7 +146,7 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
     const double s = ((L.s_sum[0] + L.s_sum[1]) + L.s_sum[2]) + L.s_sum[3];
     const double inv_s = 1.0 / s;
 
-    // W_j = e_j / s; inclusive scan of W (double); M = its running max
+    // W_j = e_j / s; C = inclusive scan of W (double)
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -152,14 +157,18 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
     double X[R];
     double A;
     tile_scan_256<R, double>(q, X, A, L.s_wtot);
-    tile_local_values<R, double>(q, X, L.s_wmax);
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) q[r][c] = X[r] + q[r][c];
 
-    // ancestors: particle j takes k in [#{t <= M_{j-1}}, #{t <= M_j}); the
-    // last particle also every k above.  O[k] = j + 1 at the first k of each
-    // non-empty range, 0 elsewhere.  kc: the counts at this thread's values;
-    // kp[r]: the count at the element before its first element of row r
-    // (the neighbour's last count, through DPP and, across waves and rows,
-    // LDS).
+    // ancestors: with M_j = max_{i <= j} C_i, particle j takes the k in
+    // [#{t <= M_{j-1}}, #{t <= M_j}), the last particle also every k above
+    // ("first j with C_j >= t" is "first j with M_j >= t").  The count is
+    // non-decreasing in its argument, so #{t <= M_j} = max_{i <= j} #{t <=
+    // C_i}: a running max of integers over the counts at the C values, which
+    // need not be monotone themselves.  O[k] = j + 1 at the first k of each
+    // non-empty range, 0 elsewhere.
     const float Pf = (float)Pi;
     const float invP = 1.0f / Pf;              // exact when POW2
     uint32_t kc[R][4];
@@ -170,26 +179,48 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
             const int j = r * ROW + 4 * tid + c;
             kc[r][c] = (uint32_t)((j >= Pi - 1) ? Pi : res_count_le<POW2>(q[r][c], ub, Pf, invP, Pi));
         }
-    uint32_t kp[R];
+    // running max in element order: within the thread's 4, across the
+    // wave's lanes (DPP), then across waves and rows (LDS)
+    uint32_t kx[R];                            // max over the elements before the thread's first in row r, within its wave
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-        kp[r] = dpp32<kWaveShr1, 0xF, true>(kc[r][3]);
-        if (lane == kWave - 1) L.s_lastk[wave][r] = kc[r][3];
+        kc[r][1] = max_(kc[r][0], kc[r][1]);
+        kc[r][2] = max_(kc[r][1], kc[r][2]);
+        kc[r][3] = max_(kc[r][2], kc[r][3]);
+        uint32_t y = kc[r][3];
+        y = max_(y, dpp32<kRowShr1, 0xF, true>(y));
+        y = max_(y, dpp32<kRowShr2, 0xF, true>(y));
+        y = max_(y, dpp32<kRowShr4, 0xF, true>(y));
+        y = max_(y, dpp32<kRowShr8, 0xF, true>(y));
+        y = max_(y, dpp32<kRowBcast15, 0xA, false>(y));
+        y = max_(y, dpp32<kRowBcast31, 0xC, false>(y));
+        kx[r] = dpp32<kWaveShr1, 0xF, true>(y);
+        const uint32_t wm = (uint32_t)__builtin_amdgcn_readlane((int)y, kWave - 1);
+        if (lane == 0) L.s_lastk[wave][r] = wm;
         *reinterpret_cast<uint2*>(&L.O[r * ROW + 4 * tid]) = make_uint2(0u, 0u);
     }
     __syncthreads();
+    {
+        uint32_t carry = 0u;                   // max over the earlier rows
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-        if (lane == 0)
-            kp[r] = wave > 0 ? L.s_lastk[wave - 1][r] : (r > 0 ? L.s_lastk[3][r - 1] : 0u);
-        const int j0 = r * ROW + 4 * tid;
-        uint32_t k0 = j0 == 0 ? 0u : kp[r];
+        for (int r = 0; r < R; ++r) {
+            uint32_t pm = carry, rm = carry;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const int j = j0 + c;
-            const uint32_t k1 = kc[r][c];
-            if (j < Pi && k1 > k0) L.O[k0] = (uint16_t)(j + 1);
-            k0 = k1 > k0 ? k1 : k0;
+            for (int w2 = 0; w2 < 4; ++w2) {
+                const uint32_t t = L.s_lastk[w2][r];
+                if (w2 < wave) pm = max_(pm, t);
+                rm = max_(rm, t);
+            }
+            carry = rm;
+            uint32_t k0 = max_(pm, kx[r]);
+            const int j0 = r * ROW + 4 * tid;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int j = j0 + c;
+                const uint32_t k1 = max_(kc[r][c], k0);
+                if (j < Pi && k1 > k0) L.O[k0] = (uint16_t)(j + 1);
+                k0 = k1;
+            }
         }
     }
     __syncthreads();
