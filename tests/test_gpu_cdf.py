@@ -103,14 +103,15 @@ def test_scan_many_groups(ps):
     assert host(tot)[0] == C_g[-1]
 
 
+@pytest.mark.parametrize("n", [(1 << 20) + 1000, 8000])
 @pytest.mark.parametrize("alpha", [0.05, 0.6, 1.0, 2.0, 7.5, 16.0, 17.0])
-def test_scan_pow_extremes_large_tiles(ps, alpha):
-    """8-row tiles (n > 2^20), where p^alpha comes from per-workgroup tables
-    for alpha <= 16 (17 takes the general pow): subnormal, tiny, huge, zero
-    and unit priorities.  The first 4096 elements are all tiny, so the CDF
-    there checks the relative accuracy of small weights; the rest spans the
-    whole float range alpha allows without overflow."""
-    n = (1 << 20) + 1000
+def test_scan_pow_extremes_large_tiles(ps, alpha, n):
+    """8-row tiles (n > 2^20) and small inputs (n <= 8192), where p^alpha
+    comes from per-workgroup tables for alpha <= 16 (17 takes the general
+    pow): subnormal, tiny, huge, zero and unit priorities.  The first 4096
+    elements are all tiny, so the CDF there checks the relative accuracy of
+    small weights; the rest spans the whole float range alpha allows without
+    overflow.  The fused update on the same input gives the same CDF."""
     rng = np.random.default_rng(int(alpha * 100))
     hi = min(38.0, 300.0 / alpha)
     lo = max(-44.5, -300.0 / alpha)
@@ -125,10 +126,14 @@ def test_scan_pow_extremes_large_tiles(ps, alpha):
     C_g = host(cdf)
     pos = C_o > 0
     e_rel = float(np.max(np.abs(C_g[pos] - C_o[pos]) / C_o[pos]))
-    say(f"pow extremes alpha={alpha}: max rel CDF err {e_rel:.3e}")
+    say(f"pow extremes alpha={alpha} n={n}: max rel CDF err {e_rel:.3e}")
     assert np.all(C_g[~pos] == 0)
     assert e_rel <= 1e-12
     assert np.all(np.diff(C_g) >= 0)
+    if n <= 8192:
+        U = si.uniform_f32(np.random.default_rng(n), 1000)
+        _, _, cdf_r, _ = ps.per_round(dev(p), dev(U), alpha, 0.5)
+        assert np.array_equal(host(cdf_r), C_g)
 
 
 # Large-tile sizes (8192-element tiles) past what one round of workgroups
