@@ -88,7 +88,7 @@ struct StratCountFp {
     double T, kT, inv_k;
     bool pow2;
     __device__ __forceinline__ double thr(int64_t i) const {
-        const double a = (double)i + (double)U[i];
+        const double a = (double)(int32_t)i + (double)U[i];     // i < k <= 2^31 - 1
         const double b = pow2 ? a * inv_k : a / (double)k;
         return b * T;
     }
@@ -201,13 +201,23 @@ __device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_
     // threads agree on the count at their shared boundary and every draw is
     // written once more than zero times)
     const int64_t span = whi - wlo;
+    // the widest window of the wave bounds the count loop for every lane
+    // (mostly 2 or 3 of the 8 slots: 2^20 draws over 2^24 uniform
+    // priorities 43.7 -> 39.2 us, LogNormal 49.7 -> 48.3 us)
+    int smax = win ? (int)span : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) smax = max_(smax, __shfl_xor(smax, m));
+    smax = __builtin_amdgcn_readfirstlane(smax);
     auto count = [&](V v) -> int64_t {
         if (!win) return strat_count(F, v);
         v = v > xl ? xl : v;
         if (!first) v = v < xp ? xp : v;
         int64_t c = wlo;
 #pragma unroll
-        for (int w = 0; w < kStratWin; ++w) c += (w <= span && t[w] <= v) ? 1 : 0;
+        for (int w = 0; w < kStratWin; ++w) {
+            if (w > smax) break;                          // (uniform in the wave)
+            c += (w <= span && t[w] <= v) ? 1 : 0;
+        }
         return c;
     };
     int64_t lo = first ? 0 : count(xp);
