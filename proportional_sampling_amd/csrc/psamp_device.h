@@ -127,21 +127,42 @@ __device__ __forceinline__ void status_dec(uint64_t w, double& v) {
 __device__ __forceinline__ void status_dec(uint64_t w, uint64_t& v) { v = w - 1; }
 
 // ------------------------------------------------------------ fp64 math
-// log2 and exp2 in double, accurate to a few 1e-16 relative (exp2) and a
-// few 1e-16 absolute (log2) -- far below what the sampling contract needs
-// (about 1e-9 on the weights).  Tables live in LDS (one copy per
-// workgroup): entry k of the log table holds {c_k, -log2(c_k)}.
+// log2 and exp2 in double: exp2 within 2.3e-16 relative (normal results),
+// log2 within 2.6e-16 of max(1, |log2 x|) (both measured on the host
+// against long double over every float exponent) -- far below what the
+// sampling contract needs (about 1e-9 on the weights).  Tables live in LDS
+// (one copy per workgroup): entry k of the log table holds {c_k, -log2(c_k)}.
+// Bit views, usable on the host too (the math below is also compiled for the
+// host, where its error bounds are tested against long double).
+__host__ __device__ __forceinline__ uint64_t bits_of(double x) {
+    return __builtin_bit_cast(uint64_t, x);
+}
+__host__ __device__ __forceinline__ double double_of(uint64_t b) {
+    return __builtin_bit_cast(double, b);
+}
+__host__ __device__ __forceinline__ double double_of_hi(uint32_t hi, uint32_t lo) {
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__host__ __device__ __forceinline__ float float_of(uint32_t b) {
+    return __builtin_bit_cast(float, b);
+}
+__host__ __device__ __forceinline__ double2 dpair(double x, double y) {
+    double2 r;
+    r.x = x;
+    r.y = y;
+    return r;
+}
+
 struct MathLds {
     double2 log_tab[128];
     double exp_tab[64];
 };
 
-__device__ __forceinline__ void math_lds_fill(MathLds* m, int tid, int nthreads) {
+__host__ __device__ __forceinline__ void math_lds_fill(MathLds* m, int tid, int nthreads) {
     for (int i = tid; i < 128; i += nthreads)
-        m->log_tab[i] = make_double2(__longlong_as_double((long long)kLog2Tab[i][0]),
-                                     __longlong_as_double((long long)kLog2Tab[i][1]));
+        m->log_tab[i] = dpair(double_of(kLog2Tab[i][0]), double_of(kLog2Tab[i][1]));
     for (int i = tid; i < 64; i += nthreads)
-        m->exp_tab[i] = __longlong_as_double((long long)kExp2Tab[i][0]);
+        m->exp_tab[i] = double_of(kExp2Tab[i][0]);
 }
 
 // The same in two steps for blocks of at least 128 threads: math_load()
@@ -155,9 +176,8 @@ __device__ __forceinline__ MathRegs math_load(int tid) {
     // Unconditional loads (indices wrapped): a guarded load would be merged
     // with its guarded LDS store and waited for on the spot.
     MathRegs r;
-    r.lg = make_double2(__longlong_as_double((long long)kLog2Tab[tid & 127][0]),
-                        __longlong_as_double((long long)kLog2Tab[tid & 127][1]));
-    r.ex = __longlong_as_double((long long)kExp2Tab[tid & 63][0]);
+    r.lg = dpair(double_of(kLog2Tab[tid & 127][0]), double_of(kLog2Tab[tid & 127][1]));
+    r.ex = double_of(kExp2Tab[tid & 63][0]);
     return r;
 }
 __device__ __forceinline__ void math_store(MathLds* m, int tid, const MathRegs& r) {
@@ -173,11 +193,11 @@ constexpr double kLn2 = 0.69314718055994530942;
 // x = 2^e * m, m in [1,2); k = top 7 fraction bits of m; c_k ~ 1/m (21
 // bits) so r = m*c_k - 1 is exact and |r| < 2^-8; ln(1+r) by Taylor to r^6
 // (truncation < 3e-18).
-__device__ __forceinline__ double log2_sig32(double x, const MathLds* M) {
-    uint64_t b = (uint64_t)__double_as_longlong(x);
+__host__ __device__ __forceinline__ double log2_sig32(double x, const MathLds* M) {
+    uint64_t b = bits_of(x);
     int e = (int)(b >> 52) - 1023;
     int k = (int)(b >> 45) & 127;
-    double m = __longlong_as_double((long long)((b & 0x000FFFFFFFFFFFFFull) | 0x3FF0000000000000ull));
+    double m = double_of((b & 0x000FFFFFFFFFFFFFull) | 0x3FF0000000000000ull);
     double2 ct = M->log_tab[k];
     double r = fma(m, ct.x, -1.0);
     double q = fma(r, -1.0 / 6.0, 0.2);
@@ -193,7 +213,7 @@ __device__ __forceinline__ double log2_sig32(double x, const MathLds* M) {
 // 2^(j/64) from the table; the power of two by ldexp.  Branch-free: y is
 // clamped to [-1100, 1100] first, where ldexp already saturates to +inf
 // (y >= 1024) or to 0 (y < -1075); a NaN y is passed through.
-__device__ __forceinline__ double exp2_tab(double y, const MathLds* M) {
+__host__ __device__ __forceinline__ double exp2_tab(double y, const MathLds* M) {
     const double yc = fmin(fmax(y, -1100.0), 1100.0);
     double N = rint(yc * 64.0);
     double f = fma(N, -1.0 / 64.0, yc);
@@ -211,16 +231,19 @@ __device__ __forceinline__ double exp2_tab(double y, const MathLds* M) {
     return (y != y) ? y : r;
 }
 
-// p^alpha for a float priority p >= 0 and alpha > 0 (double).  Branch-free:
-// the power is formed for every lane (from 1 where p is not positive and
-// finite) and the special cases are selected: 0 -> 0, +inf -> +inf,
-// negative or NaN -> NaN.
-__device__ __forceinline__ double pow_prio(float p, double alpha, const MathLds* M) {
-    const float inf = __int_as_float(0x7F800000);
+// p^alpha for a float priority p >= 0 and alpha > 0 (double), as
+// 2^(alpha log2 p).  The error of y = alpha log2 p (log2's and the
+// product's roundings, about 3.7e-16 |y|) becomes a relative error of
+// about 2.6e-16 (|y| + 1) in the power: below 3e-13 for every normal
+// result (|y| < 1075).  Branch-free: the power is formed for every lane
+// (from 1 where p is not positive and finite) and the special cases are
+// selected: 0 -> 0, +inf -> +inf, negative or NaN -> NaN.
+__host__ __device__ __forceinline__ double pow_prio(float p, double alpha, const MathLds* M) {
+    const float inf = float_of(0x7F800000u);
     const bool fin = p > 0.0f && p < inf;
     const double r = exp2_tab(alpha * log2_sig32((double)(fin ? p : 1.0f), M), M);
     const uint32_t sp_hi = (p == 0.0f) ? 0u : (p == inf) ? 0x7FF00000u : 0x7FF80000u;
-    const double sp = __hiloint2double((int)sp_hi, 0);
+    const double sp = double_of_hi(sp_hi, 0u);
     return fin ? r : sp;
 }
 
@@ -232,24 +255,30 @@ __device__ __forceinline__ double pow_prio(float p, double alpha, const MathLds*
 // with the first two factors from the tables and (1 + r)^alpha from the
 // binomial series to r^7 (truncation below 7e-16 relative for alpha <= 16).
 // Tables, formed once per workgroup with pow_prio's own log2 / exp2:
-// gk[k] = (c_k, c_k^(-alpha)), ex[e + 149] = 2^(alpha e) (alpha e split
-// exactly into a rounded part and its remainder).  About 10 fp64 operations
-// per element instead of ~27, and no rounding of alpha log2(p) (the main
-// error of pow_prio, up to ~1e-14 relative): ~5e-16 relative.
+// gk[k] = (c_k, c_k^(-alpha)), ex[e + 149] = (2^(alpha e - S_e), S_e) with
+// S_e the multiple of 64 below alpha e (alpha e split exactly into a rounded
+// part and its remainder), so that the table entry lies in [1, 2^64) and the
+// product never overflows or loses bits below DBL_MIN before the final
+// ldexp by 2^S_e, which rounds once where the result is subnormal and gives
+// +inf where it overflows.  Wherever the result is a normal double the
+// scaling is exact.  About 11 fp64 operations per element instead of ~27,
+// and no rounding of alpha log2(p) (the main error of pow_prio): within
+// 3e-15 relative for normal results, the rounding of alpha (-log2 c_k) in
+// the table (|alpha log2 c_k| <= 16) being the largest part.
 constexpr double kFastPowMaxAlpha = 16.0;
 constexpr int kPowExpMin = -149;
 constexpr int kPowExpCount = 277;                 // e in [-149, 127]
 
 struct PowLds {
     double2 gk[128];
-    double ex[kPowExpCount];
+    double2 ex[kPowExpCount];                     // (2^(alpha e - S_e), S_e as int bits)
 };
 
 struct PowCoef {
     double b[8];                                  // b[i] = binomial(alpha, i), i = 1..7
 };
 
-__device__ __forceinline__ PowCoef pow_coef(double alpha) {
+__host__ __device__ __forceinline__ PowCoef pow_coef(double alpha) {
     PowCoef c;
     c.b[0] = 1.0;
     c.b[1] = alpha;
@@ -261,32 +290,36 @@ __device__ __forceinline__ PowCoef pow_coef(double alpha) {
 
 // Every thread of the workgroup takes part; M must be filled and visible.
 // A barrier must follow before the tables are read.
-__device__ __forceinline__ void pow_tables_build(PowLds* P, const MathLds* M, double alpha,
+__host__ __device__ __forceinline__ void pow_tables_build(PowLds* P, const MathLds* M, double alpha,
                                                  int tid, int nthreads) {
     for (int i = tid; i < 128 + kPowExpCount; i += nthreads) {
         if (i < 128) {
             const double2 ct = M->log_tab[i];           // (c_k, -log2 c_k)
-            P->gk[i] = make_double2(ct.x, exp2_tab(alpha * ct.y, M));
+            P->gk[i] = dpair(ct.x, exp2_tab(alpha * ct.y, M));
         } else {
             const double e = (double)(i - 128 + kPowExpMin);
             const double hi = alpha * e;
             const double lo = fma(alpha, e, -hi);         // alpha e = hi + lo exactly
-            const double E = exp2_tab(hi, M);
-            P->ex[i - 128] = fma(E, lo * kLn2, E);        // 2^lo = 1 + lo ln2 (|lo| <= 2^-41)
+            const double S = 64.0 * floor(hi * (1.0 / 64.0));
+            const double E = exp2_tab(hi - S, M);         // hi - S in [0, 64), exact
+            P->ex[i - 128] = dpair(fma(E, lo * kLn2, E),  // 2^lo = 1 + lo ln2 (|lo| <= 2^-41)
+                                   double_of((uint64_t)(uint32_t)(int)S));
         }
     }
 }
 
-__device__ __forceinline__ double pow_prio_fast(float p, const PowLds* P, const PowCoef& c) {
-    const float inf = __int_as_float(0x7F800000);
+__host__ __device__ __forceinline__ double pow_prio_fast(float p, const PowLds* P,
+                                                        const PowCoef& c) {
+    const float inf = float_of(0x7F800000u);
     const bool fin = p > 0.0f && p < inf;
     const double d = (double)(fin ? p : 1.0f);
-    const uint32_t hi = (uint32_t)__double2hiint(d);
+    const uint64_t db = bits_of(d);
+    const uint32_t hi = (uint32_t)(db >> 32);
     const int e = (int)(hi >> 20) - 1023;
     const int k = (int)(hi >> 13) & 127;
-    const double m = __hiloint2double((int)((hi & 0x000FFFFFu) | 0x3FF00000u), __double2loint(d));
+    const double m = double_of_hi((hi & 0x000FFFFFu) | 0x3FF00000u, (uint32_t)db);
     const double2 g = P->gk[k];
-    const double E = P->ex[e - kPowExpMin];
+    const double2 Es = P->ex[e - kPowExpMin];
     const double r = fma(m, g.x, -1.0);
     double s = fma(c.b[7], r, c.b[6]);
     s = fma(s, r, c.b[5]);
@@ -295,15 +328,15 @@ __device__ __forceinline__ double pow_prio_fast(float p, const PowLds* P, const 
     s = fma(s, r, c.b[2]);
     s = fma(s, r, c.b[1]);
     const double t = r * s;                              // (1 + r)^alpha - 1
-    const double ge = g.y * E;
-    const double w = fma(ge, t, ge);
+    const double ge = g.y * Es.x;                        // in [1, 2^80)
+    const double w = ldexp(fma(ge, t, ge), (int)(uint32_t)bits_of(Es.y));
     const uint32_t sp_hi = (p == 0.0f) ? 0u : (p == inf) ? 0x7FF00000u : 0x7FF80000u;
-    const double sp = __hiloint2double((int)sp_hi, 0);
+    const double sp = double_of_hi(sp_hi, 0u);
     return fin ? w : sp;
 }
 
 // e^x for a finite double x (the particle weights).
-__device__ __forceinline__ double exp_d(double x, const MathLds* M) {
+__host__ __device__ __forceinline__ double exp_d(double x, const MathLds* M) {
     return exp2_tab(x * kLog2e, M);
 }
 

@@ -69,14 +69,15 @@ __device__ __forceinline__ int res_count_le(double x, float ub, float Pf, float 
     return k - (over ? 1 : 0) + (under ? 1 : 0);
 }
 
-// exp(x) for x <= 0 in double, to about 1e-13 relative (the weights need
-// about 1e-9 for the ancestors to follow an exact-arithmetic reading):
+// exp(x) for x <= 0 in double, within 2e-13 relative where the result is
+// a normal double (the weights need about 1e-9 for the ancestors to follow
+// an exact-arithmetic reading):
 // x = N ln2/256 + g with |g| <= ln2/512, exp(x) = 2^(N/256) e^g, 2^(j/256)
 // from a 256-entry table (correctly rounded), e^g from its cubic Taylor
 // polynomial (truncation below 1.4e-13 relative); ln2/256 rounded to double
 // adds at most |N| 2^-61 to g.  x below the double range gives 0 (the
 // conversion saturates and ldexp underflows); a NaN passes through.
-__device__ __forceinline__ double exp_row(double x, const double* __restrict__ tab) {
+__host__ __device__ __forceinline__ double exp_row(double x, const double* __restrict__ tab) {
     const double N = rint(x * 0x1.71547652b82fep+8);          // 256 / ln 2
     const double g = fma(N, -0x1.62e42fefa39efp-9, x);        // ln 2 / 256
     const int Ni = (int)N;
@@ -87,8 +88,8 @@ __device__ __forceinline__ double exp_row(double x, const double* __restrict__ t
 
 // The table of exp_row, one entry per thread of a 256-thread block: each
 // thread loads its entry with its first loads and stores it to LDS later.
-__device__ __forceinline__ double exp_row_tab_load(int tid) {
-    return __longlong_as_double((long long)kExp2Tab256[tid & 255]);
+__host__ __device__ __forceinline__ double exp_row_tab_load(int tid) {
+    return double_of(kExp2Tab256[tid & 255]);
 }
 
 template <int R>

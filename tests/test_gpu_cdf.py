@@ -136,6 +136,46 @@ def test_scan_pow_extremes_large_tiles(ps, alpha, n):
         assert np.array_equal(host(cdf_r), C_g)
 
 
+@pytest.mark.parametrize("alpha", [12.5, 15.97, 16.0])
+def test_scan_pow_table_range_ends(ps, alpha):
+    """The table pow of 8-row tiles at both ends of the double range.  (1)
+    One weight at a time from 0.95 DBL_MAX to just below it, 200 priorities
+    (its factor 2^(alpha e) times c_k^(-alpha) alone may pass DBL_MAX while
+    the weight does not): the CDF's last value, that weight, within 1e-12
+    of the oracle's and never NaN.  (2) 64 weights just above DBL_MIN (where
+    2^(alpha e) alone is subnormal): the CDF within 1e-12 of the oracle's.
+    (3) A weight that overflows: 0 before it, +inf from it on, no NaN."""
+    n = (1 << 20) + 4096 + 3
+    buf = torch.zeros(n, dtype=torch.float32, device="cuda")
+    cand = np.exp2((1024.0 + np.log2(np.linspace(0.95, 0.9999, 200))) / alpha).astype(np.float32)
+    w_o = oracle.weights(cand, alpha)
+    assert np.all(np.isfinite(w_o))
+    got = np.empty(cand.size)
+    for i, pv in enumerate(cand):
+        buf[123] = float(pv)
+        got[i] = host(ps.build_cdf(buf, alpha)[0][-1:])[0]
+    assert not np.any(np.isnan(got))
+    e_rel = float(np.max(np.abs(got - w_o) / w_o))
+    say(f"alpha={alpha}: weights near DBL_MAX, max rel err {e_rel:.3e}")
+    assert e_rel <= 1e-12
+    # weights just above DBL_MIN
+    q = np.zeros(n, np.float32)
+    q[200000:200064] = (np.float32(np.exp2(-1021.5 / alpha))
+                        * np.float32(1.0 + np.arange(64) / 128.0))
+    C_o, _ = oracle.build_cdf(q, alpha)
+    C_g = host(ps.build_cdf(dev(q), alpha)[0])
+    pos = C_o > 0
+    assert C_o[200000] >= 2.2250738585072014e-308
+    assert np.all(C_g[~pos] == 0)
+    assert float(np.max(np.abs(C_g[pos] - C_o[pos]) / C_o[pos])) <= 1e-12
+    # an overflowing weight
+    q[:] = 0
+    q[77] = np.float32(np.exp2(1025.0 / alpha))
+    q[5000] = 1.0
+    C_g = host(ps.build_cdf(dev(q), alpha)[0])
+    assert np.all(C_g[:77] == 0) and np.all(np.isposinf(C_g[77:]))
+
+
 # Large-tile sizes (8192-element tiles) past what one round of workgroups
 # covers on 256 CUs: a one-element tail, whole tiles only, a ragged tail,
 # several rounds.
