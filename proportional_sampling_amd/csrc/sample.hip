@@ -87,14 +87,21 @@ struct StratCountFp {
     int64_t k;
     double T, kT, inv_k;
     bool pow2;
-    __device__ __forceinline__ double thr(int64_t i) const {
-        const double a = (double)(int32_t)i + (double)U[i];     // i < k <= 2^31 - 1
+    using Raw = float;
+    __device__ __forceinline__ float raw(int64_t i) const { return U[i]; }
+    __device__ __forceinline__ double thr_raw(int64_t i, float u) const {
+        const double a = (double)(int32_t)i + (double)u;        // i < k <= 2^31 - 1
         const double b = pow2 ? a * inv_k : a / (double)k;
         return b * T;
     }
+    __device__ __forceinline__ double thr(int64_t i) const { return thr_raw(i, U[i]); }
     __device__ __forceinline__ int64_t estimate(double x) const {
         const double e = floor(x * kT);
         return !(e > 0.0) ? 0 : (e >= (double)k ? k : (int64_t)e);
+    }
+    __device__ __forceinline__ uint32_t estimate32(double x) const {   // the same, k < 2^31
+        const double e = floor(x * kT);
+        return !(e > 0.0) ? 0u : (e >= (double)k ? (uint32_t)k : (uint32_t)(int32_t)e);
     }
 };
 
@@ -105,12 +112,19 @@ struct StratCountInt {
     uint64_t T;
     double kT;
     int k_log2;
-    __device__ __forceinline__ uint64_t thr(int64_t i) const {
-        return int_threshold((uint64_t)i, r[i], (uint64_t)k, T, 1, k_log2);
+    using Raw = uint32_t;
+    __device__ __forceinline__ uint32_t raw(int64_t i) const { return r[i]; }
+    __device__ __forceinline__ uint64_t thr_raw(int64_t i, uint32_t u) const {
+        return int_threshold((uint64_t)i, u, (uint64_t)k, T, 1, k_log2);
     }
+    __device__ __forceinline__ uint64_t thr(int64_t i) const { return thr_raw(i, r[i]); }
     __device__ __forceinline__ int64_t estimate(uint64_t x) const {
         const double e = floor((double)x * kT);
         return !(e > 0.0) ? 0 : (e >= (double)k ? k : (int64_t)e);
+    }
+    __device__ __forceinline__ uint32_t estimate32(uint64_t x) const {
+        const double e = floor((double)x * kT);
+        return !(e > 0.0) ? 0u : (e >= (double)k ? (uint32_t)k : (uint32_t)(int32_t)e);
     }
 };
 
@@ -162,70 +176,104 @@ __device__ __forceinline__ void load_elems(const CdfT* __restrict__ cdf, int64_t
 
 // VEC: the CDF is 16-byte aligned and n % PER == 0.  Each thread takes PER
 // consecutive elements (4 up to 2^20 elements, where more threads hide
-// more latency; 8 above, where fewer thresholds per element pay).  The thresholds that can fall among its values lie
+// more latency; 8 above, where fewer thresholds per element pay).  The
+// draws it owns are those with x_before < t_i <= x_last (element 0 also
+// owns every t_i <= C_0, element n-1 every t_i above C_{n-1}), and they lie
 // in a short window [estimate(x_before) - 1, estimate(x_last) + 1]: the
-// thread forms them once (checking that the one below the window is at or
-// below its smallest value and the one above it beyond its largest), and
-// each element's count is the window's start plus the window thresholds at
-// or below its value -- a few thresholds per thread instead of a few per
-// element.  A window wider than kStratWin (many draws on these elements)
-// or a failed check falls back to strat_count per element.
+// thread forms the window's thresholds once (checking that the one below
+// the window is at or below x_before and the one above it beyond x_last).
+// Each owned draw's index is then the thread's first element plus the
+// number of its values below the threshold -- the first element at or
+// above it, as the search would find -- with no per-element loop: the
+// wave's widest window bounds the loop over the window's draws (mostly 2
+// or 3 slots), kStratWin thresholds at a time (a heavy element's many
+// draws take more rounds).  A failed check or a last thread whose draws
+// reach past the window falls back to strat_count per element.
 template <int PER, bool VEC, class CdfT, class V, class Cnt>
 __device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_t n, const Cnt& F,
                                             int32_t* __restrict__ out) {
     const int64_t e0 = ((int64_t)blockIdx.x * kStratThreads + threadIdx.x) * PER;
     if (e0 >= n) return;
     V x[PER];
-    load_elems<PER, VEC, CdfT, V>(cdf, e0, n, x);
-    const int nv = (int)min_<int64_t>(PER, n - e0);   // valid elements of this thread
+    load_elems<PER, VEC, CdfT, V>(cdf, e0, n, x);        // past the end: C_{n-1}
+    // valid elements of this thread (VEC: n % PER == 0, so all of them)
+    const int nv = VEC ? PER : (int)min_<int64_t>(PER, n - e0);
     const bool first = e0 == 0;
+    const bool last = e0 + nv == n;
     const V xp = first ? V(0) : (V)cdf[e0 - 1];
-    V xl = x[0];
+    V xl = x[PER - 1];
+    if constexpr (!VEC) {
+        xl = x[0];
 #pragma unroll
-    for (int j = 1; j < PER; ++j) xl = j < nv ? x[j] : xl;
-    const int64_t kk = F.k;
-    const int64_t ca = first ? 0 : F.estimate(xp);
-    const int64_t cb = F.estimate(xl);
-    const int64_t wlo = ca > 0 ? ca - 1 : 0;
-    const int64_t whi = cb + 1 < kk ? cb + 1 : kk - 1;
-    bool win = whi - wlo + 1 <= kStratWin;
-    V t[kStratWin];
-    if (win) {
-#pragma unroll
-        for (int w = 0; w < kStratWin; ++w) t[w] = wlo + w <= whi ? F.thr(wlo + w) : V(0);
-        if (!first && wlo > 0 && !(F.thr(wlo - 1) <= xp)) win = false;
-        if (whi + 1 < kk && !(F.thr(whi + 1) > xl)) win = false;
+        for (int j = 1; j < PER; ++j) xl = j < nv ? x[j] : xl;
     }
+    // window arithmetic in 32 bits (k <= 2^31 - 1, so every index below
+    // k + kStratWin + 1 fits an unsigned 32-bit word)
+    const uint32_t kk = (uint32_t)F.k;
+    const uint32_t ca = first ? 0u : F.estimate32(xp);
+    const uint32_t cb = F.estimate32(xl);
+    const uint32_t wlo = ca > 0 ? ca - 1 : 0u;
+    const uint32_t whi = cb + 1 < kk ? cb + 1 : kk - 1;
+    const int span = (int)(whi - wlo);              // < 0 only where the CDF decreases
+    // the first kStratWin thresholds of the window and the two checks: every
+    // fraction load unconditional (index clamped below k), so that all are
+    // in flight at once (a load under a branch is waited for inside it); a
+    // threshold past the window is formed but never used
+    using Raw = typename Cnt::Raw;
+    auto at = [&](uint32_t i) { return (int64_t)(i < kk ? i : kk - 1); };
+    Raw u[kStratWin];
+#pragma unroll
+    for (int w = 0; w < kStratWin; ++w) u[w] = F.raw(at(wlo + w));
+    const Raw ulo = F.raw(at(wlo - 1));                 // (wlo = 0: unused)
+    const Raw uhi = F.raw(at(whi + 1));
+    V t[kStratWin];
+#pragma unroll
+    for (int w = 0; w < kStratWin; ++w) t[w] = F.thr_raw(wlo + w, u[w]);
+    bool win = !(last && whi + 1 < kk);
+    if (!first && wlo > 0 && !(F.thr_raw(wlo - 1, ulo) <= xp)) win = false;
+    if (whi + 1 < kk && !(F.thr_raw(whi + 1, uhi) > xl)) win = false;
+    // the widest window of the wave bounds the loop for every lane
+    int smax = win ? span : -1;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) smax = max_(smax, __shfl_xor(smax, m));
+    smax = __builtin_amdgcn_readfirstlane(smax);
+    const int32_t eb = (int32_t)e0;
+    for (int b = 0; b <= smax; b += kStratWin) {          // (uniform in the wave)
+        if (b > 0) {
+#pragma unroll
+            for (int w = 0; w < kStratWin; ++w) u[w] = F.raw(at(wlo + b + w));
+#pragma unroll
+            for (int w = 0; w < kStratWin; ++w) t[w] = F.thr_raw(wlo + b + w, u[w]);
+        }
+#pragma unroll
+        for (int w = 0; w < kStratWin; ++w) {
+            if (b + w > smax) break;
+            const V tw = t[w];
+            const bool own = win && b + w <= span && (first || tw > xp) && (last || tw <= xl);
+            int p = 0;
+#pragma unroll
+            for (int j = 0; j < PER; ++j) p += x[j] < tw ? 1 : 0;
+            p = p < nv ? p : nv - 1;                          // past C_{n-1}: the clamp
+            if (own) out[wlo + (uint32_t)(b + w)] = eb + p;
+        }
+    }
+    if (win) return;
+    const int64_t k64 = F.k;
     // (a value outside [x_before, x_last] -- only in a CDF that decreases
     // somewhere -- is counted as the nearest end, so that neighbouring
     // threads agree on the count at their shared boundary and every draw is
     // written once more than zero times)
-    const int64_t span = whi - wlo;
-    // the widest window of the wave bounds the count loop for every lane
-    // (mostly 2 or 3 of the 8 slots: 2^20 draws over 2^24 uniform
-    // priorities 43.7 -> 39.2 us, LogNormal 49.7 -> 48.3 us)
-    int smax = win ? (int)span : 0;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) smax = max_(smax, __shfl_xor(smax, m));
-    smax = __builtin_amdgcn_readfirstlane(smax);
     auto count = [&](V v) -> int64_t {
-        if (!win) return strat_count(F, v);
         v = v > xl ? xl : v;
         if (!first) v = v < xp ? xp : v;
-        int64_t c = wlo;
-#pragma unroll
-        for (int w = 0; w < kStratWin; ++w) {
-            if (w > smax) break;                          // (uniform in the wave)
-            c += (w <= span && t[w] <= v) ? 1 : 0;
-        }
-        return c;
+        return strat_count(F, v);
     };
     int64_t lo = first ? 0 : count(xp);
 #pragma unroll
     for (int j = 0; j < PER; ++j) {
         if (j < nv) {
             const int64_t e = e0 + j;
-            int64_t hi = e == n - 1 ? kk : count(x[j]);
+            int64_t hi = e == n - 1 ? k64 : count(x[j]);
             hi = hi > lo ? hi : lo;
             for (int64_t i = lo; i < hi; ++i) out[i] = (int32_t)e;
             lo = hi;
@@ -281,9 +329,13 @@ static psamp_status launch_strat(const void* cdf, psamp_dtype cdf_t, int64_t n, 
 
 // Stratified draws from the CDF's side when they are not too sparse in it
 // (each CDF line read once, against k searches of log2 n dependent loads,
-// the lower levels of which touch about three lines per draw).  Measured:
-// B = 262144 with 8192 draws 7.1 -> 4.9 us; 2^24 with 2^20 draws 55 -> 50 us
-// and 314 -> 145 MB of HBM traffic.  For sparse draws the searches read less.
+// the lower levels of which touch about three lines per draw).  Measured
+// against the searches: B = 262144 with 8192 draws 7.1 -> 4.9 us; 2^24
+// with 2^20 draws 55 -> 50 us and 314 -> 145 MB of HBM traffic; placing
+// the window's draws directly (no per-element count loop) and issuing its
+// fraction loads together then took 2^24 / 2^20 LogNormal priorities from
+// 48.7 to 28.3 us back to back (604 -> 269 VALU instructions per wave).
+// For sparse draws the searches read less.
 inline bool strat_from_cdf(int64_t n, int64_t k) {
     return 64 * k >= n;
 }
