@@ -126,8 +126,13 @@ psamp_status psamp_sample(const void* cdf, psamp_dtype cdf_t, int64_t n,
  * [PR615] "1. Parallel build_cdf" with [PF] searchsorted.
  *   Arguments as psamp_build_cdf and psamp_sample; ws as psamp_build_cdf
  *   (the same workspace may serve both).  cdf_t PSAMP_F64 or PSAMP_U64 is
- *   fused; PSAMP_F32 (whose rounding breaks the tiles' ownership of the
- *   thresholds) and k = 0 run the two calls.
+ *   fused up to n = 2^20 and, above, when the draws are sparse (64 k < n);
+ *   above 2^20 with dense draws the call runs the two kernels of the two
+ *   calls (the scan, then the sampler that reads the CDF once from its
+ *   side), which is faster there than drawing inside the scan's tiles.
+ *   PSAMP_F32 (whose rounding breaks the tiles' ownership of the
+ *   thresholds) and k = 0 also run the two calls.  The results are the
+ *   same bits on every path.
  * Errors: those of psamp_build_cdf and psamp_sample.
  * ---------------------------------------------------------------------- */
 psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_t n,

@@ -670,9 +670,16 @@ extern "C" psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype pri
     if (!aligned(prio, 4) || !aligned(cdf, osz) || !aligned(total, osz) || !aligned(ws, 8) ||
         (k > 0 && (!aligned(u, 4) || !aligned(out_idx, 4))))
         return PSAMP_E_ALIGN;
-    if (k == 0 || cdf_t == PSAMP_F32) {
-        // nothing to draw, or a float CDF (whose rounding breaks the tiles'
-        // ownership of the thresholds): the two calls, same results
+    // The two calls (same results) when there is nothing to draw, for a
+    // float CDF (whose rounding breaks the tiles' ownership of the
+    // thresholds), and for large tiles with dense draws: there the one
+    // kernel's draw phase (a search per draw in the tile's LDS copy, behind
+    // a search for the tile's first draw) lengthens every tile's life at two
+    // workgroups per CU by more than the CDF-side sampler takes to re-read
+    // the CDF -- measured 100.1 us against 82.9 us for 2^20 draws over 2^24
+    // LogNormal priorities, while up to 2^20 priorities the one kernel is
+    // 1-3 us faster.
+    if (k == 0 || cdf_t == PSAMP_F32 || (scan_rows_for(n) != 1 && 64 * k >= n)) {
         psamp_status s = psamp_build_cdf(prio, prio_t, n, alpha, cdf, cdf_t, total, ws, ws_bytes,
                                          stream);
         if (s != PSAMP_OK || k == 0) return s;
