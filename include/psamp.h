@@ -433,7 +433,9 @@ psamp_status psamp_ceiling_copy(const float* in, double* out, int64_t n, int row
  *                          (float priorities of build_cdf, build_cdf_sample,
  *                          per_round, segtree_build/update, scatter_lww,
  *                          replay insert/update)
- *   PSAMP_CHECK_ZERO_TOTAL the total of the weights is not > 0 (build_cdf,
+ *   PSAMP_CHECK_ZERO_TOTAL the total of the weights is not a positive finite
+ *                          number: all weights 0, or a weight or the sum
+ *                          past the range of the CDF's type (build_cdf,
  *                          build_cdf_sample, per_round, sample, after
  *                          segtree_build)
  *   PSAMP_CHECK_FRACTION   a float threshold fraction U_i or u_row outside

@@ -1,6 +1,6 @@
 // check.hip -- optional device-side checks of the preconditions the library
 // cannot check on the host without a sync: priorities finite and >= 0 with
-// at least one > 0, threshold fractions in [0, 1), indices in range,
+// a positive, finite total, threshold fractions in [0, 1), indices in range,
 // log-weights that are not NaN or +inf.  [SEGT] "Operations -- Update" has
 // every update thread work on its own index, independently of the others,
 // and [PR615] "1. Parallel build_cdf" keeps the CDF rebuild free of
@@ -13,6 +13,7 @@
 // bit in a per-device word (`check_bits`, a file-scope device variable);
 // psamp_check_errors copies it to the host (syncing the stream) and can
 // clear it.  The checks never change an output.
+#include <float.h>
 #include <stdlib.h>
 
 #include <atomic>
@@ -64,9 +65,15 @@ __global__ __launch_bounds__(kCheckThreads) void k_check_i32(const int32_t* __re
 // The total of a CDF or the root of a sum tree: > 0 (and not NaN).
 __global__ void k_check_total(const void* __restrict__ t, int kind, uint64_t bit) {
     bool bad;
-    if (kind == PSAMP_F64) bad = !(*(const double*)t > 0.0);
-    else if (kind == PSAMP_F32) bad = !(*(const float*)t > 0.0f);
-    else bad = *(const uint64_t*)t == 0;
+    if (kind == PSAMP_F64) {
+        const double x = *(const double*)t;
+        bad = !(x > 0.0 && x <= DBL_MAX);                 // zero, NaN or overflowed
+    } else if (kind == PSAMP_F32) {
+        const float x = *(const float*)t;
+        bad = !(x > 0.0f && x <= FLT_MAX);
+    } else {
+        bad = *(const uint64_t*)t == 0;
+    }
     check_flag(bad && threadIdx.x == 0, bit);
 }
 

@@ -58,6 +58,22 @@ def test_valid_inputs_set_no_bit(ps):
     assert ps.check_errors() == 0
 
 
+def test_overflowing_total(ps):
+    """Finite priorities whose weights pass the double range (p^alpha of
+    3e38 at alpha 17): the total is +inf, flagged as not a positive finite
+    total; a total just below DBL_MAX is not flagged."""
+    p = si.generic_f32(5000, 4, "exp")
+    p[100] = np.float32(3e38)
+    ps.check_errors(clear=True)
+    ps.build_cdf(dev(p), 17.0)
+    assert ps.check_errors() == ps.CHECK_ZERO_TOTAL
+    q = np.zeros(5000, np.float32)
+    q[100] = np.float32(np.exp2(1023.5 / 16.0))        # p^16 about 0.7 DBL_MAX
+    ps.check_errors(clear=True)
+    ps.build_cdf(dev(q), 16.0)
+    assert ps.check_errors() == 0
+
+
 @pytest.mark.parametrize("case", ["nan", "neg", "inf", "zeros"])
 def test_bad_priorities(ps, case):
     p = si.generic_f32(5000, 4, "exp")
