@@ -79,6 +79,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample_int(
 // still written with some value in [0, n).)
 constexpr int kStratThreads = 256;
 constexpr int kStratWin = 8;       // thresholds a thread tests directly
+constexpr int kStratHeavy = 32;    // a window this wide is placed by the whole wave
 
 // F(x) for fp thresholds t_i = ((i + U_i) / k) * T (double; for a
 // power-of-two k the division is a multiplication by 1/k, the same bits).
@@ -186,21 +187,28 @@ __device__ __forceinline__ void load_elems(const CdfT* __restrict__ cdf, int64_t
 // number of its values below the threshold -- the first element at or
 // above it, as the search would find -- with no per-element loop: the
 // wave's widest window bounds the loop over the window's draws (mostly 2
-// or 3 slots), kStratWin thresholds at a time (a heavy element's many
-// draws take more rounds).  A failed check or a last thread whose draws
-// reach past the window falls back to strat_count per element.
+// or 3 slots), kStratWin thresholds at a time.  A window of kStratHeavy
+// draws or more (heavy elements), a failed check or a last thread whose
+// draws reach past the window is handed to the whole wave: it counts the
+// thresholds at the thread's boundaries (strat_count, on up to PER + 1
+// lanes at once) and 64 lanes write each element's range together -- one
+// element holding half the mass of 2^24 priorities took 92 ms for 2^20
+// draws on its one lane, and the old per-element loops were as serial.
 template <int PER, bool VEC, class CdfT, class V, class Cnt>
 __device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_t n, const Cnt& F,
                                             int32_t* __restrict__ out) {
+    const int lane = (int)(threadIdx.x & (kWave - 1));
     const int64_t e0 = ((int64_t)blockIdx.x * kStratThreads + threadIdx.x) * PER;
-    if (e0 >= n) return;
+    // (a thread past the end stays in the wave, idle: the wave fills
+    // heavy ranges together below)
+    const bool valid = e0 < n;
     V x[PER];
-    load_elems<PER, VEC, CdfT, V>(cdf, e0, n, x);        // past the end: C_{n-1}
+    load_elems<PER, VEC, CdfT, V>(cdf, valid ? e0 : 0, n, x);   // past the end: C_{n-1}
     // valid elements of this thread (VEC: n % PER == 0, so all of them)
-    const int nv = VEC ? PER : (int)min_<int64_t>(PER, n - e0);
+    const int nv = !valid ? 0 : (VEC ? PER : (int)min_<int64_t>(PER, n - e0));
     const bool first = e0 == 0;
-    const bool last = e0 + nv == n;
-    const V xp = first ? V(0) : (V)cdf[e0 - 1];
+    const bool last = valid && e0 + nv == n;
+    const V xp = (first || !valid) ? V(0) : (V)cdf[e0 - 1];
     V xl = x[PER - 1];
     if constexpr (!VEC) {
         xl = x[0];
@@ -229,11 +237,15 @@ __device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_
     V t[kStratWin];
 #pragma unroll
     for (int w = 0; w < kStratWin; ++w) t[w] = F.thr_raw(wlo + w, u[w]);
-    bool win = !(last && whi + 1 < kk);
+    bool win = valid && !(last && whi + 1 < kk);
     if (!first && wlo > 0 && !(F.thr_raw(wlo - 1, ulo) <= xp)) win = false;
     if (whi + 1 < kk && !(F.thr_raw(whi + 1, uhi) > xl)) win = false;
+    // a wide window (heavy elements) or a failed check: the wave places this
+    // thread's draws together, below
+    const bool coop = valid && (!win || span >= kStratHeavy);
+    const bool own_win = win && !coop;
     // the widest window of the wave bounds the loop for every lane
-    int smax = win ? span : -1;
+    int smax = own_win ? span : -1;
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) smax = max_(smax, __shfl_xor(smax, m));
     smax = __builtin_amdgcn_readfirstlane(smax);
@@ -249,7 +261,7 @@ __device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_
         for (int w = 0; w < kStratWin; ++w) {
             if (b + w > smax) break;
             const V tw = t[w];
-            const bool own = win && b + w <= span && (first || tw > xp) && (last || tw <= xl);
+            const bool own = own_win && b + w <= span && (first || tw > xp) && (last || tw <= xl);
             int p = 0;
 #pragma unroll
             for (int j = 0; j < PER; ++j) p += x[j] < tw ? 1 : 0;
@@ -257,25 +269,43 @@ __device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_
             if (own) out[wlo + (uint32_t)(b + w)] = eb + p;
         }
     }
-    if (win) return;
-    const int64_t k64 = F.k;
-    // (a value outside [x_before, x_last] -- only in a CDF that decreases
-    // somewhere -- is counted as the nearest end, so that neighbouring
-    // threads agree on the count at their shared boundary and every draw is
-    // written once more than zero times)
-    auto count = [&](V v) -> int64_t {
-        v = v > xl ? xl : v;
-        if (!first) v = v < xp ? xp : v;
-        return strat_count(F, v);
-    };
-    int64_t lo = first ? 0 : count(xp);
+    // The other threads, one at a time: lanes 0..nv of the wave count the
+    // thresholds at or below its boundaries (x_before, then each value;
+    // the last element of the array takes every draw), and the whole wave
+    // writes each element's range of draws.  (A value outside [x_before,
+    // x_last] -- only in a CDF that decreases somewhere -- is counted as the
+    // nearest end, so that neighbouring threads agree on the count at their
+    // shared boundary and every draw is written once more than zero times.)
+    uint64_t cm = __ballot(coop);
+    while (cm != 0) {                                     // (uniform in the wave)
+        const int h = __builtin_ctzll(cm);
+        cm &= cm - 1;
+        const int64_t he0 = (int64_t)__builtin_amdgcn_readlane((int)e0, h);
+        const int hnv = __builtin_amdgcn_readlane(nv, h);
+        const bool hfirst = he0 == 0;
+        const V hxp = readlane(xp, h);
+        const V hxl = readlane(xl, h);
+        V v = hxp;
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-        if (j < nv) {
-            const int64_t e = e0 + j;
-            int64_t hi = e == n - 1 ? k64 : count(x[j]);
+        for (int j = 1; j <= PER; ++j) {
+            const V xj = readlane(x[j - 1], h);
+            v = lane == j ? xj : v;
+        }
+        int64_t c = 0;
+        if (lane <= hnv) {
+            if (lane > 0 && he0 + lane - 1 == n - 1) {
+                c = F.k;
+            } else if (!(lane == 0 && hfirst)) {
+                v = v > hxl ? hxl : v;
+                if (!hfirst) v = v < hxp ? hxp : v;
+                c = strat_count(F, v);
+            }
+        }
+        int64_t lo = (int64_t)readlane((uint64_t)c, 0);
+        for (int j = 0; j < hnv; ++j) {
+            int64_t hi = (int64_t)readlane((uint64_t)c, j + 1);
             hi = hi > lo ? hi : lo;
-            for (int64_t i = lo; i < hi; ++i) out[i] = (int32_t)e;
+            for (int64_t i = lo + lane; i < hi; i += kWave) out[i] = (int32_t)(he0 + j);
             lo = hi;
         }
     }

@@ -347,6 +347,59 @@ def test_stratified_search_host_cdf(ps, n, k, dt, kind):
     assert np.array_equal(idx, expect)
 
 
+@pytest.mark.parametrize("case", ["one_half", "four_quarters", "all_on_one", "int_one_half"])
+def test_stratified_sample_heavy_elements(ps, case):
+    """Elements that receive a large share of the draws (one with half the
+    mass, four with a quarter each, one with all of it; 2^22 priorities,
+    2^18 draws): indices against the oracle under the excuse rule and
+    exactly the lower bounds on the GPU's own CDF; every call well inside a
+    bound that a single lane writing a heavy element's draws alone (tens of
+    milliseconds here) would break."""
+    import time
+    n, k = 1 << 22, 1 << 18
+    rng = np.random.default_rng(321)
+    if case == "int_one_half":
+        q = rng.integers(1, 1 << 10, n, dtype=np.uint32)
+        q[123457] = np.uint32(min(int(q.astype(np.int64).sum()), (1 << 32) - 1))
+        r = si.uniform_u32(rng, k)
+        Q, R = dev(q), dev(r)
+        cdf, tot = ps.build_cdf(Q)
+        idx = ps.sample(cdf, tot, R, stratified=True)
+        _, _, _, idx_o = oracle.sample_int(q, r, True)
+        assert np.array_equal(host(idx), idx_o)
+        calls = lambda: ps.sample(cdf, tot, R, stratified=True, out=idx)
+    else:
+        p = (rng.random(n, dtype=np.float32) + np.float32(0.01))
+        total = float(p.astype(np.float64).sum())
+        if case == "one_half":
+            p[123457] = np.float32(total)
+        elif case == "four_quarters":
+            p[[0, 1_000_003, 2_500_000, n - 1]] = np.float32(total / 4)
+        else:
+            p[:] = 0.0
+            p[777777] = 1.0
+        U = si.uniform_f32(rng, k)
+        P, Ud = dev(p), dev(U)
+        cdf, tot = ps.build_cdf(P, 1.0)
+        idx = ps.sample(cdf, tot, Ud, stratified=True)
+        C_o, T_o, t_o, idx_o = oracle.sample(p, 1.0, U, True)
+        assert_indices(host(idx), idx_o, t_o, C_o, T_o, f"heavy {case}")
+        C_g, T_g = host(cdf), float(host(tot)[0])
+        t_g = ((np.arange(k) + U.astype(np.float64)) / k) * T_g
+        assert np.array_equal(host(idx), np.minimum(np.searchsorted(C_g, t_g, side="left"), n - 1))
+        calls = lambda: ps.sample(cdf, tot, Ud, stratified=True, out=idx)
+    calls()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        calls()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    say(f"heavy {case}: {1e6 * min(times):.0f} us per call")
+    assert min(times) < 5e-3, times
+
+
 def test_stratified_search_int_host_cdf(ps):
     """Integer mode: exact thresholds from Python integers, host CDF."""
     for n, k in [(4097, 5000), (300007, 1 << 16), (17, 64), (1 << 20, 1 << 14)]:
