@@ -32,6 +32,25 @@
 
 namespace psamp {
 
+// The first b in [lo, n] with C[b] >= t (n if none) of a non-decreasing
+// array in LDS, every b < lo being known to lie below t.  A thread's later
+// draws land at or after its earlier ones, so it starts at its previous
+// result: one read when the draw lands on the same element again (an
+// element that takes many draws), a binary search over the rest otherwise.
+template <class Acc>
+__device__ __forceinline__ int lds_lower_bound_from(const Acc* C, int lo, int n, Acc t) {
+    if (lo < n && !(C[lo] < t)) return lo;
+    int b = lo + 1, len = n - lo - 1;
+    while (len > 1) {
+        const int half = len >> 1;
+        b = (C[b + half - 1] < t) ? b + half : b;
+        len -= half;
+    }
+    if (len == 1) b += (C[b] < t) ? 1 : 0;
+    return b > n ? n : b;
+}
+
+
 constexpr int kScanPark = 4;     // rows of an 8-row tile parked in LDS during the lookback
 
 template <class Out, class Acc>
@@ -281,27 +300,48 @@ __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SA
         const int64_t i_lo = s_range[0], i_hi = s_range[1];
         const Acc T = s_T;
         uint32_t mn = 0xFFFFFFFFu;
-        for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
-            Acc t;
-            if constexpr (kFp)
-                t = strat_threshold(i, ((const float*)sa.u)[i], sa.k, T);
-            else
-                t = int_threshold((uint64_t)i, ((const uint32_t*)sa.u)[i], (uint64_t)sa.k, T, 1,
-                                  sa.k_log2);
-            int b = 0, len = tlen;
-            while (len > 1) {
-                const int half = len >> 1;
-                b = (s_C[b + half - 1] < t) ? b + half : b;
-                len -= half;
+        // Four draws a round, their fractions (and then their drawn
+        // priorities) loaded together; each search starts at the thread's
+        // previous element, since its draws land in increasing order (one
+        // LDS read per draw when an element takes many).
+        int bp = 0;
+        for (int64_t i0 = i_lo + tid; i0 < i_hi; i0 += 4 * kScanThreads) {
+            uint32_t uq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = i0 + q * kScanThreads;
+                uq[q] = ((const uint32_t*)sa.u)[i < i_hi ? i : i0];
             }
-            b += (s_C[b] < t) ? 1 : 0;
-            if (b >= tlen) b = tlen - 1;
-            sa.out[i] = (int32_t)(base + b);
+            int bq[4] = {0, 0, 0, 0};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t i = i0 + q * kScanThreads;
+                if (i < i_hi) {
+                    Acc t;
+                    if constexpr (kFp)
+                        t = strat_threshold(i, __uint_as_float(uq[q]), sa.k, T);
+                    else
+                        t = int_threshold((uint64_t)i, uq[q], (uint64_t)sa.k, T, 1, sa.k_log2);
+                    int b = lds_lower_bound_from(s_C, bp, tlen, t);
+                    if (b >= tlen) b = tlen - 1;
+                    bp = b;
+                    bq[q] = b;
+                    sa.out[i] = (int32_t)(base + b);
+                }
+            }
             if constexpr (PER) {
-                // the drawn priority, as read before any rewrite of this tile
-                const uint32_t key = __float_as_uint(sa.prio[base + b]);
-                reinterpret_cast<uint32_t*>(sa.out_w)[i] = key;
-                mn = key < mn ? key : mn;
+                // the drawn priorities, as read before any rewrite of this tile
+                uint32_t kq[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) kq[q] = __float_as_uint(sa.prio[base + bq[q]]);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int64_t i = i0 + q * kScanThreads;
+                    if (i < i_hi) {
+                        reinterpret_cast<uint32_t*>(sa.out_w)[i] = kq[q];
+                        mn = kq[q] < mn ? kq[q] : mn;
+                    }
+                }
             }
         }
         if constexpr (PER) {
@@ -317,16 +357,32 @@ __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SA
             // rewrite: draw i is the last of its index unless draw i + 1 (in
             // this tile) lands on the same element -- the search's own test
             if (sa.newp != nullptr) {
-                for (int64_t i = i_lo + tid; i < i_hi; i += kScanThreads) {
-                    const int b = sa.out[i] - (int32_t)base;
-                    // (draw i + 1 lands on b or later; on the tile's last
-                    // element it can only land on b)
-                    bool last = i + 1 >= i_hi;
-                    if (!last && b < tlen - 1) {
-                        const Acc tn = strat_threshold(i + 1, ((const float*)sa.u)[i + 1], sa.k, T);
-                        last = s_C[b] < tn;
+                for (int64_t i0 = i_lo + tid; i0 < i_hi; i0 += 4 * kScanThreads) {
+                    int32_t bq[4];
+                    float un[4], nq[4];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {      // loads first, in range
+                        const int64_t i = i0 + q * kScanThreads;
+                        const int64_t ic = i < i_hi ? i : i0;
+                        bq[q] = sa.out[ic] - (int32_t)base;
+                        un[q] = ((const float*)sa.u)[ic + 1 < i_hi ? ic + 1 : ic];
+                        nq[q] = sa.newp[ic];
                     }
-                    if (last) sa.prio[base + b] = sa.newp[i];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int64_t i = i0 + q * kScanThreads;
+                        if (i < i_hi) {
+                            const int b = bq[q];
+                            // (draw i + 1 lands on b or later; on the tile's
+                            // last element it can only land on b)
+                            bool last = i + 1 >= i_hi;
+                            if (!last && b < tlen - 1) {
+                                const Acc tn = strat_threshold(i + 1, un[q], sa.k, T);
+                                last = s_C[b] < tn;
+                            }
+                            if (last) sa.prio[base + b] = nq[q];
+                        }
+                    }
                 }
             }
         }
