@@ -55,7 +55,7 @@ def parse():
                     help="launch every kernel from Python instead of replaying a HIP graph")
     ap.add_argument("--only", default="",
                     help="profiling helper: per_mid | scan:<n> | ceiling:<n> | copy:<MiB> | "
-                         "pf | per_large")
+                         "pf | per_large | rows | sample_large")
     return ap.parse_args()
 
 
@@ -630,6 +630,28 @@ def main():
         return
     if args.only == "per_large":
         log(json.dumps(per_large_bench(ps, torch)))
+        return
+    if args.only in ("rows", "sample_large"):
+        # five calls of one kernel (row resampling at 1024 x 4096, or the
+        # stratified sample of 2^20 draws over the PER-large CDF), nothing
+        # else timed: for counter runs
+        import synthetic_inputs as si
+        if args.only == "rows":
+            d = si.resample()
+            lw = torch.from_numpy(d["lw"]).cuda()
+            u = torch.from_numpy(d["u_row"]).cuda()
+            out = torch.empty_like(lw, dtype=torch.int32)
+            fn = lambda: ps.resample_rows(lw, u, out=out)
+        else:
+            d = si.per_large()
+            cdf, tot = ps.build_cdf(torch.from_numpy(d["p"]).cuda(), d["alpha"])
+            U = torch.from_numpy(d["U"]).cuda()
+            idx = torch.empty(U.numel(), dtype=torch.int32, device="cuda")
+            fn = lambda: ps.sample(cdf, tot, U, out=idx)
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        log(f"{args.only}: 5 calls")
         return
     if args.only.startswith("ceiling:"):
         n = int(args.only.split(":")[1])
