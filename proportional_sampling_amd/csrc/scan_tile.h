@@ -271,6 +271,20 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
     const int cnt = tile - g * kScanGroup;
     Acc base = Acc(0);     // this lane's published leaves h < g - 1, in slot order
     Acc P = Acc(0), Pn = Acc(0), Gp = Acc(0);
+    // The tile that ends a group publishes GT_g as soon as its own group's
+    // sums are visible.  Were it to wait for the older totals first (they
+    // share the first round), each total would wait for the one two groups
+    // earlier: a chain of one poll round trip per two groups that capped the
+    // whole scan's rate (tiles spent most of their life waiting on it).
+    if (!PRE && cnt == kScanGroup - 1) {
+        const uint32_t off1[1] = {a_off((uint32_t)(g * kScanGroup + lane), par)};
+        const bool need1[1] = {lane < cnt};
+        uint64_t w1[1];
+        wait_words<1>(ws, off1, need1, w1);
+        const Acc a = need1[0] ? status_value<Acc>(w1[0]) : Acc(0);
+        const Acc gt = wave_sum(lane == cnt ? A : a);
+        if (lane == 0) store_agent(&ws[gt_off((uint32_t)g, par)], status_enc(gt));
+    }
 #pragma nounroll
     for (int s0 = 0;; s0 += kLbGtWords) {
         const bool first = s0 == 0;
@@ -295,7 +309,7 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
             const Acc a = need[1] ? status_value<Acc>(w[1]) : Acc(0);
             P = wave_sum(a);
             Pn = wave_sum(lane == cnt ? A : a);
-            if (cnt == kScanGroup - 1 && lane == 0)
+            if (PRE && cnt == kScanGroup - 1 && lane == 0)
                 store_agent(&ws[gt_off((uint32_t)g, par)], status_enc(Pn));
             if (g > 0) Gp = wave_sum(need[0] ? status_value<Acc>(w[0]) : Acc(0));
         }
