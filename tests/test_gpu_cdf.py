@@ -781,6 +781,48 @@ def test_build_cdf_sample_per_large(ps):
     assert np.array_equal(host(idx_i), idx_o)
 
 
+@pytest.mark.parametrize("n,k", [((1 << 20) - 3, 1 << 18), ((1 << 22) + 5, 1 << 16),
+                                 (1 << 23, 1 << 20)])
+@pytest.mark.parametrize("case", ["one_half", "all_on_one", "int_one_half"])
+def test_build_cdf_sample_heavy_elements(ps, n, k, case):
+    """The fused call where one element takes a large share of the draws
+    (half the mass, or all of it), on both tilings: the bits of the two
+    calls, the oracle's integer indices, and a time bound that one lane
+    placing the heavy element's draws alone would break."""
+    import time
+    say(f"build_cdf_sample heavy {case} n={n} k={k}")
+    rng = np.random.default_rng(n + k)
+    if case == "int_one_half":
+        q = rng.integers(1, 1 << 10, n, dtype=np.uint32)
+        q[n // 3] = np.uint32(min(int(q.astype(np.int64).sum()), (1 << 32) - 1))
+        P, Ud, alpha = dev(q), dev(si.uniform_u32(rng, k)), 1.0
+    else:
+        p = rng.random(n, dtype=np.float32) + np.float32(0.01)
+        if case == "one_half":
+            p[n // 3] = np.float32(p.astype(np.float64).sum())
+        else:
+            p[:] = 0.0
+            p[n // 3] = 1.0
+        P, Ud, alpha = dev(p), dev(si.uniform_f32(rng, k)), 1.0
+    ws = ps.Workspace(ps.build_cdf_workspace_size(n))
+    idx, cdf, tot = ps.build_cdf_sample(P, Ud, alpha, ws=ws)
+    c_s, t_s = ps.build_cdf(P, alpha)
+    assert torch.equal(cdf, c_s) and torch.equal(tot, t_s)
+    assert torch.equal(idx, ps.sample(c_s, t_s, Ud, stratified=True))
+    if case == "int_one_half":
+        _, _, _, idx_o = oracle.sample_int(q, host(Ud), True)
+        assert np.array_equal(host(idx), idx_o)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        ps.build_cdf_sample(P, Ud, alpha, cdf=cdf, total=tot, out=idx, ws=ws)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    say(f"  {1e6 * min(times):.0f} us per call")
+    assert min(times) < 5e-3, times
+    assert ws.errors() == 0
+
+
 @pytest.mark.parametrize("mode", ["fp", "int"])
 def test_build_cdf_sample_mixed_calls_one_workspace(ps, mode):
     """The fused call and the plain scan alternate on one workspace at 2^24
