@@ -205,10 +205,12 @@ psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int64_t cap_pow
  * callers keep idx_j below n_valid.  0 <= m <= 2^31 - 1 (m = 0 is a no-op
  * and may pass NULL pointers); the batch is processed in order, in chunks
  * of 1024 entries, so later entries still win over earlier ones.  Each
- * chunk runs as 64 workgroups, one per subtree below the top 6 levels, and
- * the workgroup that finishes last recomputes those levels; it finds out it
- * is last through a counter in ws.
- * ws: psamp_segtree_update_workspace_size(cap_pow2, m) bytes (256), 4-byte
+ * chunk runs as 64 workgroups, one per subtree below the top 6 levels;
+ * each publishes its subtree's root in ws and workgroup 0 recomputes those
+ * levels from them (its wait is bounded, about a second: should other work
+ * keep the other workgroups from starting that long, the top levels are
+ * left wrong and ws is not left zero).
+ * ws: psamp_segtree_update_workspace_size(cap_pow2, m) bytes (512), 8-byte
  *   aligned, zero-filled once after allocation (every call leaves it zero
  *   again); one ws must not serve two updates that may run at the same time.
  * Errors: E_NULL, E_SIZE, E_DTYPE, E_PARAM, E_WORKSPACE, E_ALIGN, E_LAUNCH. */

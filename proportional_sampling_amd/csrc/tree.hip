@@ -26,10 +26,12 @@
 //      carried index, so in O(1)).
 // With up to 64 entries (the usual case) one wave does 2-5: a direct ranking
 // in registers, the levels with cross-lane reads; above, the whole
-// workgroup: a stable radix sort in LDS and the levels through LDS.  The
-// workgroup that finishes last (an atomic counter in the caller's
-// workspace, which that workgroup resets) recomputes the 63 nodes above the
-// subtree roots.  Every dirty node is written once per call, after both of
+// workgroup: a stable radix sort in LDS and the levels through LDS.  Each
+// workgroup publishes its subtree's root in the caller's workspace (value
+// and presence in one word), and workgroup 0 recomputes the 63 nodes above
+// the subtree roots once it has seen all of them.  (A counter that let the
+// last workgroup do it needed a release of every workgroup's stores and two
+// more round trips.)  Every dirty node is written once per call, after both of
 // its children are final, as fl(left + right) (the top levels are formed
 // again in full): the tree stays bit-equal to a fresh build.
 //
@@ -60,7 +62,8 @@ __device__ __forceinline__ uint32_t wave_incl_u32(uint32_t x) {
 }
 constexpr int kMaxDepth = 30;                    // cap <= 2^30
 constexpr int kUpdTopLevels = 6;                 // update: 2^6 subtree workgroups
-constexpr size_t kUpdWsBytes = 256;              // update: its counter (zeroed once)
+constexpr size_t kUpdWsBytes = 512;              // update: the subtree roots' words (zero between calls)
+constexpr int kRootSpin = 1 << 21;               // bounded wait for the roots (about a second)
 static_assert((1 << kUpdTopLevels) <= kWave, "the top levels are formed by one wave");
 constexpr int kSampleTreeThreads = 256;
 constexpr int kSampleTreeThreadsBig = 1024;      // large batches: fewer copies of the top levels
@@ -118,17 +121,24 @@ __global__ __launch_bounds__(kBuildThreads) void k_tree_build_pass(
     }
 }
 
-// Agent-scope (cross-XCD) loads and stores of one node, float or uint64.
-__device__ __forceinline__ void node_store_agent(float* p, float v) {
-    __hip_atomic_store(reinterpret_cast<uint32_t*>(p), __float_as_uint(v), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
+// The value of lane + s (lanes past the end get their own).
+__device__ __forceinline__ float shfl_down_v(float x, int s) { return __shfl_down(x, (unsigned)s); }
+__device__ __forceinline__ uint64_t shfl_down_v(uint64_t x, int s) {
+    const uint32_t lo = (uint32_t)__shfl_down((int)(uint32_t)x, (unsigned)s);
+    const uint32_t hi = (uint32_t)__shfl_down((int)(uint32_t)(x >> 32), (unsigned)s);
+    return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ void node_store_agent(uint64_t* p, uint64_t v) { store_agent(p, v); }
-__device__ __forceinline__ float node_load_agent(const float* p) {
-    return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t*>(p),
-                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+
+// A subtree root as published in the workspace: value and "present" in one
+// 64-bit word (0: not yet), so one agent-scope store carries both.  F32:
+// the float's bits with bit 32 set; U64: the value plus one (sums of 2^30
+// uint32 leaves stay below 2^62).
+__device__ __forceinline__ uint64_t root_enc(float v) {
+    return (uint64_t(1) << 32) | (uint64_t)__float_as_uint(v);
 }
-__device__ __forceinline__ uint64_t node_load_agent(const uint64_t* p) { return load_agent(p); }
+__device__ __forceinline__ uint64_t root_enc(uint64_t v) { return v + 1u; }
+__device__ __forceinline__ void root_dec(uint64_t w, float& v) { v = __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ void root_dec(uint64_t w, uint64_t& v) { v = w - 1u; }
 
 // A barrier of one wave: its lanes run in lockstep and its LDS accesses
 // complete in order; the wavefront-scope fences keep the compiler from
@@ -146,12 +156,12 @@ __device__ __forceinline__ void wave_sync() {
 // each dirty node (its owner) forms fl(left + right) from its own value, a
 // clean sibling from its registers, or the dirty sibling's value from LDS
 // (the next owner's, found through the carried index).  The subtree's root
-// is stored at agent scope: the workgroup that finishes last reads it.
+// also goes to *s_root, for the workgroup that forms the levels above.
 template <class V, class P>
-__device__ __forceinline__ void propagate(V* __restrict__ tree, int64_t cap, int Ds, int T, int u,
+__device__ __forceinline__ void propagate(V* __restrict__ tree, int64_t cap, int Ds, int u,
                                           const int32_t* wl, const int32_t* wj, const P* pbuf,
                                           V (*vbuf)[kUpdThreads], int32_t (*ebuf)[kUpdThreads],
-                                          double alpha, const MathLds* M) {
+                                          double alpha, const MathLds* M, V* s_root) {
     const int tid = threadIdx.x;
     const bool act = tid < u;
     int64_t L = 0, Lp = -1;
@@ -165,8 +175,8 @@ __device__ __forceinline__ void propagate(V* __restrict__ tree, int64_t cap, int
 #pragma unroll
         for (int d = 0; d < kMaxDepth; ++d)
             if (d < Ds) sib[d] = tree[((cap + L) >> d) ^ 1];
-        if (Ds == 0 && T > 0) node_store_agent(tree + cap + L, val);
-        else tree[cap + L] = val;
+        tree[cap + L] = val;
+        if (Ds == 0) *s_root = val;
         vbuf[0][tid] = val;
         ebuf[0][tid] = end;
     }
@@ -197,8 +207,8 @@ __device__ __forceinline__ void propagate(V* __restrict__ tree, int64_t cap, int
                 }
                 val = left + right;
                 end = ne;
-                if (d == Ds && T > 0) node_store_agent(tree + N, val);
-                else tree[N] = val;
+                tree[N] = val;
+                if (d == Ds) *s_root = val;
                 vbuf[bo][tid] = val;
                 ebuf[bo][tid] = end;
             }
@@ -210,14 +220,14 @@ __device__ __forceinline__ void propagate(V* __restrict__ tree, int64_t cap, int
 // One batch of up to 1024 updates.  Workgroup s of S = 2^T owns the subtree
 // below node S + s (the leaves whose top T of D bits are s): it keeps the
 // batch entries that fall there, resolves last-write-wins and recomputes
-// every dirty node of its subtree up to that node; the workgroup that
-// finishes last (a counter in the workspace, reset by that workgroup) then
-// recomputes the T levels above, from the S subtree roots.  No workgroup
+// every dirty node of its subtree up to that node and publishes the
+// subtree's root in the workspace; workgroup 0 then waits for all S roots
+// and recomputes the T levels above them (and zeroes the words again).  No workgroup
 // waits for another, so the grid need not be resident at once.
 template <class V, class P>
 __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
     V* __restrict__ tree, int64_t cap, int D, int T, const int32_t* __restrict__ idx,
-    const P* __restrict__ prio, int m, double alpha, uint32_t* __restrict__ counter) {
+    const P* __restrict__ prio, int m, double alpha, uint64_t* __restrict__ roots) {
     __shared__ uint64_t keys[kUpdThreads];
     __shared__ P pbuf[kUpdThreads];                      // the batch's values, by position
     __shared__ uint32_t hist[256 * kUpdWaves];           // (digit, wave) counts, then offsets
@@ -227,7 +237,8 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
     __shared__ int32_t wj[kUpdThreads];                  // their batch positions
     __shared__ V vbuf[2][kUpdThreads];
     __shared__ int32_t ebuf[2][kUpdThreads];
-    __shared__ uint32_t s_u, s_last;
+    __shared__ uint32_t s_u;
+    __shared__ V s_root;                                 // this subtree's root
     __shared__ uint64_t s_sk[kWave];                     // few entries: keys in order,
     __shared__ int32_t s_sp[kWave];                      //   their compact positions,
     __shared__ V s_lv[kWave];                            //   leaf values by position
@@ -241,6 +252,8 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
     const int Ds = D - T;                                // levels inside a subtree
     const int sub = (int)blockIdx.x;
     if (sizeof(P) == 4 && sizeof(V) == 4) math_lds_fill(&M, tid, kUpdThreads);
+    // the root as it stands (a subtree without entries publishes it as is)
+    if (T > 0 && tid == 0) s_root = tree[S + sub];
 
     // 1. this subtree's entries, keyed (leaf << 32) | batch position (an entry
     // outside [0, cap) belongs to no subtree); the batch's values by position
@@ -367,15 +380,15 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
                 if (act) sibl[(d - 1) * kWave + lane] = val;
             }
             if (act) {
-                if (Ds == 0 && T > 0) node_store_agent(tree + cap + L, leafv);
-                else tree[cap + L] = leafv;
+                tree[cap + L] = leafv;
+                if (Ds == 0) s_root = leafv;
 #pragma unroll 1
                 for (int d = 1; d <= Ds; ++d) {
                     if ((owned >> d) & 1u) {
                         const int64_t N = (cap + L) >> d;
                         const V x = sibl[(d - 1) * kWave + lane];
-                        if (d == Ds && T > 0) node_store_agent(tree + N, x);
-                        else tree[N] = x;
+                        tree[N] = x;
+                        if (d == Ds) s_root = x;
                     }
                 }
             }
@@ -449,32 +462,42 @@ __global__ __launch_bounds__(kUpdThreads) void k_tree_update(
         __syncthreads();
     }
     // 4, 5: the whole workgroup (the winners may be up to 1024)
-    propagate<V, P>(tree, cap, Ds, T, (int)s_u, wl, wj, pbuf, vbuf, ebuf, alpha, &M);
+    propagate<V, P>(tree, cap, Ds, (int)s_u, wl, wj, pbuf, vbuf, ebuf, alpha, &M, &s_root);
 
 done:
     if (T == 0) return;
-    // 6. the last workgroup to get here recomputes the top T levels (every
-    // node there, from the S subtree roots: the same fl(left + right) a
-    // fresh build forms)
+    // 6. publish this subtree's root; workgroup 0 waits for all S of them
+    // (value and presence in one word) and recomputes every node of the top
+    // T levels from them -- the same fl(left + right) a fresh build forms --
+    // then zeroes the words for the next call.  No workgroup waits for
+    // another's start: workgroup 0 waits only for roots that the others
+    // publish without waiting.
     __syncthreads();
-    if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        s_last = old == (uint32_t)S - 1 ? 1u : 0u;
-        if (s_last)
-            __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) store_agent(roots + sub, root_enc(s_root));
+    if (sub != 0 || wave != 0) return;                   // S <= 64: one wave
+    // lane i holds node S + i; at stride s, lane i (a multiple of 2s) forms
+    // node S / 2s + i / 2s as (its value) + (lane i + s's value): left + right
+    V x = V(0);
+    {
+        const bool need = lane < S;
+        uint64_t w = need ? load_agent(roots + lane) : 1u;
+        int spins = kRootSpin;
+        asm volatile("" : "+s"(spins));                  // (not unrolled)
+        while (__any(w == 0)) {
+            __builtin_amdgcn_s_sleep(1);
+            if (w == 0) w = load_agent(roots + lane);
+            if (--spins == 0) break;
+        }
+        if (need) root_dec(w, x);
     }
-    __syncthreads();
-    if (!s_last) return;
-    if (wave != 0) return;                               // S <= 64: one wave
-    V* top = vbuf[0];                                    // top[j]: node j, j in [1, 2S)
-    if (tid < S) top[S + tid] = node_load_agent(tree + S + tid);
-    wave_sync();
-    for (int h = S >> 1; h >= 1; h >>= 1) {
-        if (tid < h) top[h + tid] = top[2 * (h + tid)] + top[2 * (h + tid) + 1];
-        wave_sync();
+    for (int st = 1; st < S; st <<= 1) {
+        const V y = shfl_down_v(x, st);                  // (every lane shuffles)
+        if ((lane & (2 * st - 1)) == 0 && lane < S) {
+            x = x + y;
+            tree[S / (2 * st) + lane / (2 * st)] = x;
+        }
     }
-    if (tid >= 1 && tid < S) tree[tid] = top[tid];
+    if (tid < S) store_agent(roots + tid, 0u);
 }
 
 // The threshold of draw i (see psamp_segtree_sample).
@@ -627,7 +650,7 @@ extern "C" psamp_status psamp_segtree_build(void* tree, psamp_dtype tree_t, int6
     return e;
 }
 
-// The update's workspace: the counter that finds the last subtree workgroup.
+// The update's workspace: one word per subtree root (zero between calls).
 extern "C" size_t psamp_segtree_update_workspace_size(int64_t cap_pow2, int64_t m) {
     (void)cap_pow2;
     (void)m;
@@ -645,7 +668,7 @@ extern "C" psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int
     if (m == 0) return PSAMP_OK;
     if (!tree || !idx || !prio) return PSAMP_E_NULL;
     if (!ws || ws_bytes < kUpdWsBytes) return PSAMP_E_WORKSPACE;
-    if (!aligned(tree, 16) || !aligned(prio, 4) || !aligned(idx, 4) || !aligned(ws, 4))
+    if (!aligned(tree, 16) || !aligned(prio, 4) || !aligned(idx, 4) || !aligned(ws, 8))
         return PSAMP_E_ALIGN;
     hipStream_t st = as_stream(stream);
     if (check_on() && tree_t == PSAMP_F32) check_prio((const float*)prio, m, st);
@@ -660,11 +683,11 @@ extern "C" psamp_status psamp_segtree_update(void* tree, psamp_dtype tree_t, int
         if (tree_t == PSAMP_F32)
             hipLaunchKernelGGL((k_tree_update<float, float>), dim3(1u << T), dim3(kUpdThreads), 0,
                                st, (float*)tree, cap_pow2, D, T, idx + off,
-                               (const float*)prio + off, mm, alpha, (uint32_t*)ws);
+                               (const float*)prio + off, mm, alpha, (uint64_t*)ws);
         else
             hipLaunchKernelGGL((k_tree_update<uint64_t, uint32_t>), dim3(1u << T),
                                dim3(kUpdThreads), 0, st, (uint64_t*)tree, cap_pow2, D, T,
-                               idx + off, (const uint32_t*)prio + off, mm, 0.0, (uint32_t*)ws);
+                               idx + off, (const uint32_t*)prio + off, mm, 0.0, (uint64_t*)ws);
         psamp_status e = launch_status();
         if (e != PSAMP_OK) return e;
     }

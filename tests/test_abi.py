@@ -153,11 +153,11 @@ def test_segtree_validation(L):
     assert s(FAKE, F32, 1024, 10, FAKE, F32, 4, 3, FAKE, None) == E_PARAM
     assert s(FAKE + 8, F32, 1024, 10, FAKE, F32, 4, 0, FAKE, None) == E_ALIGN   # tree: 16 B
     assert u(FAKE, F32, 1024, FAKE, FAKE, F32, 4, 0.6, None, 0, None) == E_WS
-    assert u(FAKE, F32, 1024, FAKE, FAKE, F32, 4, 0.6, FAKE, 255, None) == E_WS
-    assert L.psamp_segtree_update_workspace_size(1024, 1024) == 256
-    assert u(FAKE + 8, F32, 1024, FAKE, FAKE, F32, 4, 0.6, FAKE, 256, None) == E_ALIGN
-    assert u(FAKE, F32, 1024, FAKE + 2, FAKE, F32, 4, 0.6, FAKE, 256, None) == E_ALIGN
-    assert u(FAKE, F32, 1024, FAKE, FAKE, F32, 4, 0.6, FAKE + 2, 256, None) == E_ALIGN
+    assert u(FAKE, F32, 1024, FAKE, FAKE, F32, 4, 0.6, FAKE, 511, None) == E_WS
+    assert L.psamp_segtree_update_workspace_size(1024, 1024) == 512   # one word per subtree root
+    assert u(FAKE + 8, F32, 1024, FAKE, FAKE, F32, 4, 0.6, FAKE, 512, None) == E_ALIGN
+    assert u(FAKE, F32, 1024, FAKE + 2, FAKE, F32, 4, 0.6, FAKE, 512, None) == E_ALIGN
+    assert u(FAKE, F32, 1024, FAKE, FAKE, F32, 4, 0.6, FAKE + 4, 512, None) == E_ALIGN
 
 
 def test_resample_and_scatter_validation(L):
@@ -235,7 +235,7 @@ def test_replay_validation(L):
     assert L.psamp_replay_sample(ref, FAKE, 1 << 20, 1, 0.4, FAKE, FAKE, None) == E_WS
     rb.cursor = 1000                                                    # corrupted state
     assert L.psamp_replay_update(ref, FAKE, FAKE, 4, None) == E_PARAM
-    assert L.psamp_replay_workspace_size(1000, 8192) == 256 + 256     # update, then IS
+    assert L.psamp_replay_workspace_size(1000, 8192) == 512 + 256     # update, then IS
     assert L.psamp_replay_workspace_size(1000, 1 << 20) > 0
 
 
