@@ -24,7 +24,7 @@
 //    adds the published sums of the earlier tiles of its group and the
 //    published totals of the earlier groups, each with a fixed DPP tree.
 //    No sum depends on timing, so the fp64 CDF is the same bits on every
-//    run, and no wait chain is longer than two hops;
+//    run, and each tile looks back in one round trip;
 //  * the status words alternate between two parities from call to call;
 //    each call zeroes the other parity, so the workspace needs no reset.
 #include "psamp_host.h"

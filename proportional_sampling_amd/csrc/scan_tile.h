@@ -19,7 +19,10 @@
 //   * A tile waits only for sums of tiles near it: it reads A of its own
 //     group and of the previous one (and forms GT_{g-1} itself), and the
 //     published totals of the groups before that, which are 64 or more tiles
-//     older.  One hop, no serial fold.
+//     older, all in one round trip; no partial sum is folded serially.  (The
+//     tile that ends a group publishes GT_g after that round, so each total
+//     follows the one two groups before it; publishing it before the round
+//     cost that tile a second round trip and measured slower.)
 //   * Inside a tile, a running max removes rounding dips between threads;
 //     every tile is clamped from above by excl_{j+1} and its last element is
 //     set to excl_{j+1}.  So C[end_j - 1] == excl_{j+1} <= C[end_j], the CDF
@@ -271,20 +274,6 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
     const int cnt = tile - g * kScanGroup;
     Acc base = Acc(0);     // this lane's published leaves h < g - 1, in slot order
     Acc P = Acc(0), Pn = Acc(0), Gp = Acc(0);
-    // The tile that ends a group publishes GT_g as soon as its own group's
-    // sums are visible.  Were it to wait for the older totals first (they
-    // share the first round), each total would wait for the one two groups
-    // earlier: a chain of one poll round trip per two groups that capped the
-    // whole scan's rate (tiles spent most of their life waiting on it).
-    if (!PRE && cnt == kScanGroup - 1) {
-        const uint32_t off1[1] = {a_off((uint32_t)(g * kScanGroup + lane), par)};
-        const bool need1[1] = {lane < cnt};
-        uint64_t w1[1];
-        wait_words<1>(ws, off1, need1, w1);
-        const Acc a = need1[0] ? status_value<Acc>(w1[0]) : Acc(0);
-        const Acc gt = wave_sum(lane == cnt ? A : a);
-        if (lane == 0) store_agent(&ws[gt_off((uint32_t)g, par)], status_enc(gt));
-    }
 #pragma nounroll
     for (int s0 = 0;; s0 += kLbGtWords) {
         const bool first = s0 == 0;
@@ -309,7 +298,7 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
             const Acc a = need[1] ? status_value<Acc>(w[1]) : Acc(0);
             P = wave_sum(a);
             Pn = wave_sum(lane == cnt ? A : a);
-            if (PRE && cnt == kScanGroup - 1 && lane == 0)
+            if (cnt == kScanGroup - 1 && lane == 0)
                 store_agent(&ws[gt_off((uint32_t)g, par)], status_enc(Pn));
             if (g > 0) Gp = wave_sum(need[0] ? status_value<Acc>(w[0]) : Acc(0));
         }
