@@ -424,13 +424,48 @@ __device__ __forceinline__ float is_weight_lp(double pmin, double lpmin, double 
     return (float)exp2_tab(e * (lpmin - lp), M);
 }
 
+// Minimum over the 64 lanes (every lane active), in every lane: the DPP
+// steps of wave_incl_scan with min (lanes without a source take the
+// identity), then lane 63's value -- register-to-register moves instead of
+// six round trips through the LDS crossbar.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp32_or(uint32_t old, uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
 __device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        const uint32_t y = (uint32_t)__shfl_xor((int)x, m);
-        x = y < x ? y : x;
-    }
-    return x;
+    constexpr uint32_t I = 0xFFFFFFFFu;
+    auto mn = [](uint32_t a, uint32_t b) { return a < b ? a : b; };
+    x = mn(x, dpp32_or<kRowShr1, 0xF>(I, x));
+    x = mn(x, dpp32_or<kRowShr2, 0xF>(I, x));
+    x = mn(x, dpp32_or<kRowShr4, 0xF>(I, x));
+    x = mn(x, dpp32_or<kRowShr8, 0xF>(I, x));
+    x = mn(x, dpp32_or<kRowBcast15, 0xA>(I, x));
+    x = mn(x, dpp32_or<kRowBcast31, 0xC>(I, x));
+    return (uint32_t)__builtin_amdgcn_readlane((int)x, kWave - 1);
+}
+// Maximum over the 64 lanes (every lane active), in every lane, the same way.
+__device__ __forceinline__ int wave_max_i32(int x) {
+    constexpr uint32_t I = 0x80000000u;                  // INT_MIN
+    auto mx = [](int a, int b) { return a > b ? a : b; };
+    x = mx(x, (int)dpp32_or<kRowShr1, 0xF>(I, (uint32_t)x));
+    x = mx(x, (int)dpp32_or<kRowShr2, 0xF>(I, (uint32_t)x));
+    x = mx(x, (int)dpp32_or<kRowShr4, 0xF>(I, (uint32_t)x));
+    x = mx(x, (int)dpp32_or<kRowShr8, 0xF>(I, (uint32_t)x));
+    x = mx(x, (int)dpp32_or<kRowBcast15, 0xA>(I, (uint32_t)x));
+    x = mx(x, (int)dpp32_or<kRowBcast31, 0xC>(I, (uint32_t)x));
+    return __builtin_amdgcn_readlane(x, kWave - 1);
+}
+__device__ __forceinline__ float wave_max_f32(float x) {
+    constexpr uint32_t I = 0xFF800000u;                  // -inf
+    auto f = [](float v) { return __float_as_uint(v); };
+    auto g = [](uint32_t v) { return __uint_as_float(v); };
+    x = fmaxf(x, g(dpp32_or<kRowShr1, 0xF>(I, f(x))));
+    x = fmaxf(x, g(dpp32_or<kRowShr2, 0xF>(I, f(x))));
+    x = fmaxf(x, g(dpp32_or<kRowShr4, 0xF>(I, f(x))));
+    x = fmaxf(x, g(dpp32_or<kRowShr8, 0xF>(I, f(x))));
+    x = fmaxf(x, g(dpp32_or<kRowBcast15, 0xA>(I, f(x))));
+    x = fmaxf(x, g(dpp32_or<kRowBcast31, 0xC>(I, f(x))));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), kWave - 1));
 }
 
 // ------------------------------------------------------ streaming stores

@@ -30,12 +30,6 @@ namespace psamp {
 
 constexpr int kResThreads = 256;
 
-__device__ __forceinline__ float wave_max_f32(float x) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m));
-    return x;
-}
-
 // Threshold k of a row, in float exactly as the page forms it: fl(fl(k + u)
 // / P).  For P a power of two, fl(a * (1/P)) is the same float (1/P is exact
 // and both round the same exact quotient), without the division sequence.

@@ -246,9 +246,7 @@ __device__ __forceinline__ void strat_place(const CdfT* __restrict__ cdf, int64_
     const bool own_win = win && !coop;
     // the widest window of the wave bounds the loop for every lane
     int smax = own_win ? span : -1;
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) smax = max_(smax, __shfl_xor(smax, m));
-    smax = __builtin_amdgcn_readfirstlane(smax);
+    smax = wave_max_i32(smax);
     const int32_t eb = (int32_t)e0;
     for (int b = 0; b <= smax; b += kStratWin) {          // (uniform in the wave)
         if (b > 0) {
