@@ -93,6 +93,7 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     }
     const uint32_t calls = (uint32_t)calls_w;
     const int par = (int)(calls & 1u);
+    const KDiv kd(k);
 
     // ---- 1. scan (as psamp_build_cdf); every tile learns T in its lookback
     double q[R][4];
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
 
     // ---- 2. this tile's samples: the thresholds in (excl, excl_next]
     if (wave == 0) {
-        const int64_t r = first_above2(excl, excl_next, T, StratFp{Us, k, T}, k);
+        const int64_t r = first_above2(excl, excl_next, T, StratFp{Us, kd, T}, k);
         if (lane == 0) s_range[0] = (tile == 0) ? 0 : r;
         if (lane == 32) s_range[1] = last_tile ? k : r;
     }
@@ -182,7 +183,7 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     double my_lp = 0.0;
     uint32_t mn = 0xFFFFFFFFu;
     for (int64_t i = i1; i < i_hi; i += kScanThreads) {
-        const double t = strat_threshold(i, Us[i], k, T);
+        const double t = strat_threshold(i, Us[i], kd, T);
         int b = 0, len = tlen;
         while (len > 1) {
             const int half = len >> 1;
@@ -196,7 +197,6 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
         const float pb = s_p[b];
         const uint32_t key = __float_as_uint(pb);
         mn = key < mn ? key : mn;
-        if (one_pass && pb > 0.0f) my_lp = log2_sig32((double)pb, &M);
     }
     if (one_pass) s_b[tid] = my_b;
     mn = wave_min_u32(mn);
@@ -208,6 +208,12 @@ __global__ __launch_bounds__(kScanThreads) void k_per_round(
     // adjacent and all in this tile, and only this tile reads that part of
     // the priority array)
     if (tid == 0) store_agent(&ws[min_off((uint32_t)tile, par)], (uint64_t)s_min + 1);
+    // (the drawn priority's log2, for its IS weight, only now: off the path
+    // to the published minimum)
+    if (one_pass && my_b >= 0) {
+        const float pb = s_p[my_b];
+        if (pb > 0.0f) my_lp = log2_sig32((double)pb, &M);
+    }
     const bool vec_out = vec_ok && tlen == TILE;
 #pragma unroll
     for (int r = 0; r < R; ++r) {

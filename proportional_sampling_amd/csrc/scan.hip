@@ -275,6 +275,7 @@ __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SA
 
     if constexpr (SAMPLE) {
         // this tile's draws: [first t_i > excl_j, first t_i > excl_{j+1})
+        const KDiv kd(sa.k);
         if (wave == 0) {
             uint64_t tw = readlane(par ? t1_w : t0_w, 0);   // normally already present
             const uint32_t off[1] = {(uint32_t)(kHdrT + par)};
@@ -286,7 +287,7 @@ __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SA
             status_dec(tw, T);
             int64_t rr;
             if constexpr (kFp)
-                rr = first_above2(excl, next, T, StratFp{(const float*)sa.u, sa.k, T}, sa.k);
+                rr = first_above2(excl, next, T, StratFp{(const float*)sa.u, kd, T}, sa.k);
             else
                 rr = first_above2(excl, next, T,
                                   StratInt{(const uint32_t*)sa.u, sa.k, T, sa.k_log2}, sa.k);
@@ -319,7 +320,7 @@ __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SA
                 if (i < i_hi) {
                     Acc t;
                     if constexpr (kFp)
-                        t = strat_threshold(i, __uint_as_float(uq[q]), sa.k, T);
+                        t = strat_threshold(i, __uint_as_float(uq[q]), kd, T);
                     else
                         t = int_threshold((uint64_t)i, uq[q], (uint64_t)sa.k, T, 1, sa.k_log2);
                     int b = lds_lower_bound_from(s_C, bp, tlen, t);
@@ -377,7 +378,7 @@ __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SA
                             // last element it can only land on b)
                             bool last = i + 1 >= i_hi;
                             if (!last && b < tlen - 1) {
-                                const Acc tn = strat_threshold(i + 1, un[q], sa.k, T);
+                                const Acc tn = strat_threshold(i + 1, un[q], kd, T);
                                 last = s_C[b] < tn;
                             }
                             if (last) sa.prio[base + b] = nq[q];

@@ -447,20 +447,33 @@ __device__ __forceinline__ Acc tile_value(Acc x, Acc excl, Acc next, bool last_e
 }
 
 // ------------------------------------------- stratified draws of a tile
-// Stratified threshold of draw i (the same operations as psamp_sample).
-__device__ __forceinline__ double strat_threshold(int64_t i, float u, int64_t k, double T) {
+// Stratified threshold of draw i (the same operations as psamp_sample):
+// fl(fl(fl(i + u) / k) * T).  For a power-of-two k the division is the
+// multiplication by inv_k = 1/k (exact, so the same bits), which spares the
+// long chain of a double divide on the path to the draws.
+struct KDiv {
+    int64_t k;
+    double inv_k;
+    bool pow2;
+    __device__ __forceinline__ explicit KDiv(int64_t k_)
+        : k(k_), inv_k(1.0 / (double)k_), pow2((k_ & (k_ - 1)) == 0) {}
+    __device__ __forceinline__ double div(double a) const {
+        return pow2 ? a * inv_k : a / (double)k;
+    }
+};
+__device__ __forceinline__ double strat_threshold(int64_t i, float u, const KDiv& kd, double T) {
     const double a = (double)i + (double)u;
-    const double b = a / (double)k;
+    const double b = kd.div(a);
     return b * T;
 }
 
 // t_i for fp and integer mode (integer: the exact map onto [1, T]).
 struct StratFp {
     const float* U;
-    int64_t k;
+    KDiv kd;
     double T;
     __device__ __forceinline__ double operator()(int64_t i) const {
-        return strat_threshold(i, U[i], k, T);
+        return strat_threshold(i, U[i], kd, T);
     }
 };
 struct StratInt {
