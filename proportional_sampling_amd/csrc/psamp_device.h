@@ -96,6 +96,26 @@ __device__ __forceinline__ T wave_sum(T x) {
     return readlane(wave_incl_scan(x), kWave - 1);
 }
 
+// N independent wave_sums, step by step together: the same bits as N calls,
+// in the time of about one (each step of one sum waits for the last).
+template <class T, int N>
+__device__ __forceinline__ void wave_sums(T (&x)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = x[i] + dpp<kRowShr1, 0xF, true>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = x[i] + dpp<kRowShr2, 0xF, true>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = x[i] + dpp<kRowShr4, 0xF, true>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = x[i] + dpp<kRowShr8, 0xF, true>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = x[i] + dpp<kRowBcast15, 0xA, false>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = x[i] + dpp<kRowBcast31, 0xC, false>(x[i]);
+#pragma unroll
+    for (int i = 0; i < N; ++i) x[i] = readlane(x[i], kWave - 1);
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 // ------------------------------------------------------- atomics / status

@@ -295,12 +295,16 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
         }
         if (!have) wait_words<kLbGtWords + 2>(ws, off, need, w);
         if (first) {
+            // P_j, P_{j+1} and GT_{g-1}, formed together
             const Acc a = need[1] ? status_value<Acc>(w[1]) : Acc(0);
-            P = wave_sum(a);
-            Pn = wave_sum(lane == cnt ? A : a);
+            Acc x[3] = {a, lane == cnt ? A : a,
+                        (g > 0 && need[0]) ? status_value<Acc>(w[0]) : Acc(0)};
+            wave_sums(x);
+            P = x[0];
+            Pn = x[1];
             if (cnt == kScanGroup - 1 && lane == 0)
                 store_agent(&ws[gt_off((uint32_t)g, par)], status_enc(Pn));
-            if (g > 0) Gp = wave_sum(need[0] ? status_value<Acc>(w[0]) : Acc(0));
+            if (g > 0) Gp = x[2];
         }
 #pragma unroll
         for (int i = 0; i < kLbGtWords; ++i)
@@ -309,11 +313,11 @@ __device__ __forceinline__ void lookback(int tile, int n_tiles, int par, Acc A, 
     }
     if (g > 0 && lane == (g - 1) % kWave) base = base + Gp;
     const bool mine = lane == g % kWave;
-    const Acc excl = wave_sum(mine ? base + P : base);
-    const Acc next = wave_sum(mine ? base + Pn : base);
+    Acc y[2] = {mine ? base + P : base, mine ? base + Pn : base};
+    wave_sums(y);                       // excl_j, excl_{j+1}
     if (lane == 0) {
-        s_excl[0] = excl;
-        s_excl[1] = next;
+        s_excl[0] = y[0];
+        s_excl[1] = y[1];
         if (!PRE && tile == n_tiles - 1) store_agent(&ws[kHdrCalls], (uint64_t)(calls + 1u));
     }
 }
@@ -348,33 +352,43 @@ __device__ __forceinline__ void lookback_all(int tile, int n_tiles, int par, Acc
             off[i] = a_off((uint32_t)(need[i] ? t : 0), par);
         }
         wait_words<kAllWords>(ws, off, need, w);
+        // the round's group totals (and P_j, P_{j+1} when g is among them),
+        // formed together
+        Acc x[kAllWords + 2];
+        const int ig = g - h0;             // g's slot in this round, if any
+#pragma unroll
+        for (int i = 0; i < kAllWords; ++i) {
+            Acc a = need[i] ? status_value<Acc>(w[i]) : Acc(0);
+            if (i == ig) {
+                if (lane == cnt) a = A;
+                const Acc below = lane < cnt ? a : Acc(0);
+                x[kAllWords] = below;
+                x[kAllWords + 1] = lane == cnt ? a : below;
+            }
+            x[i] = a;
+        }
+        if (ig < 0 || ig >= kAllWords) x[kAllWords] = x[kAllWords + 1] = Acc(0);
+        wave_sums(x);
+        if (ig >= 0 && ig < kAllWords) {
+            P = x[kAllWords];
+            Pn = x[kAllWords + 1];
+        }
 #pragma unroll
         for (int i = 0; i < kAllWords; ++i) {
             const int h = h0 + i;
-            if (h < G) {
-                Acc a = need[i] ? status_value<Acc>(w[i]) : Acc(0);
-                if (h == g) {
-                    const Acc below = lane < cnt ? a : Acc(0);
-                    P = wave_sum(below);
-                    Pn = wave_sum(lane == cnt ? A : below);
-                    if (lane == cnt) a = A;
-                }
-                const Acc gt = wave_sum(a);
-                if (lane == h % kWave) {
-                    if (h < g) accx = accx + gt;
-                    acct = acct + gt;
-                }
+            if (h < G && lane == h % kWave) {
+                if (h < g) accx = accx + x[i];
+                acct = acct + x[i];
             }
         }
     }
     const bool mine = lane == g % kWave;
-    const Acc excl = wave_sum(mine ? accx + P : accx);
-    const Acc next = wave_sum(mine ? accx + Pn : accx);
-    const Acc T = wave_sum(acct);
+    Acc y[3] = {mine ? accx + P : accx, mine ? accx + Pn : accx, acct};
+    wave_sums(y);                       // excl_j, excl_{j+1}, T
     if (lane == 0) {
-        s_out[0] = excl;
-        s_out[1] = next;
-        s_out[2] = T;
+        s_out[0] = y[0];
+        s_out[1] = y[1];
+        s_out[2] = y[2];
         if (tile == n_tiles - 1) store_agent(&ws[kHdrCalls], (uint64_t)(calls + 1u));
     }
 }

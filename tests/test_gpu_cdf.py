@@ -921,6 +921,50 @@ def test_per_round_one_workspace_shrinking_then_growing(ps):
     assert ws.errors() == 0
 
 
+@pytest.mark.parametrize("n,k,rewrite", [(262144, 8192, True), (8192, 8192, True),
+                                         (300001, 5000, False), (1 << 20, 4096, True),
+                                         (5000, 300, True), (1000, 7, True)])
+def test_per_round_chain_on_one_workspace(ps, n, k, rewrite):
+    """Chained fused updates on one workspace: every update equals the four
+    separate calls bit for bit, also with work between updates -- a priority
+    written outside the updates, the same value written again, a scan on the
+    same workspace (the call parity moves), another alpha -- with and without
+    the rewrite, and with more draws in a tile than it has threads (8192
+    priorities, 8192 draws)."""
+    rounds = 8
+    p = si.generic_f32(n, n + 3, "lognormal")
+    p[::29] = 0.0
+    p[0] = max(p[0], np.float32(1e-3))
+    ws = ps.Workspace(ps.per_round_workspace_size(n, k))
+    Pd = dev(p)
+    p_ref = p.copy()
+    alpha, beta = 0.7, 0.5
+    for r in range(rounds):
+        say(f"chain n={n} k={k} rewrite={rewrite} update {r}")
+        U = si.uniform_f32(np.random.default_rng(900 + r), k)
+        newp = si.generic_f32(k, 950 + r, "exp") if rewrite else None
+        if r == 2:                      # a write between updates
+            j = n // 2
+            p_ref[j] = np.float32(2.5) if p_ref[j] != np.float32(2.5) else np.float32(3.5)
+            Pd[j] = float(p_ref[j])
+        if r == 3:                      # the same value written again: nothing changes
+            Pd[n // 3] = float(p_ref[n // 3])
+        if r == 4:                      # a scan on the same workspace in between
+            ps.build_cdf(Pd, 0.3, ws=ws)
+        if r == 6:                      # another alpha
+            alpha = 0.9
+        C_s, T_s, idx_s, w_s, p_s = _separate_round(ps, p_ref, U, newp, alpha, beta)
+        idx, w, cdf, tot = ps.per_round(Pd, dev(U), alpha, beta,
+                                        dev(newp) if rewrite else None, ws=ws)
+        assert np.array_equal(host(cdf), C_s), f"update {r}: cdf"
+        assert np.array_equal(host(tot), T_s), f"update {r}: total"
+        assert np.array_equal(host(idx), idx_s), f"update {r}: indices"
+        assert np.array_equal(host(w), w_s), f"update {r}: weights"
+        assert np.array_equal(host(Pd), p_s), f"update {r}: priorities"
+        p_ref = p_s
+    assert ws.errors() == 0
+
+
 @pytest.mark.parametrize("n,rows,nt", [(4, 8, True), (1 << 20, 8, True), ((1 << 22) + 12, 4, False),
                                        (8200, 8, False), (4100, 2, False), ((1 << 20) + 4, 2, True)])
 def test_ceiling_copy(ps, n, rows, nt):
