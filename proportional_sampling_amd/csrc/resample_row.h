@@ -10,7 +10,9 @@
 // must be good to ~1e-9 for the ancestors to agree with an exact-arithmetic
 // reading), W_j = exp(lw_j - m) / s with s = sum_j exp(lw_j - m) (equal to
 // exp(lw_j - lse) with lse = m + log s, one exp per particle instead of
-// two), thresholds in float exactly as the page computes them.
+// two), thresholds in float exactly as the page computes them.  The scan
+// runs over the unnormalised e_j = exp(lw_j - m), its total is s, and the
+// division by s goes into the threshold counts (C_j = E_j / s).
 //
 // One 256-thread workgroup per row; reads and writes are 16-byte vectors.
 // No search: the thresholds are non-decreasing in k, so particle j is the
@@ -39,25 +41,27 @@ __device__ __forceinline__ double res_threshold(int k, float ub, float Pf, float
     return (double)(POW2 ? __fmul_rn(a, invP) : __fdiv_rn(a, Pf));
 }
 
-// #{k in [0, P) : t_k <= x}.  fl(k + u) is within 2^-12 of k + u (k < 2^13)
-// and t_k P equals it for a power-of-two P (else the division adds at most
-// 2^-11 more), so t_k P lies within d = 2^-12 (2^-10) of k + u, and y =
-// x P - u in double within 2^-39 of its exact value.  When y is at least
-// eps = 2^-11 (2^-9) away from every integer, the count is floor(y) + 1
-// clamped to [0, P] with no threshold formed; otherwise at most one k can be
-// counted differently by that estimate, and one check on each side fixes
-// it.  (A wave takes the checks for some lane on a few per cent of the
-// counts.)
+// #{k in [0, P) : t_k <= x} for x = E inv_s, E an unnormalised CDF value
+// and sP = P inv_s.  fl(k + u) is within 2^-12 of k + u (k < 2^13) and t_k P
+// equals it for a power-of-two P (else the division adds at most 2^-11
+// more), so t_k P lies within d = 2^-12 (2^-10) of k + u, and y = E sP - u
+// in double within 2^-38 of x P - u.  When y is at least eps = 2^-11 (2^-9)
+// away from every integer, the count is floor(y) + 1 clamped to [0, P] with
+// no threshold formed; otherwise at most one k can be counted differently
+// by that estimate, and one check on each side (against x itself) fixes it.
+// (A wave takes the checks for some lane on a few per cent of the counts.)
 template <bool POW2>
-__device__ __forceinline__ int res_count_le(double x, float ub, float Pf, float invP, int P) {
+__device__ __forceinline__ int res_count_le(double E, double inv_s, double sP, float ub, float Pf,
+                                            float invP, int P) {
     constexpr double kEps = POW2 ? 0x1p-11 : 0x1p-9;
-    const double y = fma(x, (double)P, -(double)ub);  // one rounding
+    const double y = fma(E, sP, -(double)ub);          // one rounding
     const double e = floor(y);
     const double fr = y - e;                          // exact (Sterbenz)
     // floor(y) + 1 clamped to [0, P] (the conversion saturates; NaN gives 0)
     const int k = max_(min_((int)e, P - 1) + 1, 0);
     // fr in [eps, 1 - eps] (fr - 0.5 is exact: fr is a multiple of 2^-40)
     if (__builtin_expect(fabs(fr - 0.5) <= 0.5 - kEps, 1)) return k;
+    const double x = E * inv_s;
     const bool over = k > 0 && res_threshold<POW2>(k - 1, ub, Pf, invP) > x;
     const bool under = k < P && res_threshold<POW2>(k, ub, Pf, invP) <= x;
     return k - (over ? 1 : 0) + (under ? 1 : 0);
@@ -94,7 +98,6 @@ struct ResLds {
     uint32_t s_lastk[4][R];
     double s_wtot[4][R];
     float s_max[4];
-    double s_sum[4];
     double etab[256];          // the table of exp_row (the caller stores it)
 };
 
@@ -124,38 +127,25 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
     const double m =
         (double)fmaxf(fmaxf(L.s_max[0], L.s_max[1]), fmaxf(L.s_max[2], L.s_max[3]));
 
-    // e_j = exp(lw_j - m) in double, thread-local prefixes, row sum s
+    // e_j = exp(lw_j - m) in double and their thread-local prefixes; the
+    // unnormalised CDF E (double) and its total s
     double q[R][4];
-    double ssum = 0.0;
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const double e = (v[r][c] == ninf) ? 0.0 : exp_row((double)v[r][c] - m, L.etab);
-            q[r][c] = e;
-            ssum = ssum + e;
-        }
-    ssum = wave_sum(ssum);
-    if (lane == 0) L.s_sum[wave] = ssum;
-    __syncthreads();
-    const double s = ((L.s_sum[0] + L.s_sum[1]) + L.s_sum[2]) + L.s_sum[3];
-    const double inv_s = 1.0 / s;
-
-    // W_j = e_j / s; C = inclusive scan of W (double)
-#pragma unroll
-    for (int r = 0; r < R; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            const double w = q[r][c] * inv_s;
-            q[r][c] = (c == 0) ? w : q[r][c - 1] + w;
+            q[r][c] = (c == 0) ? e : q[r][c - 1] + e;
         }
     double X[R];
-    double A;
-    tile_scan_256<R, double>(q, X, A, L.s_wtot);
+    double s;
+    tile_scan_256<R, double>(q, X, s, L.s_wtot);
 #pragma unroll
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) q[r][c] = X[r] + q[r][c];
+    const double inv_s = 1.0 / s;
+    const double sP = (double)Pi / s;
 
     // ancestors: with M_j = max_{i <= j} C_i, particle j takes the k in
     // [#{t <= M_{j-1}}, #{t <= M_j}), the last particle also every k above
@@ -172,7 +162,8 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
             const int j = r * ROW + 4 * tid + c;
-            kc[r][c] = (uint32_t)((j >= Pi - 1) ? Pi : res_count_le<POW2>(q[r][c], ub, Pf, invP, Pi));
+            kc[r][c] = (uint32_t)((j >= Pi - 1) ? Pi
+                                                : res_count_le<POW2>(q[r][c], inv_s, sP, ub, Pf, invP, Pi));
         }
     // running max in element order: within the thread's 4, across the
     // wave's lanes (DPP), then across waves and rows (LDS)
