@@ -121,7 +121,7 @@ template <int R, bool VEC, bool SAMPLE>
 constexpr int scan_waves_per_simd() { return (R > 1 && VEC && !SAMPLE) ? 3 : 2; }
 
 template <int IPT, bool VEC, class In, class Out, bool SAMPLE = false, bool FAST = false,
-          bool PER = false>
+          bool PER = false, bool KEEP = false>
 __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SAMPLE>())) void k_build_cdf(
     const In* __restrict__ in, int64_t n, double alpha, Out* __restrict__ cdf,
     Out* __restrict__ total, uint64_t* __restrict__ ws, int n_tiles,
@@ -259,7 +259,7 @@ __global__ __launch_bounds__(kScanThreads, (scan_waves_per_simd<IPT / 4, VEC, SA
             if constexpr (SAMPLE) s_C[e0 + k] = c;
         }
         if (full) {
-            store4<(R > 1)>(tout + e0, o);
+            store4<(R > 1 && !KEEP)>(tout + e0, o);
         } else {
 #pragma unroll
             for (int k = 0; k < 4; ++k)
@@ -511,7 +511,7 @@ static bool use_fast_pow(double alpha) {
     return IPT == 32 && std::is_same<In, float>::value && alpha <= kFastPowMaxAlpha;
 }
 
-template <int IPT, class In, class Out, bool FAST>
+template <int IPT, class In, class Out, bool FAST, bool KEEP>
 static psamp_status launch_scan_t(const void* prio, int64_t n, double alpha, void* cdf,
                                   void* total, void* ws, uint64_t max_slots, int vec_ok,
                                   hipStream_t st) {
@@ -519,36 +519,39 @@ static psamp_status launch_scan_t(const void* prio, int64_t n, double alpha, voi
     if (trace_enabled()) trace_launch("k_build_cdf", tiles, kScanThreads, n);
     const bool vec_in = aligned(prio, 16) && n % 4 == 0;
     if (vec_in)
-        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Out, false, FAST>), dim3(tiles),
+        hipLaunchKernelGGL((k_build_cdf<IPT, true, In, Out, false, FAST, false, KEEP>), dim3(tiles),
                            dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Out*)cdf,
                            (Out*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, SampleArgs{});
     else
-        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Out, false, FAST>), dim3(tiles),
+        hipLaunchKernelGGL((k_build_cdf<IPT, false, In, Out, false, FAST, false, KEEP>), dim3(tiles),
                            dim3(kScanThreads), 0, st, (const In*)prio, n, alpha, (Out*)cdf,
                            (Out*)total, (uint64_t*)ws, tiles, max_slots, vec_ok, SampleArgs{});
     return launch_status();
 }
 
-template <int IPT, class In, class Out>
+template <int IPT, class In, class Out, bool KEEP>
 static psamp_status launch_scan(const void* prio, int64_t n, double alpha, void* cdf, void* total,
                                 void* ws, uint64_t max_slots, int vec_ok, hipStream_t st) {
     if constexpr (IPT == 32 && std::is_same<In, float>::value) {
         if (use_fast_pow<IPT, In>(alpha))
-            return launch_scan_t<IPT, In, Out, true>(prio, n, alpha, cdf, total, ws, max_slots,
-                                                     vec_ok, st);
+            return launch_scan_t<IPT, In, Out, true, KEEP>(prio, n, alpha, cdf, total, ws,
+                                                           max_slots, vec_ok, st);
     }
-    return launch_scan_t<IPT, In, Out, false>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok,
-                                              st);
+    return launch_scan_t<IPT, In, Out, false, KEEP>(prio, n, alpha, cdf, total, ws, max_slots,
+                                                    vec_ok, st);
 }
 
-template <class In, class Out>
+// KEEP: large tiles store the CDF like small ones (not streamed out), so that
+// a search right after it finds it in the Infinity Cache.
+template <class In, class Out, bool KEEP = false>
 static psamp_status launch_build_cdf(const void* prio, int64_t n, double alpha, void* cdf,
                                      void* total, void* ws, size_t ws_bytes, hipStream_t st) {
     const uint64_t max_slots = ws_tile_capacity(ws_bytes);
     const int vec_ok = aligned(cdf, 16);   // 16-byte stores of whole tiles
     if (scan_rows_for(n) == 1)
-        return launch_scan<4, In, Out>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, st);
-    return launch_scan<32, In, Out>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, st);
+        return launch_scan<4, In, Out, KEEP>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok,
+                                             st);
+    return launch_scan<32, In, Out, KEEP>(prio, n, alpha, cdf, total, ws, max_slots, vec_ok, st);
 }
 
 // The fused scan + stratified sample: k_tile_sums, then the scan with
@@ -677,6 +680,25 @@ psamp_status launch_per_update(float* prio, int64_t n, double alpha, double beta
 
 using namespace psamp;
 
+// psamp_build_cdf after its argument checks (KEEP: see launch_build_cdf).
+template <bool KEEP>
+static psamp_status build_cdf_checked(const void* prio, psamp_dtype prio_t, int64_t n,
+                                      double alpha, void* cdf, psamp_dtype cdf_t, void* total,
+                                      void* ws, size_t ws_bytes, void* stream) {
+    const bool in = prio_t == PSAMP_U32;
+    hipStream_t st = as_stream(stream);
+    const bool chk = check_on();
+    if (chk && !in) check_prio((const float*)prio, n, st);
+    psamp_status e;
+    if (in)
+        e = launch_build_cdf<uint32_t, uint64_t, KEEP>(prio, n, 0.0, cdf, total, ws, ws_bytes, st);
+    else if (cdf_t == PSAMP_F64)
+        e = launch_build_cdf<float, double, KEEP>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
+    else e = launch_build_cdf<float, float, KEEP>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
+    if (chk && e == PSAMP_OK) check_total(total, cdf_t, st);
+    return e;
+}
+
 extern "C" size_t psamp_build_cdf_workspace_size(int64_t n) {
     if (n < 1 || n > kMaxN) return 0;
     return ws_bytes_for_tiles(ceil_div(n, kMinTile));
@@ -696,16 +718,8 @@ extern "C" psamp_status psamp_build_cdf(const void* prio, psamp_dtype prio_t, in
     const size_t osz = cdf_t == PSAMP_F32 ? 4 : 8;
     if (!aligned(prio, 4) || !aligned(cdf, osz) || !aligned(total, osz) || !aligned(ws, 8))
         return PSAMP_E_ALIGN;
-    hipStream_t st = as_stream(stream);
-    const bool chk = check_on();
-    if (chk && fp) check_prio((const float*)prio, n, st);
-    psamp_status e;
-    if (in) e = launch_build_cdf<uint32_t, uint64_t>(prio, n, 0.0, cdf, total, ws, ws_bytes, st);
-    else if (cdf_t == PSAMP_F64)
-        e = launch_build_cdf<float, double>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
-    else e = launch_build_cdf<float, float>(prio, n, alpha, cdf, total, ws, ws_bytes, st);
-    if (chk && e == PSAMP_OK) check_total(total, cdf_t, st);
-    return e;
+    return build_cdf_checked<false>(prio, prio_t, n, alpha, cdf, cdf_t, total, ws, ws_bytes,
+                                    stream);
 }
 
 extern "C" psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype prio_t, int64_t n,
@@ -737,8 +751,11 @@ extern "C" psamp_status psamp_build_cdf_sample(const void* prio, psamp_dtype pri
     // LogNormal priorities, while up to 2^20 priorities the one kernel is
     // 1-3 us faster.
     if (k == 0 || cdf_t == PSAMP_F32 || (scan_rows_for(n) != 1 && 64 * k >= n)) {
-        psamp_status s = psamp_build_cdf(prio, prio_t, n, alpha, cdf, cdf_t, total, ws, ws_bytes,
-                                         stream);
+        // (the CDF kept in the Infinity Cache for the sample that reads it)
+        psamp_status s = k == 0 ? build_cdf_checked<false>(prio, prio_t, n, alpha, cdf, cdf_t,
+                                                           total, ws, ws_bytes, stream)
+                                : build_cdf_checked<true>(prio, prio_t, n, alpha, cdf, cdf_t,
+                                                          total, ws, ws_bytes, stream);
         if (s != PSAMP_OK || k == 0) return s;
         return psamp_sample(cdf, cdf_t, n, total, u, u_t, k, 1, out_idx, stream);
     }
