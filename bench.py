@@ -141,7 +141,7 @@ class PerMid:
 
 
 KERNEL_NAMES = {
-    "build_cdf": "k_build_cdf<4, true, float, double, false, false, false>",
+    "build_cdf": "k_build_cdf<4, true, float, double, false, false, false, false>",
     "sample": "k_sample_strat_fp<4, true, double>",
     "is_weights": "k_isw_exch<float, 1, 1>",
     "scatter_lww": "k_scatter_grouped",
