@@ -41,24 +41,24 @@ __device__ __forceinline__ double res_threshold(int k, float ub, float Pf, float
     return (double)(POW2 ? __fmul_rn(a, invP) : __fdiv_rn(a, Pf));
 }
 
-// #{k in [0, P) : t_k <= x} for x = E inv_s, E an unnormalised CDF value
-// and sP = P inv_s.  fl(k + u) is within 2^-12 of k + u (k < 2^13) and t_k P
-// equals it for a power-of-two P (else the division adds at most 2^-11
-// more), so t_k P lies within d = 2^-12 (2^-10) of k + u, and y = E sP - u
-// in double within 2^-38 of x P - u.  When y is at least eps = 2^-11 (2^-9)
-// away from every integer, the count is floor(y) + 1 clamped to [0, P] with
-// no threshold formed; otherwise at most one k can be counted differently
-// by that estimate, and one check on each side (against x itself) fixes it.
+// #{k in [0, P) : t_k <= x} for x = E inv_s, E an unnormalised CDF value,
+// sP = P inv_s and omu = 1 - u (exact).  fl(k + u) is within 2^-12 of k + u
+// (k < 2^13) and t_k P equals it for a power-of-two P (else the division adds
+// at most 2^-11 more), so t_k P lies within d = 2^-12 (2^-10) of k + u.
+// z = E sP + (1 - u) in double (one rounding) is x P - u + 1 to within 2^-38,
+// and positive (E >= 0, u < 1): its truncation is floor(x P - u) + 1 and its
+// fraction that of x P - u.  When that fraction is at least eps = 2^-11
+// (2^-9) away from 0 and 1, the count is the truncation clamped to P, with
+// no threshold formed; otherwise at most one k can be counted differently by
+// that estimate, and one check on each side (against x itself) fixes it.
 // (A wave takes the checks for some lane on a few per cent of the counts.)
 template <bool POW2>
-__device__ __forceinline__ int res_count_le(double E, double inv_s, double sP, float ub, float Pf,
-                                            float invP, int P) {
+__device__ __forceinline__ int res_count_le(double E, double inv_s, double sP, double omu,
+                                            float ub, float Pf, float invP, int P) {
     constexpr double kEps = POW2 ? 0x1p-11 : 0x1p-9;
-    const double y = fma(E, sP, -(double)ub);          // one rounding
-    const double e = floor(y);
-    const double fr = y - e;                          // exact (Sterbenz)
-    // floor(y) + 1 clamped to [0, P] (the conversion saturates; NaN gives 0)
-    const int k = max_(min_((int)e, P - 1) + 1, 0);
+    const double z = fma(E, sP, omu);                  // one rounding
+    const int k = min_((int)z, P);                    // (the conversion gives 0 for NaN)
+    const double fr = __builtin_amdgcn_fract(z);      // z - floor(z), exact
     // fr in [eps, 1 - eps] (fr - 0.5 is exact: fr is a multiple of 2^-40)
     if (__builtin_expect(fabs(fr - 0.5) <= 0.5 - kEps, 1)) return k;
     const double x = E * inv_s;
@@ -67,18 +67,22 @@ __device__ __forceinline__ int res_count_le(double E, double inv_s, double sP, f
     return k - (over ? 1 : 0) + (under ? 1 : 0);
 }
 
-// exp(x) for x <= 0 in double, within 2e-13 relative where the result is
-// a normal double (the weights need about 1e-9 for the ancestors to follow
-// an exact-arithmetic reading):
-// x = N ln2/256 + g with |g| <= ln2/512, exp(x) = 2^(N/256) e^g, 2^(j/256)
-// from a 256-entry table (correctly rounded), e^g from its cubic Taylor
-// polynomial (truncation below 1.4e-13 relative); ln2/256 rounded to double
-// adds at most |N| 2^-61 to g.  x below the double range gives 0 (the
-// conversion saturates and ldexp underflows); a NaN passes through.
+// exp(x) for x in [-2^20, 0] in double, within 2e-13 relative where the
+// result is a normal double (the weights need about 1e-9 for the ancestors
+// to follow an exact-arithmetic reading):
+// x = N ln2/256 + g with |g| <= ln2/512 (to within a rounding), exp(x) =
+// 2^(N/256) e^g, 2^(j/256) from a 256-entry table (correctly rounded), e^g
+// from its cubic Taylor polynomial (truncation below 1.4e-13 relative);
+// ln2/256 rounded to double adds at most |N| 2^-61 to g.  N is rounded to
+// an integer by adding 1.5 2^52 (the sum's unit is 1), which also leaves N in
+// the sum's low word.  Below the double range the result is 0 (ldexp
+// underflows); a NaN passes through.  The caller keeps x at or above -2^20.
 __host__ __device__ __forceinline__ double exp_row(double x, const double* __restrict__ tab) {
-    const double N = rint(x * 0x1.71547652b82fep+8);          // 256 / ln 2
+    constexpr double kShift = 0x1.8p52;
+    const double t = fma(x, 0x1.71547652b82fep+8, kShift);   // 256 / ln 2
+    const double N = t - kShift;                              // exact
+    const int Ni = (int)(uint32_t)bits_of(t);                 // N, two's complement
     const double g = fma(N, -0x1.62e42fefa39efp-9, x);        // ln 2 / 256
-    const int Ni = (int)N;
     const double b = fma(g, fma(g, 1.0 / 6.0, 0.5), 1.0);
     const double s = tab[Ni & 255];
     return ldexp(fma(s, g * b, s), Ni >> 8);
@@ -134,7 +138,8 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
     for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            const double e = (v[r][c] == ninf) ? 0.0 : exp_row((double)v[r][c] - m, L.etab);
+            // (-inf, and a NaN, weigh 0: exp(-1000) is 0 in double)
+            const double e = exp_row(fmax((double)v[r][c] - m, -1000.0), L.etab);
             q[r][c] = (c == 0) ? e : q[r][c - 1] + e;
         }
     double X[R];
@@ -156,6 +161,7 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
     // non-empty range, 0 elsewhere.
     const float Pf = (float)Pi;
     const float invP = 1.0f / Pf;              // exact when POW2
+    const double omu = 1.0 - (double)ub;
     uint32_t kc[R][4];
 #pragma unroll
     for (int r = 0; r < R; ++r)
@@ -163,7 +169,7 @@ __device__ __forceinline__ void res_ancestors(const float (&v)[R][4], int Pi, fl
         for (int c = 0; c < 4; ++c) {
             const int j = r * ROW + 4 * tid + c;
             kc[r][c] = (uint32_t)((j >= Pi - 1) ? Pi
-                                                : res_count_le<POW2>(q[r][c], inv_s, sP, ub, Pf, invP, Pi));
+                                                : res_count_le<POW2>(q[r][c], inv_s, sP, omu, ub, Pf, invP, Pi));
         }
     // running max in element order: within the thread's 4, across the
     // wave's lanes (DPP), then across waves and rows (LDS)

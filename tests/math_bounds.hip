@@ -180,7 +180,8 @@ int main(int argc, char** argv) {
     special &= exp2_tab(0.0, &M) == 1.0 && exp2_tab(1.0, &M) == 2.0 && exp2_tab(-1.0, &M) == 0.5;
     special &= exp2_tab(1024.0, &M) == (double)inf && exp2_tab(-1076.0, &M) == 0.0;
     special &= std::isnan(exp2_tab(NAN, &M));
-    special &= exp_row(0.0, etab) == 1.0 && exp_row(-800.0, etab) == 0.0;
+    special &= exp_row(0.0, etab) == 1.0 && exp_row(-800.0, etab) == 0.0 &&
+               exp_row(-1000.0, etab) == 0.0 && exp_row(-1048576.0, etab) == 0.0;
     special &= std::isnan(exp_row(NAN, etab));
 
     std::printf("{\n");
