@@ -298,6 +298,9 @@ const float* psamp_replay_total(const psamp_replay* rb);
  *   u_row  : rows floats in [0, 1).
  *   out_anc: rows x P int32, row stride ld_out elements (>= P).
  *   1 <= P <= 8192, 1 <= rows <= 2^31 - 1.
+ *   A -inf log-weight weighs 0.  A NaN or +inf one breaks the precondition
+ *   (PSAMP_CHECK_LOGWEIGHT when checks are on); the ancestors are then
+ *   still written and in [0, P), with no other guarantee.
  * Errors: E_NULL, E_SIZE, E_ALIGN, E_LAUNCH.
  * ---------------------------------------------------------------------- */
 psamp_status psamp_resample_rows(const float* logw, int64_t rows, int64_t P,
